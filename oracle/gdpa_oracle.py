@@ -1,0 +1,256 @@
+"""fp64 CPU oracle for Generalized Dot-Product Attention (GDPA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's
+CPU-baseline leg use it.  It shares no code with the HIP library.
+
+What it computes (Kunlun paper summary, section 2.2 "low-level module
+optimisations", GDPA bullet; Telegram review of the same paper, layer steps 1
+and 2): the personalised FFN recast as one multi-head attention operator.  The
+tokens of a sample's user history are the queries; the keys and values are
+per-sample weights derived from that sample's non-sequential context.  For a
+jagged batch with sample b owning rows offsets[b]:offsets[b+1] of Q[T,H,d] and
+per-sample K[b], V[b] of shape [n,H,d], per head h:
+
+    S = scale * X Kb^T            (X = Q rows of b, head h; Kb = K[b,:,h,:])
+    P = phi(S)                    (row softmax over the n context rows, or SiLU)
+    O = P Vb
+
+The pages give no formula for the score map, the scale, masking or the
+normalisation.  Readings taken (each listed with its reason in the design notes):
+  * phi is a row softmax over the sample's n rows, or the elementwise SiLU
+    s*sigmoid(s), which is the FFN form silu(x K^T) V;
+  * scale defaults to 1/sqrt(d) for softmax and 1.0 for SiLU;
+  * no mask: each token sees all n rows of its own sample and nothing else;
+  * d_v = d_qk = d, K and V are distinct per head;
+  * no FFN bias.
+
+Everything is plain float64 numpy: a matrix product is the only library step.
+No blocking, no online softmax, no fusion.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+PHIS = ("softmax", "silu")
+
+
+def as_f64(x) -> np.ndarray:
+    """float64 numpy copy of a numpy array or a (CPU or device) torch tensor."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        try:
+            import torch  # local: only to widen bf16, which numpy cannot hold
+            x = x.to(torch.float64)
+        except ImportError:  # pragma: no cover
+            pass
+        x = x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def default_scale(phi: str, d: int) -> float:
+    """1/sqrt(d) for softmax (standard attention), 1.0 for SiLU (the plain FFN form)."""
+    if phi == "softmax":
+        return 1.0 / math.sqrt(d)
+    if phi == "silu":
+        return 1.0
+    raise ValueError(f"phi must be one of {PHIS}, got {phi!r}")
+
+
+def sigmoid(s: np.ndarray) -> np.ndarray:
+    """Logistic function, evaluated without overflow on either side."""
+    out = np.empty_like(s)
+    pos = s >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-s[pos]))
+    e = np.exp(s[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def silu(s: np.ndarray) -> np.ndarray:
+    """SiLU(s) = s * sigmoid(s)."""
+    return s * sigmoid(s)
+
+
+def silu_grad(s: np.ndarray) -> np.ndarray:
+    """d/ds [s sigmoid(s)] = sigmoid(s) (1 + s (1 - sigmoid(s)))."""
+    g = sigmoid(s)
+    return g * (1.0 + s * (1.0 - g))
+
+
+def row_softmax(s: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Softmax over the last axis and its log-sum-exp (natural log)."""
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=-1, keepdims=True)
+    return e / l, (m + np.log(l))[..., 0]
+
+
+# ---------------------------------------------------------------------------
+# One (sample, head) pair: the definition itself.
+# ---------------------------------------------------------------------------
+
+def gdpa_forward_bh(x: np.ndarray, kb: np.ndarray, vb: np.ndarray, phi: str,
+                    scale: float) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """O = phi(scale * x kb^T) vb for one sample and head.
+
+    x: [L, d] query rows, kb, vb: [n, d].  Returns (O [L, d], lse [L] or None).
+    """
+    s = scale * (x @ kb.T)                      # [L, n]
+    if phi == "softmax":
+        p, lse = row_softmax(s)
+        return p @ vb, lse
+    if phi == "silu":
+        return silu(s) @ vb, None
+    raise ValueError(phi)
+
+
+def gdpa_backward_bh(x: np.ndarray, kb: np.ndarray, vb: np.ndarray, do: np.ndarray,
+                     phi: str, scale: float):
+    """Gradients of sum(O * dO) w.r.t. x, kb, vb for one sample and head.
+
+    Chain rule through O = P V, P = phi(S), S = scale x kb^T:
+      dV = P^T dO;  dP = dO V^T;
+      softmax: dS = P * (dP - rowsum(dO * O));  SiLU: dS = dP * silu'(S);
+      dX = scale dS kb;  dK = scale dS^T x.
+    """
+    s = scale * (x @ kb.T)
+    dp = do @ vb.T
+    if phi == "softmax":
+        p, _ = row_softmax(s)
+        o = p @ vb
+        dvec = (do * o).sum(axis=-1, keepdims=True)
+        ds = p * (dp - dvec)
+    elif phi == "silu":
+        p = silu(s)
+        ds = dp * silu_grad(s)
+    else:
+        raise ValueError(phi)
+    dv = p.T @ do
+    dx = scale * (ds @ kb)
+    dk = scale * (ds.T @ x)
+    return dx, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Jagged batch.
+# ---------------------------------------------------------------------------
+
+def _check(q, offsets, k, v):
+    T, H, d = q.shape
+    B, n, Hk, dk_ = k.shape
+    if v.shape != k.shape or Hk != H or dk_ != d:
+        raise ValueError("shape mismatch between Q [T,H,d] and K/V [B,n,H,d]")
+    if len(offsets) != B + 1 or offsets[0] != 0 or offsets[-1] != T:
+        raise ValueError("offsets must have B+1 entries from 0 to T")
+    if np.any(np.diff(offsets) < 0):
+        raise ValueError("offsets must be non-decreasing")
+    return T, H, d, B, n
+
+
+def gdpa_forward(q, offsets, k, v, phi: str = "softmax", scale: Optional[float] = None,
+                 samples: Optional[Sequence[int]] = None):
+    """Forward over a jagged batch.
+
+    q: [T,H,d]; offsets: [B+1]; k, v: [B,n,H,d].  Returns (O [T,H,d],
+    lse [T,H] for softmax else None), float64.  With `samples`, only those
+    samples' rows are computed (the rest stay NaN): samples are independent.
+    """
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    offsets = np.asarray(as_f64(offsets), dtype=np.int64)
+    T, H, d, B, n = _check(q, offsets, k, v)
+    if scale is None:
+        scale = default_scale(phi, d)
+    o = np.full((T, H, d), np.nan)
+    lse = np.full((T, H), np.nan) if phi == "softmax" else None
+    for b in (range(B) if samples is None else samples):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        for h in range(H):
+            ob, lb = gdpa_forward_bh(q[r0:r1, h, :], k[b, :, h, :], v[b, :, h, :], phi, scale)
+            o[r0:r1, h, :] = ob
+            if lse is not None:
+                lse[r0:r1, h] = lb
+    return o, lse
+
+
+def gdpa_backward(q, offsets, k, v, do, phi: str = "softmax", scale: Optional[float] = None,
+                  samples: Optional[Sequence[int]] = None):
+    """Backward over a jagged batch: (dQ [T,H,d], dK [B,n,H,d], dV [B,n,H,d]).
+
+    dK and dV are sums over each sample's own tokens; an empty sample gets zeros.
+    With `samples`, rows and K/V slots of other samples stay NaN.
+    """
+    q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    offsets = np.asarray(as_f64(offsets), dtype=np.int64)
+    T, H, d, B, n = _check(q, offsets, k, v)
+    if scale is None:
+        scale = default_scale(phi, d)
+    dq = np.full((T, H, d), np.nan)
+    dk = np.full((B, n, H, d), np.nan)
+    dv = np.full((B, n, H, d), np.nan)
+    for b in (range(B) if samples is None else samples):
+        r0, r1 = int(offsets[b]), int(offsets[b + 1])
+        for h in range(H):
+            gx, gk, gv = gdpa_backward_bh(q[r0:r1, h, :], k[b, :, h, :], v[b, :, h, :],
+                                          do[r0:r1, h, :], phi, scale)
+            dq[r0:r1, h, :] = gx
+            dk[b, :, h, :] = gk
+            dv[b, :, h, :] = gv
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Stacked residual layers with generated K/V (Telegram review, layer step 1:
+# K and V come from the context features; paper summary section 2.1: the
+# weight-generation module of the interaction block; GDPA "allows stable
+# stacking of the PFFN", read as a plain residual between layers).
+# ---------------------------------------------------------------------------
+
+def weight_generation(ctx, w, n: int, H: int, d: int) -> np.ndarray:
+    """K (or V) = (C W).reshape(B, n, H, d) for context C [B, c] and W [c, n*H*d]."""
+    ctx, w = as_f64(ctx), as_f64(w)
+    return (ctx @ w).reshape(ctx.shape[0], n, H, d)
+
+
+def stacked_forward(x0, offsets, ctx, w_k: List, w_v: List, heads: int, n: int,
+                    phi: str = "silu", scale: Optional[float] = None):
+    """X_{l+1} = X_l + GDPA(X_l as [T,H,d]; C W_K^l, C W_V^l).  Returns [X_0..X_L] ([T,H*d])."""
+    x = as_f64(x0)
+    T, HD = x.shape
+    d = HD // heads
+    xs = [x]
+    for wk, wv in zip(w_k, w_v):
+        kl = weight_generation(ctx, wk, n, heads, d)
+        vl = weight_generation(ctx, wv, n, heads, d)
+        o, _ = gdpa_forward(x.reshape(T, heads, d), offsets, kl, vl, phi, scale)
+        x = x + o.reshape(T, HD)
+        xs.append(x)
+    return xs
+
+
+def stacked_backward(xs: List[np.ndarray], offsets, ctx, w_k: List, w_v: List, do,
+                     heads: int, n: int, phi: str = "silu", scale: Optional[float] = None):
+    """Backward of stacked_forward for loss sum(X_L * dO).
+
+    dX_l = dX_{l+1} + dQ_l (the residual passes the gradient through unchanged);
+    dW^l = C^T dK_l.reshape(B, -1) (and likewise for V).  Returns (dX_0, [dW_K], [dW_V]).
+    """
+    ctx = as_f64(ctx)
+    dx = as_f64(do)
+    T, HD = dx.shape
+    d = HD // heads
+    B = ctx.shape[0]
+    dwk = [None] * len(w_k)
+    dwv = [None] * len(w_v)
+    for l in reversed(range(len(w_k))):
+        kl = weight_generation(ctx, w_k[l], n, heads, d)
+        vl = weight_generation(ctx, w_v[l], n, heads, d)
+        gq, gk, gv = gdpa_backward(xs[l].reshape(T, heads, d), offsets, kl, vl,
+                                   dx.reshape(T, heads, d), phi, scale)
+        dwk[l] = ctx.T @ gk.reshape(B, -1)
+        dwv[l] = ctx.T @ gv.reshape(B, -1)
+        dx = dx + gq.reshape(T, HD)
+    return dx, dwk, dwv

@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size parity runs")
+
+
+@pytest.fixture(scope="session")
+def gdpa_lib():
+    """The HIP-backed binding; GPU tests fail loudly if it is missing."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test selected but no GPU is visible")
+    import context_cross_attention_amd as cca
+    cca.load()  # raises if the shared library was not built
+    return cca
