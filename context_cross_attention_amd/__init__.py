@@ -1,0 +1,257 @@
+"""Python binding of libgdpa.so (MI355X / gfx950 GDPA kernels).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  torch is used for device memory and the current stream.  There is no
+fallback: if the shared library is missing or a call fails, an exception is
+raised.
+
+    o, lse = fwd(q, offsets, k, v, phi="softmax")
+    dq, dk, dv = bwd(q, offsets, k, v, o, lse, do, phi="softmax")
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdpa.so")
+
+PHI = {"softmax": 0, "silu": 1}
+DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+FWD_RESIDUAL = 0x1
+BWD_ACCUM_DQ = 0x2
+
+STATUS = {0: "GDPA_OK", 1: "GDPA_ERR_INVALID_ARGUMENT", 2: "GDPA_ERR_UNSUPPORTED",
+          3: "GDPA_ERR_WORKSPACE_TOO_SMALL", 4: "GDPA_ERR_HIP"}
+
+
+class GdpaProblem(ctypes.Structure):
+    """Mirror of gdpa_problem in include/gdpa.h."""
+    _fields_ = [("batch", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("max_seqlen", ctypes.c_int32), ("n_kv", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("phi", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class GdpaError(RuntimeError):
+    def __init__(self, status: int, where: str, hip_error: int = 0):
+        msg = f"{where}: {STATUS.get(status, status)}"
+        if status == 4:
+            msg += f" (hipError_t {hip_error})"
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+EXPORTS = ("gdpa_workspace_bytes", "gdpa_fwd", "gdpa_bwd", "gdpa_weightgen_fwd",
+           "gdpa_weightgen_bwd_w", "gdpa_check_offsets", "gdpa_status_str",
+           "gdpa_last_hip_error")
+
+
+def load(path: str = LIB_PATH):
+    """Load libgdpa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found: build it with `python -m context_cross_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(GdpaProblem)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.gdpa_workspace_bytes.argtypes = [P, ctypes.c_int]
+    lib.gdpa_workspace_bytes.restype = sz
+    lib.gdpa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_fwd.restype = ctypes.c_int
+    lib.gdpa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_bwd.restype = ctypes.c_int
+    lib.gdpa_weightgen_fwd.argtypes = [i32, i32, i64, vp, vp, vp, vp]
+    lib.gdpa_weightgen_fwd.restype = ctypes.c_int
+    lib.gdpa_weightgen_bwd_w.argtypes = [i32, i32, i64, vp, vp, vp, vp]
+    lib.gdpa_weightgen_bwd_w.restype = ctypes.c_int
+    lib.gdpa_check_offsets.argtypes = [vp, i32, i32, i32]
+    lib.gdpa_check_offsets.restype = ctypes.c_int
+    lib.gdpa_status_str.argtypes = [ctypes.c_int]
+    lib.gdpa_status_str.restype = ctypes.c_char_p
+    lib.gdpa_last_hip_error.argtypes = []
+    lib.gdpa_last_hip_error.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise GdpaError(status, where, _lib.gdpa_last_hip_error() if status == 4 else 0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def default_scale(phi: str, d: int) -> float:
+    """1/sqrt(d) for softmax, 1 for SiLU (the plain FFN form)."""
+    return 1.0 / math.sqrt(d) if phi == "softmax" else 1.0
+
+
+def make_problem(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, phi: str,
+                 scale: Optional[float], flags: int = 0, max_seqlen: Optional[int] = None,
+                 total_tokens: Optional[int] = None) -> GdpaProblem:
+    B, n, H, d = k.shape
+    T = q.shape[0] if total_tokens is None else total_tokens
+    if phi not in PHI:
+        raise ValueError(f"phi must be one of {tuple(PHI)}")
+    if q.dtype not in DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return GdpaProblem(B, T, T if max_seqlen is None else max_seqlen, n, H, d, PHI[phi],
+                       default_scale(phi, d) if scale is None else float(scale), DTYPE[q.dtype], flags)
+
+
+def _require(t: torch.Tensor, name: str, shape, dtype, device):
+    if t.shape != torch.Size(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def workspace_bytes(prob: GdpaProblem, backward: bool) -> int:
+    return int(load().gdpa_workspace_bytes(ctypes.byref(prob), 1 if backward else 0))
+
+
+def _workspace(prob: GdpaProblem, backward: bool, device, workspace: Optional[torch.Tensor]):
+    need = workspace_bytes(prob, backward)
+    if workspace is not None and workspace.numel() >= need:
+        return workspace
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+
+def fwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+        phi: str = "softmax", scale: Optional[float] = None, residual: Optional[torch.Tensor] = None,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        want_lse: bool = True, workspace: Optional[torch.Tensor] = None
+        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """GDPA forward.  q [T,H,d], offsets int32 [B+1], k, v [B,n,H,d] (same dtype, device).
+
+    Returns (o [T,H,d], lse [T,H] float32 for softmax when want_lse, else None).
+    With `residual` ([T,H,d]), o = residual + GDPA(q, k, v).
+    """
+    lib = load()
+    B, n, H, d = k.shape
+    T = q.shape[0]
+    dev = q.device
+    _require(q, "q", (T, H, d), q.dtype, dev)
+    _require(k, "k", (B, n, H, d), q.dtype, dev)
+    _require(v, "v", (B, n, H, d), q.dtype, dev)
+    _require(offsets, "offsets", (B + 1,), torch.int32, dev)
+    flags = 0
+    if residual is not None:
+        _require(residual, "residual", (T, H, d), q.dtype, dev)
+        flags |= FWD_RESIDUAL
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out, "out", (T, H, d), q.dtype, dev)
+    if phi == "softmax" and want_lse and lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if phi != "softmax":
+        lse = None
+    prob = make_problem(q, offsets, k, phi, scale, flags)
+    ws = _workspace(prob, False, dev, workspace)
+    st = lib.gdpa_fwd(ctypes.byref(prob), _ptr(offsets), _ptr(q), _ptr(k), _ptr(v), _ptr(residual),
+                      _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream())
+    _check(st, "gdpa_fwd")
+    return out, lse
+
+
+def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+        o: Optional[torch.Tensor], lse: Optional[torch.Tensor], do: torch.Tensor,
+        phi: str = "softmax", scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+        accumulate_dq: bool = False, dk: Optional[torch.Tensor] = None,
+        dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """GDPA backward of sum(O * dO).  Returns (dq, dk, dv).
+
+    For softmax, o and lse are the forward's outputs; for SiLU they are unused.
+    With accumulate_dq, dq (which may be `do` itself) receives dq + dQ.
+    """
+    lib = load()
+    B, n, H, d = k.shape
+    T = q.shape[0]
+    dev = q.device
+    for name, t in (("q", q), ("do", do)):
+        _require(t, name, (T, H, d), q.dtype, dev)
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, (B, n, H, d), q.dtype, dev)
+    _require(offsets, "offsets", (B + 1,), torch.int32, dev)
+    if phi == "softmax":
+        _require(o, "o", (T, H, d), q.dtype, dev)
+        _require(lse, "lse", (T, H), torch.float32, dev)
+    else:
+        o, lse = None, None
+    flags = 0
+    if accumulate_dq:
+        if dq is None:
+            raise ValueError("accumulate_dq needs dq")
+        flags |= BWD_ACCUM_DQ
+    if dq is None:
+        dq = torch.empty_like(q)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _require(dq, "dq", (T, H, d), q.dtype, dev)
+    _require(dk, "dk", (B, n, H, d), q.dtype, dev)
+    _require(dv, "dv", (B, n, H, d), q.dtype, dev)
+    prob = make_problem(q, offsets, k, phi, scale, flags)
+    ws = _workspace(prob, True, dev, workspace)
+    st = lib.gdpa_bwd(ctypes.byref(prob), _ptr(offsets), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                      _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                      _stream())
+    _check(st, "gdpa_bwd")
+    return dq, dk, dv
+
+
+def weightgen_fwd(ctx: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """out[B, cols] = ctx[B, c] @ w[c, cols] (bf16, fp32 accumulation)."""
+    lib = load()
+    B, c = ctx.shape
+    cols = w.shape[1]
+    _require(ctx, "ctx", (B, c), torch.bfloat16, ctx.device)
+    _require(w, "w", (c, cols), torch.bfloat16, ctx.device)
+    if out is None:
+        out = torch.empty((B, cols), dtype=torch.bfloat16, device=ctx.device)
+    _require(out, "out", (B, cols), torch.bfloat16, ctx.device)
+    _check(lib.gdpa_weightgen_fwd(B, c, cols, _ptr(ctx), _ptr(w), _ptr(out), _stream()),
+           "gdpa_weightgen_fwd")
+    return out
+
+
+def weightgen_bwd_w(ctx: torch.Tensor, d_out: torch.Tensor, d_w: Optional[torch.Tensor] = None):
+    """d_w[c, cols] = ctx[B, c]^T @ d_out[B, cols] (bf16, fp32 accumulation)."""
+    lib = load()
+    B, c = ctx.shape
+    cols = d_out.shape[1]
+    _require(ctx, "ctx", (B, c), torch.bfloat16, ctx.device)
+    _require(d_out, "d_out", (B, cols), torch.bfloat16, ctx.device)
+    if d_w is None:
+        d_w = torch.empty((c, cols), dtype=torch.bfloat16, device=ctx.device)
+    _require(d_w, "d_w", (c, cols), torch.bfloat16, ctx.device)
+    _check(lib.gdpa_weightgen_bwd_w(B, c, cols, _ptr(ctx), _ptr(d_out), _ptr(d_w), _stream()),
+           "gdpa_weightgen_bwd_w")
+    return d_w
+
+
+def check_offsets(offsets_host, total_tokens: int, max_seqlen: int) -> bool:
+    """Host-side offsets check (gdpa_check_offsets) on a CPU int32 tensor."""
+    lib = load()
+    t = torch.as_tensor(offsets_host, dtype=torch.int32).contiguous()
+    return lib.gdpa_check_offsets(ctypes.c_void_p(t.data_ptr()), t.numel() - 1, total_tokens,
+                                  max_seqlen) == 0

@@ -1,0 +1,233 @@
+// C ABI of the GDPA library: argument checks, workspace layout and launches.
+// Every check happens on the host before the first HIP call, so invalid
+// arguments are reported without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/gdpa.h"
+#include "gdpa_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+gdpa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return GDPA_OK;
+  g_last_hip_error = (int)e;
+  return GDPA_ERR_HIP;
+}
+
+gdpa_status check_problem(const gdpa_problem* p) {
+  if (p == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->batch < 1 || p->total_tokens < 0 || p->max_seqlen < 0 || p->n_kv < 1 || p->heads < 1 ||
+      p->head_dim < 1)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->phi != GDPA_PHI_SOFTMAX && p->phi != GDPA_PHI_SILU) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->dtype != GDPA_F32 && p->dtype != GDPA_BF16) return GDPA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->scale)) return GDPA_ERR_INVALID_ARGUMENT;
+  // Element counts index with 32-bit token and row numbers and 64-bit offsets.
+  if ((int64_t)p->total_tokens * p->heads > INT32_MAX) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)p->batch * p->n_kv * p->heads > INT32_MAX) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) return GDPA_ERR_UNSUPPORTED;
+  if (p->flags & ~(uint32_t)(GDPA_FWD_RESIDUAL | GDPA_BWD_ACCUM_DQ)) return GDPA_ERR_UNSUPPORTED;
+  return GDPA_OK;
+}
+
+// Workspace layouts (each region 256-byte aligned).
+//   forward : tile_start [B+1] int32
+//   backward: order [B] int32 | dvec [T*H] fp32 (softmax) | dq_acc [T*H*d] fp32 (bf16,
+//             when the context rows span several work-groups)
+struct BwdPlan {
+  int waves = 0, chunks = 0;
+  size_t order_off = 0, dvec_off = 0, acc_off = 0, total = 0;
+  bool need_acc = false;
+};
+
+BwdPlan bwd_plan(const gdpa_problem* p) {
+  BwdPlan pl;
+  const size_t TH = (size_t)p->total_tokens * p->heads;
+  if (p->dtype == GDPA_BF16) {
+    pl.waves = gdpa::bwd_bf16_waves(p->head_dim, p->n_kv);
+    const int nj = 32 * pl.waves;
+    pl.chunks = (p->n_kv + nj - 1) / nj;
+    pl.need_acc = pl.chunks > 1;
+  }
+  size_t off = 0;
+  pl.order_off = off;
+  off += align_up(sizeof(int32_t) * (size_t)p->batch);
+  pl.dvec_off = off;
+  if (p->phi == GDPA_PHI_SOFTMAX) off += align_up(sizeof(float) * TH);
+  pl.acc_off = off;
+  if (pl.need_acc) off += align_up(sizeof(float) * TH * p->head_dim);
+  pl.total = off;
+  return pl;
+}
+
+size_t fwd_workspace(const gdpa_problem* p) {
+  return align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdpa_workspace_bytes(const gdpa_problem* p, int backward) {
+  if (check_problem(p) != GDPA_OK) return 0;
+  return backward ? bwd_plan(p).total : fwd_workspace(p);
+}
+
+gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
+                     const void* v, const void* residual, void* o, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  const gdpa_status st = check_problem(p);
+  if (st != GDPA_OK) return st;
+  if (offsets == nullptr || k == nullptr || v == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->total_tokens > 0 && (q == nullptr || o == nullptr)) return GDPA_ERR_INVALID_ARGUMENT;
+  const bool resid = (p->flags & GDPA_FWD_RESIDUAL) != 0;
+  if (resid && residual == nullptr && p->total_tokens > 0) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->flags & GDPA_BWD_ACCUM_DQ) return GDPA_ERR_INVALID_ARGUMENT;
+  if (resid && residual == o && residual != q) return GDPA_ERR_INVALID_ARGUMENT;
+  if (o != nullptr && (o == q || o == k || o == v)) return GDPA_ERR_INVALID_ARGUMENT;
+  const size_t need = fwd_workspace(p);
+  if (p->dtype == GDPA_BF16 && (workspace == nullptr || workspace_bytes < need))
+    return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  if (p->total_tokens == 0) return GDPA_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  gdpa::FwdArgs a{};
+  a.offsets = offsets;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.residual = residual;
+  a.o = o;
+  a.lse = (p->phi == GDPA_PHI_SOFTMAX) ? lse : nullptr;
+  a.B = p->batch;
+  a.T = p->total_tokens;
+  a.n = p->n_kv;
+  a.H = p->heads;
+  a.scale = p->scale;
+  if (p->dtype == GDPA_F32) return hip_status(gdpa::launch_fwd_f32(a, p->head_dim, p->phi, resid, s));
+
+  int32_t* tile_start = (int32_t*)workspace;
+  hipError_t e = gdpa::launch_tile_scan(offsets, p->batch, gdpa::kFwdTileRows, tile_start, s);
+  if (e != hipSuccess) return hip_status(e);
+  a.tile_start = tile_start;
+  const int grid = gdpa::fwd_bf16_grid(p->total_tokens, p->batch, p->heads);
+  return hip_status(gdpa::launch_fwd_bf16(a, p->head_dim, p->phi, resid, grid, s));
+}
+
+gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
+                     const void* v, const void* o, const float* lse, const void* d_o, void* dq,
+                     void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  const gdpa_status st = check_problem(p);
+  if (st != GDPA_OK) return st;
+  if (offsets == nullptr || k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->total_tokens > 0 && (q == nullptr || d_o == nullptr || dq == nullptr))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  const bool softmax = p->phi == GDPA_PHI_SOFTMAX;
+  if (softmax && p->total_tokens > 0 && (o == nullptr || lse == nullptr))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->flags & GDPA_FWD_RESIDUAL) return GDPA_ERR_INVALID_ARGUMENT;
+  const bool accum = (p->flags & GDPA_BWD_ACCUM_DQ) != 0;
+  if (dq != nullptr && dq == d_o && !accum) return GDPA_ERR_INVALID_ARGUMENT;
+  if (dk == dv || dk == k || dk == v || dv == k || dv == v) return GDPA_ERR_INVALID_ARGUMENT;
+  const BwdPlan pl = bwd_plan(p);
+  if (workspace == nullptr || workspace_bytes < pl.total) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  gdpa::BwdArgs a{};
+  a.offsets = offsets;
+  a.order = (const int32_t*)(ws + pl.order_off);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.d_o = d_o;
+  a.lse = lse;
+  a.dvec = softmax ? (const float*)(ws + pl.dvec_off) : nullptr;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dq_acc = pl.need_acc ? (float*)(ws + pl.acc_off) : nullptr;
+  a.B = p->batch;
+  a.T = p->total_tokens;
+  a.n = p->n_kv;
+  a.H = p->heads;
+  a.n_chunks = pl.chunks;
+  a.scale = p->scale;
+  a.accum_dq = accum ? 1 : 0;
+
+  const size_t TH = (size_t)p->total_tokens * p->heads;
+  hipError_t e = hipSuccess;
+  if (softmax && TH > 0) {
+    e = gdpa::launch_softmax_dvec(o, d_o, (int)TH, p->head_dim, p->dtype == GDPA_BF16,
+                                  (float*)(ws + pl.dvec_off), s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (p->dtype == GDPA_F32) return hip_status(gdpa::launch_bwd_f32(a, p->head_dim, p->phi, s));
+
+  e = gdpa::launch_longest_first(offsets, p->batch, (int32_t*)(ws + pl.order_off), s);
+  if (e != hipSuccess) return hip_status(e);
+  if (pl.need_acc) {
+    e = gdpa::launch_zero_f32(a.dq_acc, TH * p->head_dim, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  e = gdpa::launch_bwd_bf16(a, p->head_dim, p->phi, pl.waves, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (pl.need_acc) e = gdpa::launch_dq_finalize(a.dq_acc, dq, TH * p->head_dim, accum, s);
+  return hip_status(e);
+}
+
+gdpa_status gdpa_weightgen_fwd(int32_t batch, int32_t ctx_dim, int64_t cols, const void* ctx,
+                               const void* w, void* out, void* stream) {
+  if (batch < 1 || ctx_dim < 1 || cols < 1 || ctx == nullptr || w == nullptr || out == nullptr)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (cols % 8 != 0 || ctx_dim % 8 != 0) return GDPA_ERR_UNSUPPORTED;
+  if (cols / 128 >= INT32_MAX || batch / 128 >= 65535) return GDPA_ERR_UNSUPPORTED;
+  return hip_status(gdpa::launch_gemm_bf16(false, batch, cols, ctx_dim, ctx, w, out,
+                                           (hipStream_t)stream));
+}
+
+gdpa_status gdpa_weightgen_bwd_w(int32_t batch, int32_t ctx_dim, int64_t cols, const void* ctx,
+                                 const void* d_out, void* d_w, void* stream) {
+  if (batch < 1 || ctx_dim < 1 || cols < 1 || ctx == nullptr || d_out == nullptr || d_w == nullptr)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (cols % 8 != 0 || ctx_dim % 8 != 0) return GDPA_ERR_UNSUPPORTED;
+  if (cols / 128 >= INT32_MAX || ctx_dim / 128 >= 65535) return GDPA_ERR_UNSUPPORTED;
+  return hip_status(gdpa::launch_gemm_bf16(true, ctx_dim, cols, batch, ctx, d_out, d_w,
+                                           (hipStream_t)stream));
+}
+
+gdpa_status gdpa_check_offsets(const int32_t* host_offsets, int32_t batch, int32_t total_tokens,
+                               int32_t max_seqlen) {
+  if (host_offsets == nullptr || batch < 1 || total_tokens < 0 || max_seqlen < 0)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (host_offsets[0] != 0 || host_offsets[batch] != total_tokens) return GDPA_ERR_INVALID_ARGUMENT;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t len = (int64_t)host_offsets[b + 1] - host_offsets[b];
+    if (len < 0 || len > max_seqlen) return GDPA_ERR_INVALID_ARGUMENT;
+  }
+  return GDPA_OK;
+}
+
+const char* gdpa_status_str(gdpa_status s) {
+  switch (s) {
+    case GDPA_OK: return "GDPA_OK";
+    case GDPA_ERR_INVALID_ARGUMENT: return "GDPA_ERR_INVALID_ARGUMENT";
+    case GDPA_ERR_UNSUPPORTED: return "GDPA_ERR_UNSUPPORTED";
+    case GDPA_ERR_WORKSPACE_TOO_SMALL: return "GDPA_ERR_WORKSPACE_TOO_SMALL";
+    case GDPA_ERR_HIP: return "GDPA_ERR_HIP";
+  }
+  return "GDPA_ERR_UNKNOWN";
+}
+
+int gdpa_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,382 @@
+// GDPA backward: dQ, dK, dV of sum(O * dO), with dK and dV summed over each
+// sample's own tokens (the keys and values are per-sample weights derived from
+// that sample's context; Kunlun paper summary section 2.2, GDPA bullet).
+//
+// bf16 path.  One work-group owns (sample b, head h, a chunk of 32 * NW context
+// rows); wave w owns 32 of those rows and keeps their dK and dV accumulators in
+// registers while the work-group walks all of the sample's query rows, 32 at a
+// time.  So dK and dV are reduced per sample without atomics.  Per 32-row query
+// tile (Q and dO staged in LDS, row-major):
+//   S  = Q K^T,  dP = dO V^T      (M = tokens, N = the wave's context rows)
+//   P  = phi(S); dS = softmax: P (dP - rowsum(dO O)),  SiLU: dP silu'(S)
+//   dV += P^T dO, dK += scale dS^T Q   (A = P^T / dS^T straight from the C tile,
+//                                       B = dO / Q columns via LDS transpose reads)
+//   dQ  = scale dS K over all the work-group's context rows: dS^T goes to LDS and
+//         every wave computes 16x16 output tiles from it.
+// When the context rows need more than one work-group, dQ partial sums go to an
+// fp32 buffer with atomics and a final pass rounds them.
+//
+// Work-groups are launched longest sample first (longest-processing-time list
+// scheduling by the hardware dispatcher).
+//
+// fp32 path: plain loops in fp32, for the small fp32 workload.
+#include "gdpa_device.h"
+#include "gdpa_launch.h"
+
+namespace gdpa {
+
+template <int D, int PHI, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
+  constexpr int NJ = 32 * NW;          // context rows per work-group
+  constexpr int BQ = kBwdRowsPerWave;  // query rows per step
+  constexpr int KS = D / 16, DT = D / 32, LD = D + 8, CH = D / 8;
+  constexpr int LDT = BQ + 8;          // dS^T row stride
+  constexpr int NT = NW * 64;
+  constexpr int DQ_TILES = (BQ / 16) * (D / 16);
+  constexpr int TPW = DQ_TILES / NW;   // 16x16 dQ tiles per wave
+  static_assert(TPW * NW == DQ_TILES && TPW >= 1, "dQ tiles must split evenly over waves");
+
+  __shared__ __align__(16) uint16_t Kc[NJ * LD];
+  __shared__ __align__(16) uint16_t Qs[BQ * LD];
+  __shared__ __align__(16) uint16_t dOs[BQ * LD];
+  __shared__ __align__(16) uint16_t dSt[NJ * LDT];
+  __shared__ float lse_s[BQ], dvec_s[BQ];
+
+  const int H = a.H, n = a.n, nch = a.n_chunks;
+  const int item = blockIdx.x;
+  const int rank = item / (H * nch);
+  const int rem = item - rank * H * nch;
+  const int h = rem / nch, jc = rem - h * nch;
+  const int b = a.order[rank];
+  const int seq0 = a.offsets[b], L = a.offsets[b + 1] - seq0;
+  const int j0 = jc * NJ;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const size_t rs = (size_t)H * D;
+  const uint16_t* Kg = (const uint16_t*)a.k + ((size_t)b * n * H + h) * D;
+  const uint16_t* Vg = (const uint16_t*)a.v + ((size_t)b * n * H + h) * D;
+
+  // K chunk, row-major, into LDS (zero rows past n).
+  for (int idx = tid; idx < NJ * CH; idx += NT) {
+    const int j = idx / CH, c = idx % CH;
+    const u32x4 v = (j0 + j < n) ? gload16(Kg + (size_t)(j0 + j) * rs + 8 * c) : u32x4{};
+    lds_write16(&Kc[j * LD + 8 * c], v);
+  }
+  // The wave's V rows as B operand of dP = dO V^T: lane (j + 32 g), items d = 16 ks + 8 g + i.
+  const int jl = 32 * wave + lr;  // local context row of this lane
+  const int jw = j0 + jl;
+  const bool jvalid = jw < n;
+  bf16x8 vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    vf[ks] = jvalid ? as_bf16x8(gload16(Vg + (size_t)jw * rs + 16 * ks + 8 * g)) : bf16x8{};
+
+  f32x16 dK[DT], dV[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dK[dt] = f32x16{};
+    dV[dt] = f32x16{};
+  }
+
+  // Transpose-read addressing for the dV / dK products (row order of the C tile,
+  // as in the forward kernel) and for the dQ product (contiguous rows, 16x16x32).
+  const int trG = lane >> 4;
+  const int tr_off = (4 * (trG >> 1) + ((lane & 15) >> 2)) * LD + 16 * (trG & 1) + 4 * (lane & 3);
+  const int q16_row = 8 * trG + ((lane & 15) >> 2), q16_col = 4 * (lane & 3);
+
+  const float sl2 = a.scale * kLog2e;
+  const uint16_t* Qg = (const uint16_t*)a.q + (size_t)h * D;
+  const uint16_t* dOg = (const uint16_t*)a.d_o + (size_t)h * D;
+
+  for (int tq = 0; tq < L; tq += BQ) {
+    const int rows = min(BQ, L - tq);
+    __syncthreads();  // previous step is done with Qs, dOs, dSt
+    for (int idx = tid; idx < BQ * CH; idx += NT) {
+      const int t = idx / CH, c = idx % CH;
+      const bool ok = t < rows;
+      const size_t off = (size_t)(seq0 + tq + t) * rs + 8 * c;
+      lds_write16(&Qs[t * LD + 8 * c], ok ? gload16(Qg + off) : u32x4{});
+      lds_write16(&dOs[t * LD + 8 * c], ok ? gload16(dOg + off) : u32x4{});
+    }
+    if (PHI == 0 && tid < BQ) {
+      const bool ok = tid < rows;
+      const size_t r = (size_t)(seq0 + tq + tid) * H + h;
+      lse_s[tid] = ok ? a.lse[r] * kLog2e : INFINITY;
+      dvec_s[tid] = ok ? a.dvec[r] : 0.f;
+    }
+    __syncthreads();
+
+    // S = Q K^T and dP = dO V^T for the wave's 32 context rows.
+    f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 qa = lds_read8(&Qs[lr * LD + 16 * ks + 8 * g]);
+      const bf16x8 kb = lds_read8(&Kc[jl * LD + 16 * ks + 8 * g]);
+      S = mfma32(qa, kb, S);
+      const bf16x8 da = lds_read8(&dOs[lr * LD + 16 * ks + 8 * g]);
+      dP = mfma32(da, vf[ks], dP);
+    }
+
+    // Lane (j + 32 g), register r: token t = 8 (r / 4) + 4 g + r % 4 of the step.
+    f32x16 P, dS;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 8 * (r >> 2) + 4 * g + (r & 3);
+      float p, ds;
+      if (PHI == 0) {
+        p = fast_exp2(S[r] * sl2 - lse_s[t]);
+        ds = p * (dP[r] - dvec_s[t]);
+      } else {
+        const float s = S[r] * a.scale;
+        const float sg = fast_sigmoid(s);
+        p = s * sg;
+        ds = dP[r] * sg * (1.0f + s * (1.0f - sg));
+      }
+      if (!jvalid) {
+        p = 0.f;
+        ds = 0.f;
+      }
+      P[r] = p;
+      dS[r] = ds * a.scale;
+    }
+
+    // dS^T rows of this wave into LDS: row jl, tokens 8 q + 4 g .. + 3.
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
+      v[0] = f2bf(dS[4 * q4 + 0]); v[1] = f2bf(dS[4 * q4 + 1]);
+      v[2] = f2bf(dS[4 * q4 + 2]); v[3] = f2bf(dS[4 * q4 + 3]);
+      *(GDPA_LDS bf16x4*)(&dSt[jl * LDT + 8 * q4 + 4 * g]) = v;
+    }
+
+    // dV += P^T dO, dK += dS^T Q (contraction over the 32 tokens of the step).
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 pa = pack_c8(P, kk);
+      const bf16x8 sa = pack_c8(dS, kk);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int o = 16 * kk * LD + tr_off + 32 * dt;
+        const bf16x8 dob = cat8(lds_read_tr4(&dOs[o]), lds_read_tr4(&dOs[o + 8 * LD]));
+        dV[dt] = mfma32(pa, dob, dV[dt]);
+        const bf16x8 qb = cat8(lds_read_tr4(&Qs[o]), lds_read_tr4(&Qs[o + 8 * LD]));
+        dK[dt] = mfma32(sa, qb, dK[dt]);
+      }
+    }
+    __syncthreads();  // dS^T complete
+
+    // dQ[32 x D] = dS[32 x NJ] K[NJ x D] with 16x16x32 tiles; wave w takes TPW tiles.
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tile = wave * TPW + i;
+      const int t0 = 16 * (tile / (D / 16)), d0 = 16 * (tile % (D / 16));
+      f32x4 acc = f32x4{};
+#pragma unroll 4
+      for (int js = 0; js < NJ; js += 32) {
+        const int ra = (js + q16_row) * LDT + t0 + q16_col;
+        const bf16x8 av = cat8(lds_read_tr4(&dSt[ra]), lds_read_tr4(&dSt[ra + 4 * LDT]));
+        const int rb = (js + q16_row) * LD + d0 + q16_col;
+        const bf16x8 bv = cat8(lds_read_tr4(&Kc[rb]), lds_read_tr4(&Kc[rb + 4 * LD]));
+        acc = mfma16(av, bv, acc);
+      }
+      // Lane (d + 16 q), register r: token t0 + 4 q + r, column d0 + lane % 16.
+      const int d = d0 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 4 * (lane >> 4) + r;
+        if (t < rows) {
+          const size_t idx = (size_t)(seq0 + tq + t) * rs + (size_t)h * D + d;
+          if (nch == 1) {
+            uint16_t* dqp = (uint16_t*)a.dq + idx;
+            float v = acc[r];
+            if (a.accum_dq) v += bf2f(*dqp);
+            *dqp = __builtin_bit_cast(uint16_t, f2bf(v));
+          } else {
+            atomicAdd(a.dq_acc + idx, acc[r]);
+          }
+        }
+      }
+    }
+  }
+
+  // dK, dV: lane (d + 32 g), register r holds context row 32 w + 8 (r / 4) + 4 g + r % 4.
+  uint16_t* dkp = (uint16_t*)a.dk + ((size_t)b * n * H + h) * D;
+  uint16_t* dvp = (uint16_t*)a.dv + ((size_t)b * n * H + h) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + 32 * wave + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (j < n) {
+        const size_t idx = (size_t)j * rs + 32 * dt + lr;
+        dkp[idx] = __builtin_bit_cast(uint16_t, f2bf(dK[dt][r]));
+        dvp[idx] = __builtin_bit_cast(uint16_t, f2bf(dV[dt][r]));
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path
+// ---------------------------------------------------------------------------
+
+template <int D, int PHI>
+__device__ __forceinline__ void f32_ds(float s_raw, float dp, float scale, float lse, float dvec,
+                                       float& p, float& ds) {
+  const float s = s_raw * scale;
+  if (PHI == 0) {
+    p = expf(s - lse);
+    ds = p * (dp - dvec);
+  } else {
+    const float sg = 1.0f / (1.0f + expf(-s));
+    p = s * sg;
+    ds = dp * sg * (1.0f + s * (1.0f - sg));
+  }
+}
+
+// dQ: one thread per (token, head).
+template <int D, int PHI>
+__global__ __launch_bounds__(128) void bwd_f32_dq_kernel(const BwdArgs a) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.T * a.H) return;
+  const int t = idx / a.H, h = idx - t * a.H;
+  const int b = find_sample(a.offsets, a.B, t);
+  const size_t rs = (size_t)a.H * D;
+  const float* qp = (const float*)a.q + (size_t)t * rs + (size_t)h * D;
+  const float* dop = (const float*)a.d_o + (size_t)t * rs + (size_t)h * D;
+  const float lse = PHI == 0 ? a.lse[(size_t)t * a.H + h] : 0.f;
+  const float dvec = PHI == 0 ? a.dvec[(size_t)t * a.H + h] : 0.f;
+  float acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) acc[e] = 0.f;
+  const float* Kb = (const float*)a.k + ((size_t)b * a.n * a.H + h) * D;
+  const float* Vb = (const float*)a.v + ((size_t)b * a.n * a.H + h) * D;
+  for (int j = 0; j < a.n; ++j) {
+    const float* kj = Kb + (size_t)j * rs;
+    const float* vj = Vb + (size_t)j * rs;
+    float s = 0.f, dp = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      s = fmaf(qp[e], kj[e], s);
+      dp = fmaf(dop[e], vj[e], dp);
+    }
+    float p, ds;
+    f32_ds<D, PHI>(s, dp, a.scale, lse, dvec, p, ds);
+    ds *= a.scale;
+#pragma unroll
+    for (int e = 0; e < D; ++e) acc[e] = fmaf(ds, kj[e], acc[e]);
+  }
+  float* dqp = (float*)a.dq + (size_t)t * rs + (size_t)h * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) dqp[e] = acc[e] + (a.accum_dq ? dqp[e] : 0.f);
+}
+
+// dK, dV: one thread per (sample, context row, head, 32-column slice).
+template <int D, int PHI>
+__global__ __launch_bounds__(128) void bwd_f32_dkdv_kernel(const BwdArgs a) {
+  constexpr int DS = D / 32;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long)a.B * a.n * a.H * DS) return;
+  const int sl = idx % DS;
+  const long bjh = idx / DS;
+  const int h = bjh % a.H;
+  const long bj = bjh / a.H;
+  const int j = bj % a.n;
+  const int b = (int)(bj / a.n);
+  const size_t rs = (size_t)a.H * D;
+  const float* kj = (const float*)a.k + ((size_t)b * a.n + j) * rs + (size_t)h * D;
+  const float* vj = (const float*)a.v + ((size_t)b * a.n + j) * rs + (size_t)h * D;
+  float gk[32], gv[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    gk[e] = 0.f;
+    gv[e] = 0.f;
+  }
+  for (int t = a.offsets[b]; t < a.offsets[b + 1]; ++t) {
+    const float* qp = (const float*)a.q + (size_t)t * rs + (size_t)h * D;
+    const float* dop = (const float*)a.d_o + (size_t)t * rs + (size_t)h * D;
+    float s = 0.f, dp = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      s = fmaf(qp[e], kj[e], s);
+      dp = fmaf(dop[e], vj[e], dp);
+    }
+    const float lse = PHI == 0 ? a.lse[(size_t)t * a.H + h] : 0.f;
+    const float dvec = PHI == 0 ? a.dvec[(size_t)t * a.H + h] : 0.f;
+    float p, ds;
+    f32_ds<D, PHI>(s, dp, a.scale, lse, dvec, p, ds);
+    ds *= a.scale;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      gv[e] = fmaf(p, dop[32 * sl + e], gv[e]);
+      gk[e] = fmaf(ds, qp[32 * sl + e], gk[e]);
+    }
+  }
+  float* dkp = (float*)a.dk + ((size_t)b * a.n + j) * rs + (size_t)h * D + 32 * sl;
+  float* dvp = (float*)a.dv + ((size_t)b * a.n + j) * rs + (size_t)h * D + 32 * sl;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    dkp[e] = gk[e];
+    dvp[e] = gv[e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+int bwd_bf16_waves(int d, int n) {
+  // 8 waves (256 context rows) per work-group; 4 when the context is short
+  // or the head is narrow.
+  if (d == 32) return 4;
+  return n <= 128 ? 4 : 8;
+}
+
+template <int D, int NW>
+static hipError_t bwd_bf16_dw(const BwdArgs& a, int phi, hipStream_t s) {
+  const long items = (long)a.B * a.H * a.n_chunks;
+  if (items == 0) return hipSuccess;
+  const dim3 g((unsigned)items), blk(NW * 64);
+  if (phi == 0) hipLaunchKernelGGL((bwd_bf16_kernel<D, 0, NW>), g, blk, 0, s, a);
+  else hipLaunchKernelGGL((bwd_bf16_kernel<D, 1, NW>), g, blk, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, hipStream_t s) {
+  if (d == 32 && waves == 4) return bwd_bf16_dw<32, 4>(a, phi, s);
+  if (d == 64 && waves == 4) return bwd_bf16_dw<64, 4>(a, phi, s);
+  if (d == 64 && waves == 8) return bwd_bf16_dw<64, 8>(a, phi, s);
+  if (d == 128 && waves == 4) return bwd_bf16_dw<128, 4>(a, phi, s);
+  if (d == 128 && waves == 8) return bwd_bf16_dw<128, 8>(a, phi, s);
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+static hipError_t bwd_f32_d(const BwdArgs& a, int phi, hipStream_t s) {
+  const long nq = (long)a.T * a.H;
+  const long nkv = (long)a.B * a.n * a.H * (D / 32);
+  // dK/dV first: with an accumulated dQ the dQ buffer may be the dO buffer itself.
+  if (nkv > 0) {
+    const dim3 g((unsigned)((nkv + 127) / 128)), blk(128);
+    if (phi == 0) hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, 0>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, 1>), g, blk, 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (nq > 0) {
+    const dim3 g((unsigned)((nq + 127) / 128)), blk(128);
+    if (phi == 0) hipLaunchKernelGGL((bwd_f32_dq_kernel<D, 0>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_f32_dq_kernel<D, 1>), g, blk, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_f32(const BwdArgs& a, int d, int phi, hipStream_t s) {
+  switch (d) {
+    case 32: return bwd_f32_d<32>(a, phi, s);
+    case 64: return bwd_f32_d<64>(a, phi, s);
+    case 128: return bwd_f32_d<128>(a, phi, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdpa

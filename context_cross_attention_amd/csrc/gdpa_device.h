@@ -1,0 +1,110 @@
+// Device-side helpers shared by the GDPA kernels (gfx950 / CDNA4 only).
+//
+// MFMA operand layouts used throughout (v_mfma_f32_32x32x16_bf16, wave64,
+// lane l, g = l / 32):
+//   A (32 x 16, M x K): lane l holds A[m = l % 32][k = 8 g + i], i = 0..7
+//   B (16 x 32, K x N): lane l holds B[k = 8 g + i][n = l % 32]
+//   C (32 x 32):        lane l, register r holds C[m = 8 (r / 4) + 4 g + r % 4][n = l % 32]
+// The contraction pairs item i of lane (m + 32 g) of A with item i of lane
+// (n + 32 g) of B, so any relabelling of k applied to both operands gives the
+// same product; the kernels use that freedom to feed a C tile straight back in
+// as an A or B operand.
+//
+// ds_read_b64_tr_b16 (transpose read from LDS, 4 x 16-bit per lane): within
+// each group of 16 lanes, output lane i, item r is element i % 4 of the 8-byte
+// chunk addressed by lane 4 r + i / 4 of the group.  If lane 4 r + c of group G
+// addresses row R_r(G), columns c0(G) + 4 c .. + 3 of a row-major 16-bit tile,
+// lane 16 G + i receives column c0(G) + i of rows R_0..R_3: a column-major
+// operand read from a row-major tile.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdpa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define GDPA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16-byte LDS read of 8 bf16 (address must be 16-byte aligned).
+__device__ __forceinline__ bf16x8 lds_read8(const uint16_t* p) {
+  return *(const GDPA_LDS bf16x8*)(p);
+}
+// Transpose read: see the header comment.  Address must be 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const uint16_t* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDPA_LDS s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ void lds_write16(uint16_t* p, u32x4 v) { *(GDPA_LDS u32x4*)(p) = v; }
+__device__ __forceinline__ void lds_write8(uint16_t* p, u32x2 v) { *(GDPA_LDS u32x2*)(p) = v; }
+
+__device__ __forceinline__ u32x4 gload16(const uint16_t* p) { return *(const u32x4*)(p); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ __bf16 f2bf(float x) { return (__bf16)x; }
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                        float a6, float a7) {
+  bf16x8 r;
+  r[0] = f2bf(a0); r[1] = f2bf(a1); r[2] = f2bf(a2); r[3] = f2bf(a3);
+  r[4] = f2bf(a4); r[5] = f2bf(a5); r[6] = f2bf(a6); r[7] = f2bf(a7);
+  return r;
+}
+// Registers 8 kk .. 8 kk + 7 of a 32x32 C tile as a bf16 operand.
+__device__ __forceinline__ bf16x8 pack_c8(const f32x16& c, int kk) {
+  return pack8(c[8 * kk + 0], c[8 * kk + 1], c[8 * kk + 2], c[8 * kk + 3], c[8 * kk + 4],
+               c[8 * kk + 5], c[8 * kk + 6], c[8 * kk + 7]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// sigmoid(s) with one exp2 and one reciprocal; exact limits 0 and 1 at the tails.
+__device__ __forceinline__ float fast_sigmoid(float s) {
+  return fast_rcp(1.0f + fast_exp2(-s * kLog2e));
+}
+
+__device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// Work-group id remapped so that the WGs of one XCD (hardware places WG i on
+// XCD i % 8) take a contiguous range of the work list; neighbouring work items
+// (the q-tiles of one sample and head) then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+  const int per = grid >> 3;  // grid is a multiple of 8
+  return (bid & 7) * per + (bid >> 3);
+}
+
+// Largest b in [0, B-1] with tile_start[b] <= tile (tile_start non-decreasing,
+// tile_start[0] = 0).
+__device__ __forceinline__ int find_sample(const int32_t* __restrict__ tile_start, int B, int tile) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace gdpa

@@ -1,0 +1,296 @@
+// GDPA forward (Kunlun paper summary, section 2.2, GDPA bullet: the personalised
+// FFN recast as one fused attention kernel with sequence tokens as queries and
+// context-derived weights as keys and values).
+//
+// bf16 path.  One work-group = 4 waves = one tile of 128 query rows of one
+// (sample, head); each wave owns 32 rows.  The sample's K and V are streamed
+// through LDS in blocks of 64 context rows and shared by the 4 waves.  Per block:
+//   S^T = K Q^T       (32x32x16 bf16 MFMA; A = K rows from LDS, B = the wave's
+//                      Q rows, held in registers for the whole tile)
+//   P   = phi(S)      (in registers: online softmax in base 2, or SiLU)
+//   O^T += V^T P^T    (A = V columns via LDS transpose reads, B = P straight
+//                      from the C layout of S^T, rounded to bf16)
+// Computing S^T rather than S puts one query row per lane, so the softmax row
+// max is a register max plus one cross-half exchange, and the C tile of S^T is
+// already in the B-operand layout that the second product needs.
+//
+// fp32 path: plain per-(token, head) loop in fp32, for the small fp32 workload.
+#include "gdpa_device.h"
+#include "gdpa_launch.h"
+
+namespace gdpa {
+
+template <int D, int PHI, bool RESID>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
+  constexpr int BM = kFwdTileRows, BN = 64, KS = D / 16, DT = D / 32, LD = D + 8;
+  constexpr int CH = D / 8;                   // 16-byte chunks per K/V row
+  constexpr int SI = (BN * CH + 255) / 256;   // staging chunks per thread per tensor
+  __shared__ __align__(16) uint16_t Ks[BN * LD];
+  __shared__ __align__(16) uint16_t Vs[BN * LD];
+
+  const int H = a.H, B = a.B, n = a.n;
+  const int total = a.tile_start[B];
+  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  if (wid >= total * H) return;
+  const int qtile = wid / H, h = wid - qtile * H;
+  const int b = find_sample(a.tile_start, B, qtile);
+  const int row0 = a.offsets[b] + (qtile - a.tile_start[b]) * BM;
+  const int rows = min(BM, a.offsets[b + 1] - row0);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int trow = wave * 32 + lr;
+  const bool tvalid = trow < rows;
+  const size_t rs = (size_t)H * D;  // token / context row stride in elements
+
+  // This lane's query row, as B operand: items i <-> d = 16 ks + 8 g + i.
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + (size_t)(row0 + trow) * rs + (size_t)h * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[ks] = tvalid ? as_bf16x8(gload16(qp + 16 * ks)) : bf16x8{};
+  }
+
+  const uint16_t* Kg = (const uint16_t*)a.k + ((size_t)b * n * H + h) * D;
+  const uint16_t* Vg = (const uint16_t*)a.v + ((size_t)b * n * H + h) * D;
+  u32x4 kreg[SI], vreg[SI];
+  auto gload_block = [&](int jb) {
+#pragma unroll
+    for (int i = 0; i < SI; ++i) {
+      const int idx = i * 256 + tid, j = idx / CH, c = idx % CH;
+      const bool ok = (idx < BN * CH) && (jb + j < n);
+      kreg[i] = ok ? gload16(Kg + (size_t)(jb + j) * rs + 8 * c) : u32x4{};
+      vreg[i] = ok ? gload16(Vg + (size_t)(jb + j) * rs + 8 * c) : u32x4{};
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int i = 0; i < SI; ++i) {
+      const int idx = i * 256 + tid, j = idx / CH, c = idx % CH;
+      if (idx < BN * CH) {
+        lds_write16(&Ks[j * LD + 8 * c], kreg[i]);
+        lds_write16(&Vs[j * LD + 8 * c], vreg[i]);
+      }
+    }
+  };
+
+  // Transpose-read addressing: lane 16 G + 4 r + c reads row 4 (G / 2) + r,
+  // columns 16 (G % 2) + 4 c of a 32-row slab (second read: rows + 8).  Lane
+  // (d + 32 g) then holds V[j][d] for j = 4 g + i (i < 4) and 8 + 4 g + i - 4,
+  // matching the row order of the S^T C tile.
+  const int trG = lane >> 4;
+  const int tr_off = (4 * (trG >> 1) + ((lane & 15) >> 2)) * LD + 16 * (trG & 1) + 4 * (lane & 3);
+
+  f32x16 O[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale * kLog2e;
+
+  gload_block(0);
+  for (int jb = 0; jb < n; jb += BN) {
+    __syncthreads();
+    store_block();
+    __syncthreads();
+    if (jb + BN < n) gload_block(jb + BN);
+
+    f32x16 S[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      S[mt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        S[mt] = mfma32(lds_read8(&Ks[(32 * mt + lr) * LD + 16 * ks + 8 * g]), qf[ks], S[mt]);
+    }
+
+    if (PHI == 0) {
+      // Online softmax over the context rows, base 2.
+      const bool tail = jb + BN > n;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float s = S[mt][r] * sl2;
+          if (tail) {
+            const int j = jb + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (j >= n) s = -INFINITY;
+          }
+          S[mt][r] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = fast_exp2(m_run - m_new);
+      l_run *= corr;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt] *= corr;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(S[mt][r] - m_new);
+          l_run += p;
+          S[mt][r] = p;
+        }
+      m_run = m_new;
+    } else {
+      // SiLU; rows past n are zero in K and V, and silu(0) = 0.
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = S[mt][r] * a.scale;
+          S[mt][r] = s * fast_sigmoid(s);
+        }
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 p = pack_c8(S[mt], kk);
+        const uint16_t* vb = &Vs[(32 * mt + 16 * kk) * LD + tr_off];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x4 lo = lds_read_tr4(vb + 32 * dt);
+          const bf16x4 hi = lds_read_tr4(vb + 8 * LD + 32 * dt);
+          O[dt] = mfma32(cat8(lo, hi), p, O[dt]);
+        }
+      }
+  }
+
+  if (PHI == 0) {
+    const float l_tot = l_run + wave_xor32(l_run);
+    const float inv = 1.0f / l_tot;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[dt] *= inv;
+    if (tvalid && g == 0 && a.lse != nullptr)
+      a.lse[(size_t)(row0 + trow) * H + h] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+  if (tvalid) {
+    // Lane (t, g), register r holds O[t][d = 32 dt + 8 (r / 4) + 4 g + r % 4].
+    const size_t base = (size_t)(row0 + trow) * rs + (size_t)h * D + 4 * g;
+    uint16_t* op = (uint16_t*)a.o + base;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int col = 32 * dt + 8 * q4;
+        float v0 = O[dt][4 * q4 + 0], v1 = O[dt][4 * q4 + 1];
+        float v2 = O[dt][4 * q4 + 2], v3 = O[dt][4 * q4 + 3];
+        if (RESID) {
+          const u32x2 rr = *(const u32x2*)((const uint16_t*)a.residual + base + col);
+          v0 += __uint_as_float(rr[0] << 16);
+          v1 += __uint_as_float(rr[0] & 0xffff0000u);
+          v2 += __uint_as_float(rr[1] << 16);
+          v3 += __uint_as_float(rr[1] & 0xffff0000u);
+        }
+        bf16x4 ov;
+        ov[0] = f2bf(v0); ov[1] = f2bf(v1); ov[2] = f2bf(v2); ov[3] = f2bf(v3);
+        *(bf16x4*)(op + col) = ov;
+      }
+  }
+}
+
+// fp32: one thread per (token, head), online softmax / SiLU accumulation in fp32.
+template <int D, int PHI, bool RESID>
+__global__ __launch_bounds__(128) void fwd_f32_kernel(const FwdArgs a) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.T * a.H) return;
+  const int t = idx / a.H, h = idx - t * a.H;
+  const int b = find_sample(a.offsets, a.B, t);
+  const size_t rs = (size_t)a.H * D;
+  const float* qp = (const float*)a.q + (size_t)t * rs + (size_t)h * D;
+  float q[D], acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    q[e] = qp[e];
+    acc[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const float* Kb = (const float*)a.k + ((size_t)b * a.n * a.H + h) * D;
+  const float* Vb = (const float*)a.v + ((size_t)b * a.n * a.H + h) * D;
+  for (int j = 0; j < a.n; ++j) {
+    const float* kj = Kb + (size_t)j * rs;
+    const float* vj = Vb + (size_t)j * rs;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) s = fmaf(q[e], kj[e], s);
+    s *= a.scale;
+    if (PHI == 0) {
+      const float m_new = fmaxf(m, s);
+      const float c = expf(m - m_new), p = expf(s - m_new);
+      l = l * c + p;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vj[e], acc[e] * c);
+      m = m_new;
+    } else {
+      const float p = s / (1.0f + expf(-s));
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vj[e], acc[e]);
+    }
+  }
+  float* op = (float*)a.o + (size_t)t * rs + (size_t)h * D;
+  const float* rp = RESID ? (const float*)a.residual + (size_t)t * rs + (size_t)h * D : nullptr;
+  const float inv = (PHI == 0) ? 1.0f / l : 1.0f;
+#pragma unroll
+  for (int e = 0; e < D; ++e) op[e] = acc[e] * inv + (RESID ? rp[e] : 0.f);
+  if (PHI == 0 && a.lse != nullptr) a.lse[(size_t)t * a.H + h] = m + logf(l);
+}
+
+int fwd_bf16_grid(int T, int B, int H) {
+  // sum_b ceil(L_b / BM) <= floor(T / BM) + B; round up to a multiple of 8 (XCDs).
+  const long tiles = (long)T / kFwdTileRows + B;
+  const long items = tiles * H;
+  return (int)((items + 7) / 8 * 8);
+}
+
+template <int D>
+static hipError_t fwd_bf16_d(const FwdArgs& a, int phi, bool resid, int grid, hipStream_t s) {
+  const dim3 g(grid), blk(256);
+  if (phi == 0) {
+    if (resid) hipLaunchKernelGGL((fwd_bf16_kernel<D, 0, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<D, 0, false>), g, blk, 0, s, a);
+  } else {
+    if (resid) hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, false>), g, blk, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int phi, bool resid, int grid, hipStream_t s) {
+  if (grid == 0) return hipSuccess;
+  switch (d) {
+    case 32: return fwd_bf16_d<32>(a, phi, resid, grid, s);
+    case 64: return fwd_bf16_d<64>(a, phi, resid, grid, s);
+    case 128: return fwd_bf16_d<128>(a, phi, resid, grid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+static hipError_t fwd_f32_d(const FwdArgs& a, int phi, bool resid, hipStream_t s) {
+  const long items = (long)a.T * a.H;
+  const dim3 g((unsigned)((items + 127) / 128)), blk(128);
+  if (phi == 0) {
+    if (resid) hipLaunchKernelGGL((fwd_f32_kernel<D, 0, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((fwd_f32_kernel<D, 0, false>), g, blk, 0, s, a);
+  } else {
+    if (resid) hipLaunchKernelGGL((fwd_f32_kernel<D, 1, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((fwd_f32_kernel<D, 1, false>), g, blk, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, int phi, bool resid, hipStream_t s) {
+  if ((long)a.T * a.H == 0) return hipSuccess;
+  switch (d) {
+    case 32: return fwd_f32_d<32>(a, phi, resid, s);
+    case 64: return fwd_f32_d<64>(a, phi, resid, s);
+    case 128: return fwd_f32_d<128>(a, phi, resid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdpa

@@ -1,0 +1,74 @@
+// Internal launch interface between the C ABI (gdpa_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdpa {
+
+// Forward q-tile height of the bf16 MFMA kernel (4 waves x 32 rows).
+constexpr int kFwdTileRows = 128;
+// Backward: each wave owns 32 context rows; q rows are visited 32 at a time.
+constexpr int kBwdRowsPerWave = 32;
+// Largest batch the on-device longest-first ordering sorts (larger: natural order).
+constexpr int kMaxSortBatch = 4096;
+
+struct FwdArgs {
+  const int32_t* offsets;     // [B+1]
+  const int32_t* tile_start;  // [B+1] q-tile prefix sums (bf16 path)
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* residual;
+  void* o;
+  float* lse;
+  int B, T, n, H;
+  float scale;
+};
+
+struct BwdArgs {
+  const int32_t* offsets;  // [B+1]
+  const int32_t* order;    // [B] samples, longest first
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* d_o;
+  const float* lse;   // [T*H] softmax
+  const float* dvec;  // [T*H] softmax: rowsum(dO * O)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;      // [T*H*d] fp32, used when the context rows span several work-groups
+  int B, T, n, H;
+  int n_chunks;       // work-groups per (sample, head)
+  float scale;
+  int accum_dq;
+};
+
+// Scheduling and small passes (gdpa_sched.hip).
+hipError_t launch_tile_scan(const int32_t* offsets, int B, int tile_rows, int32_t* tile_start,
+                            hipStream_t s);
+hipError_t launch_longest_first(const int32_t* offsets, int B, int32_t* order, hipStream_t s);
+hipError_t launch_softmax_dvec(const void* o, const void* d_o, int rows, int d, bool bf16,
+                               float* dvec, hipStream_t s);
+hipError_t launch_zero_f32(float* p, size_t count, hipStream_t s);
+hipError_t launch_dq_finalize(const float* acc, void* dq, size_t count, bool accumulate,
+                              hipStream_t s);
+
+// Forward (gdpa_fwd.hip).
+int fwd_bf16_grid(int T, int B, int H);
+hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int phi, bool residual, int grid,
+                           hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, int d, int phi, bool residual, hipStream_t s);
+
+// Backward (gdpa_bwd.hip).
+int bwd_bf16_waves(int d, int n);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdArgs& a, int d, int phi, hipStream_t s);
+
+// Weight-generation GEMM (gdpa_gemm.hip): C[M][N] = op(A) B, bf16 in/out, fp32 accumulate.
+// a_trans = false: A is [M][K]; a_trans = true: A is [K][M].  B is [K][N].
+hipError_t launch_gemm_bf16(bool a_trans, int M, int64_t N, int K, const void* A, const void* B,
+                            void* C, hipStream_t s);
+
+}  // namespace gdpa

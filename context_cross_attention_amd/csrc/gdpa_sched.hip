@@ -1,0 +1,192 @@
+// Jagged-batch scheduling and small auxiliary passes.
+//
+// The jagged batch (per-sample user histories of irregular length, the source
+// of the "irregular tensor shapes" that the Kunlun paper summary blames for low
+// utilisation in section 1) is turned into work lists on the device, so the host
+// never has to read the offsets back.
+#include "gdpa_device.h"
+#include "gdpa_launch.h"
+
+namespace gdpa {
+
+// tile_start[b] = sum_{b' < b} ceil(len(b') / tile_rows), tile_start[B] = total.
+// One work-group of 1024 threads scans the batch in chunks of 1024 samples.
+__global__ __launch_bounds__(1024) void tile_scan_kernel(const int32_t* __restrict__ off, int B,
+                                                         int tile_rows,
+                                                         int32_t* __restrict__ tile_start) {
+  __shared__ int32_t wave_sums[16];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += 1024) {
+    const int b = base + tid;
+    int c = 0;
+    if (b < B) {
+      const int len = off[b + 1] - off[b];
+      c = (len + tile_rows - 1) / tile_rows;
+    }
+    // inclusive scan inside the wave
+    int x = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wave_sums[wave] = x;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_sums[w];
+    const int excl = carry + before + x - c;
+    if (b < B) tile_start[b] = excl;
+    __syncthreads();
+    if (tid == 1023) carry = excl + c;
+    __syncthreads();
+  }
+  if (tid == 0) tile_start[B] = carry;
+}
+
+// order[] = samples sorted by length, longest first (ties by index), so that
+// the hardware dispatcher, which starts work-groups in index order, performs
+// longest-processing-time-first list scheduling.  Bitonic sort in LDS.
+__global__ __launch_bounds__(1024) void longest_first_kernel(const int32_t* __restrict__ off, int B,
+                                                             int32_t* __restrict__ order) {
+  __shared__ uint64_t key[kMaxSortBatch];
+  const int tid = threadIdx.x;
+  int N = 1;
+  while (N < B) N <<= 1;
+  for (int i = tid; i < N; i += 1024) {
+    if (i < B) {
+      const uint32_t len = (uint32_t)(off[i + 1] - off[i]);
+      key[i] = ((uint64_t)(0x7fffffffu - len) << 32) | (uint32_t)i;
+    } else {
+      key[i] = ~0ull;
+    }
+  }
+  __syncthreads();
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < N; i += 1024) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const bool up = (i & k) == 0;
+          const uint64_t a = key[i], c = key[ixj];
+          if ((a > c) == up) {
+            key[i] = c;
+            key[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < B; i += 1024) order[i] = (int32_t)(key[i] & 0xffffffffu);
+}
+
+__global__ void iota_kernel(int32_t* order, int B) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < B) order[i] = i;
+}
+
+// dvec[row] = sum_e O[row, e] * dO[row, e] in fp32 (softmax backward term).
+// One row of d elements per group of d/8 lanes.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void softmax_dvec_kernel(const void* __restrict__ o,
+                                                           const void* __restrict__ d_o, int rows,
+                                                           float* __restrict__ dvec) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 elements per lane
+  const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int row = gtid / LPR, part = gtid % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const size_t base = (size_t)row * D + part * 8;
+    if (BF16) {
+      const u32x4 a = *(const u32x4*)((const uint16_t*)o + base);
+      const u32x4 c = *(const u32x4*)((const uint16_t*)d_o + base);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc += __uint_as_float(a[i] << 16) * __uint_as_float(c[i] << 16);
+        acc += __uint_as_float(a[i] & 0xffff0000u) * __uint_as_float(c[i] & 0xffff0000u);
+      }
+    } else {
+      const float* a = (const float*)o + base;
+      const float* c = (const float*)d_o + base;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += a[i] * c[i];
+    }
+  }
+#pragma unroll
+  for (int d = LPR / 2; d > 0; d >>= 1) acc += __shfl_xor(acc, d, 64);
+  if (row < rows && part == 0) dvec[row] = acc;
+}
+
+__global__ void zero_f32_kernel(float* __restrict__ p, size_t count) {
+  const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i + 4 <= count) {
+    *(f32x4*)(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    for (size_t j = i; j < count; ++j) p[j] = 0.f;
+  }
+}
+
+// dq = bf16(acc (+ dq)) elementwise.
+__global__ void dq_finalize_kernel(const float* __restrict__ acc, uint16_t* __restrict__ dq,
+                                   size_t count, int accumulate) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float v = acc[i];
+  if (accumulate) v += bf2f(dq[i]);
+  dq[i] = __builtin_bit_cast(uint16_t, f2bf(v));
+}
+
+hipError_t launch_tile_scan(const int32_t* offsets, int B, int tile_rows, int32_t* tile_start,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(tile_scan_kernel, dim3(1), dim3(1024), 0, s, offsets, B, tile_rows,
+                     tile_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_longest_first(const int32_t* offsets, int B, int32_t* order, hipStream_t s) {
+  if (B <= kMaxSortBatch) {
+    hipLaunchKernelGGL(longest_first_kernel, dim3(1), dim3(1024), 0, s, offsets, B, order);
+  } else {
+    hipLaunchKernelGGL(iota_kernel, dim3((B + 255) / 256), dim3(256), 0, s, order, B);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_dvec(const void* o, const void* d_o, int rows, int d, bool bf16,
+                               float* dvec, hipStream_t s) {
+  const long threads = (long)rows * (d / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  if (rows == 0) return hipSuccess;
+#define GDPA_DVEC(D)                                                                            \
+  if (d == D) {                                                                                 \
+    if (bf16) hipLaunchKernelGGL((softmax_dvec_kernel<D, true>), grid, block, 0, s, o, d_o,     \
+                                 rows, dvec);                                                   \
+    else hipLaunchKernelGGL((softmax_dvec_kernel<D, false>), grid, block, 0, s, o, d_o, rows,   \
+                            dvec);                                                              \
+    return hipGetLastError();                                                                   \
+  }
+  GDPA_DVEC(32) GDPA_DVEC(64) GDPA_DVEC(128)
+#undef GDPA_DVEC
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero_f32(float* p, size_t count, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  const size_t threads = (count + 3) / 4;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p,
+                     count);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_finalize(const float* acc, void* dq, size_t count, bool accumulate,
+                              hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
+                     acc, (uint16_t*)dq, count, accumulate ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace gdpa

@@ -1,0 +1,137 @@
+/*
+ * gdpa.h - C ABI of the MI355X (gfx950) Generalized Dot-Product Attention library.
+ *
+ * GDPA (Kunlun paper summary, section 2.2 "low-level module optimisations",
+ * GDPA bullet) recasts the personalised FFN as one fused multi-head attention
+ * operator: the tokens of a sample's user history are the queries, and weights
+ * derived from that sample's non-sequential context are the keys and values
+ * (Telegram review of the paper, layer steps 1 and 2: K and V are made from the
+ * context features, the event sequence becomes Q and "looks at" them).
+ *
+ * For a jagged batch, sample b owns token rows offsets[b] .. offsets[b+1]-1.
+ * For every token t of sample b and head h:
+ *
+ *     s_j      = scale * < Q[t,h,:], K[b,j,h,:] >          j = 0 .. n_kv-1
+ *     p        = phi(s)    (row softmax over j, or SiLU elementwise)
+ *     O[t,h,:] = sum_j p_j V[b,j,h,:]
+ *
+ * With phi = SiLU and scale = 1 this is the per-sample two-layer FFN
+ * silu(x K^T) V.  The pages give no formula for phi, the scale, masking or
+ * normalisation; the readings taken are: no mask (a token sees every context
+ * row of its own sample and nothing of other samples), softmax over the n_kv
+ * context rows, scale chosen by the caller (1/sqrt(d) for softmax and 1 for
+ * SiLU are the usual values), d_v = d_qk = d, no bias.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers, caller-owned; the library never
+ *     allocates or frees them.  Tensors are dense row-major:
+ *       Q, O, dO, dQ, residual : [T][H][d]      (token-major, heads inner)
+ *       K, V, dK, dV           : [B][n_kv][H][d]
+ *       lse                    : [T][H] float32 (natural log)
+ *       offsets                : [B+1] int32, offsets[0] = 0, non-decreasing,
+ *                                offsets[B] = T, every length <= max_seqlen.
+ *     The offsets contents are the caller's contract (checking them on the
+ *     device would need a synchronisation); gdpa_check_offsets() checks a host
+ *     copy.  Empty samples (length 0) are allowed.
+ *   - dtype GDPA_BF16: bf16 tensors, fp32 accumulation, bf16 results rounded to
+ *     nearest even.  dtype GDPA_F32: fp32 tensors and fp32 arithmetic.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronises it.  Errors in the arguments are reported
+ *     before anything is launched.  A launch failure returns GDPA_ERR_HIP and
+ *     stores the hipError_t for gdpa_last_hip_error() (per thread).
+ *   - No exceptions cross the ABI.  The library keeps no mutable global state
+ *     and is safe to call from several threads.
+ */
+#ifndef GDPA_H
+#define GDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDPA_OK = 0,
+  GDPA_ERR_INVALID_ARGUMENT = 1,  /* null pointer, size out of range, non-finite scale */
+  GDPA_ERR_UNSUPPORTED = 2,       /* valid but not implemented: head_dim, dtype, flags */
+  GDPA_ERR_WORKSPACE_TOO_SMALL = 3,
+  GDPA_ERR_HIP = 4                /* a HIP launch or runtime call failed */
+} gdpa_status;
+
+typedef enum { GDPA_PHI_SOFTMAX = 0, GDPA_PHI_SILU = 1 } gdpa_phi;
+typedef enum { GDPA_F32 = 0, GDPA_BF16 = 1 } gdpa_dtype;
+
+/* gdpa_fwd: O = residual + GDPA(...) instead of O = GDPA(...). `residual` may alias `q`. */
+#define GDPA_FWD_RESIDUAL 0x1u
+/* gdpa_bwd: dQ += result instead of dQ = result.  With this flag `dq` may alias `d_o`
+ * (the stacked-layer backward dX_l = dX_{l+1} + dQ_l, done in place). */
+#define GDPA_BWD_ACCUM_DQ 0x2u
+
+typedef struct {
+  int32_t batch;         /* B >= 1 */
+  int32_t total_tokens;  /* T = offsets[B] >= 0 */
+  int32_t max_seqlen;    /* >= every sample length (host-known bound) */
+  int32_t n_kv;          /* context rows per sample, >= 1 */
+  int32_t heads;         /* H >= 1 */
+  int32_t head_dim;      /* d: 32, 64 or 128 */
+  int32_t phi;           /* gdpa_phi */
+  float scale;           /* finite; applied to the scores before phi */
+  int32_t dtype;         /* gdpa_dtype of Q, K, V, O, residual, dO, dQ, dK, dV */
+  uint32_t flags;        /* GDPA_FWD_RESIDUAL, GDPA_BWD_ACCUM_DQ */
+} gdpa_problem;
+
+/* Bytes of device workspace gdpa_fwd (backward = 0) or gdpa_bwd (backward = 1)
+ * needs for this problem; 0 if the problem is invalid.  The workspace is
+ * scratch owned by the caller; its contents need no initialisation and are
+ * undefined after the call.  Two calls in flight at once need two workspaces. */
+size_t gdpa_workspace_bytes(const gdpa_problem* p, int backward);
+
+/* Forward.  q [T,H,d], k, v [B,n,H,d] in; o [T,H,d] out (overwritten).
+ * lse [T,H] float32: log-sum-exp of each score row (natural log) - written when
+ * non-NULL and phi = softmax, required by gdpa_bwd for softmax; ignored for SiLU.
+ * residual [T,H,d]: added to O when GDPA_FWD_RESIDUAL is set (may alias q;
+ * must not alias o unless it is the same buffer as q and o is not q). */
+gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* q,
+                     const void* k, const void* v, const void* residual, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of sum(O * dO).  In: q, k, v, d_o, and for softmax also o and lse
+ * from gdpa_fwd (ignored for SiLU, may be NULL).  Out: dq [T,H,d] (overwritten,
+ * or accumulated with GDPA_BWD_ACCUM_DQ), dk, dv [B,n,H,d] (overwritten; each is
+ * the sum over the sample's own tokens, zero for an empty sample).  With SiLU,
+ * o and lse are not read and may be NULL. */
+gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
+                     const void* v, const void* o, const float* lse, const void* d_o, void* dq,
+                     void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Weight generation (paper summary section 2.1, interaction block; Telegram
+ * review, layer step 1: K and V are obtained from the context features), read
+ * as one linear map per layer:  out[B, cols] = ctx[B, ctx_dim] * w[ctx_dim, cols],
+ * bf16 in and out, fp32 accumulation.  With cols = n_kv*H*d the output is K or V
+ * in the [B][n_kv][H][d] layout.  Requires cols % 8 == 0 and ctx_dim % 8 == 0. */
+gdpa_status gdpa_weightgen_fwd(int32_t batch, int32_t ctx_dim, int64_t cols, const void* ctx,
+                               const void* w, void* out, void* stream);
+
+/* Gradient of the weight-generation map w.r.t. w:  d_w[ctx_dim, cols] = ctx^T * d_out
+ * (overwritten), bf16 in and out, fp32 accumulation over the batch. */
+gdpa_status gdpa_weightgen_bwd_w(int32_t batch, int32_t ctx_dim, int64_t cols, const void* ctx,
+                                 const void* d_out, void* d_w, void* stream);
+
+/* Host-side check of a HOST copy of offsets: returns GDPA_OK when offsets[0] = 0,
+ * the array is non-decreasing, offsets[B] = total_tokens and every length is at
+ * most max_seqlen; GDPA_ERR_INVALID_ARGUMENT otherwise. */
+gdpa_status gdpa_check_offsets(const int32_t* host_offsets, int32_t batch, int32_t total_tokens,
+                               int32_t max_seqlen);
+
+/* Static description of a status code. */
+const char* gdpa_status_str(gdpa_status s);
+
+/* hipError_t of the last GDPA_ERR_HIP returned on this thread (0 if none). */
+int gdpa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDPA_H */

@@ -1,0 +1,122 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared entry
+point, and rejects invalid arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import context_cross_attention_amd as cca
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "gdpa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdpa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cca.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(cca.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def P(**kw):
+    base = dict(batch=2, total_tokens=10, max_seqlen=8, n_kv=4, heads=2, head_dim=64, phi=0,
+                scale=0.125, dtype=1, flags=0)
+    base.update(kw)
+    return cca.GdpaProblem(**base)
+
+
+V = ctypes.c_void_p(256)   # never dereferenced: every case fails validation first
+
+
+def fwd(lib, p, ws_bytes=1 << 20, **ptrs):
+    a = dict(offsets=V, q=V, k=V, v=V, residual=None, o=ctypes.c_void_p(512), lse=None, ws=V)
+    a.update(ptrs)
+    return lib.gdpa_fwd(ctypes.byref(p), a["offsets"], a["q"], a["k"], a["v"], a["residual"], a["o"],
+                        a["lse"], a["ws"], ws_bytes, None)
+
+
+def bwd(lib, p, ws_bytes=1 << 30, **ptrs):
+    a = dict(offsets=V, q=V, k=V, v=V, o=V, lse=V, do=V, dq=ctypes.c_void_p(1024),
+             dk=ctypes.c_void_p(2048), dv=ctypes.c_void_p(4096), ws=V)
+    a.update(ptrs)
+    return lib.gdpa_bwd(ctypes.byref(p), a["offsets"], a["q"], a["k"], a["v"], a["o"], a["lse"],
+                        a["do"], a["dq"], a["dk"], a["dv"], a["ws"], ws_bytes, None)
+
+
+INVALID, UNSUPPORTED, WS_SMALL = 1, 2, 3
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), INVALID), (dict(n_kv=0), INVALID), (dict(heads=0), INVALID),
+    (dict(total_tokens=-1), INVALID), (dict(phi=7), INVALID), (dict(dtype=9), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(head_dim=48), UNSUPPORTED), (dict(head_dim=256), UNSUPPORTED),
+    (dict(flags=0x80), UNSUPPORTED), (dict(flags=cca.BWD_ACCUM_DQ), INVALID),
+])
+def test_fwd_rejects_bad_problem(lib, kw, status):
+    assert fwd(lib, P(**kw)) == status
+
+
+def test_fwd_rejects_bad_pointers(lib):
+    assert lib.gdpa_fwd(None, V, V, V, V, None, V, None, V, 1 << 20, None) == INVALID
+    assert fwd(lib, P(), offsets=None) == INVALID
+    assert fwd(lib, P(), k=None) == INVALID
+    assert fwd(lib, P(), o=None) == INVALID
+    assert fwd(lib, P(flags=cca.FWD_RESIDUAL), residual=None) == INVALID
+    assert fwd(lib, P(), o=V) == INVALID          # output aliases an input
+    assert fwd(lib, P(), ws=None) == WS_SMALL
+    assert fwd(lib, P(), ws_bytes=4) == WS_SMALL
+
+
+def test_bwd_rejects_bad_arguments(lib):
+    assert bwd(lib, P(head_dim=16)) == UNSUPPORTED
+    assert bwd(lib, P(), lse=None) == INVALID      # softmax needs lse
+    assert bwd(lib, P(), o=None) == INVALID
+    assert bwd(lib, P(), dk=None) == INVALID
+    assert bwd(lib, P(flags=cca.FWD_RESIDUAL)) == INVALID
+    assert bwd(lib, P(), dq=V, do=V) == INVALID    # in-place dQ needs the accumulate flag
+    assert bwd(lib, P(), dk=ctypes.c_void_p(2048), dv=ctypes.c_void_p(2048)) == INVALID
+    assert bwd(lib, P(), ws_bytes=8) == WS_SMALL
+
+
+def test_weightgen_rejects_bad_arguments(lib):
+    assert lib.gdpa_weightgen_fwd(0, 512, 1024, V, V, V, None) == INVALID
+    assert lib.gdpa_weightgen_fwd(4, 512, 1020, V, V, V, None) == UNSUPPORTED
+    assert lib.gdpa_weightgen_fwd(4, 500, 1024, V, V, V, None) == UNSUPPORTED
+    assert lib.gdpa_weightgen_bwd_w(4, 512, 1024, V, None, V, None) == INVALID
+
+
+def test_workspace_sizes(lib):
+    assert cca.workspace_bytes(P(head_dim=48), False) == 0
+    f = cca.workspace_bytes(P(batch=1000), False)
+    assert f >= 4 * 1001 and f % 256 == 0
+    # softmax backward keeps rowsum(dO*O) per (token, head); SiLU does not.
+    soft = cca.workspace_bytes(P(total_tokens=1000, phi=0), True)
+    silu = cca.workspace_bytes(P(total_tokens=1000, phi=1), True)
+    assert soft - silu >= 4 * 1000 * 2
+    # context rows beyond one backward work-group add an fp32 dQ buffer
+    big = cca.workspace_bytes(P(total_tokens=1000, phi=1, n_kv=1024, head_dim=128), True)
+    assert big - silu >= 4 * 1000 * 2 * 128
+
+
+def test_status_strings_and_offsets_check(lib):
+    assert lib.gdpa_status_str(0) == b"GDPA_OK"
+    assert lib.gdpa_status_str(3) == b"GDPA_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.gdpa_last_hip_error() == 0
+    assert cca.check_offsets([0, 3, 3, 10], 10, 7)
+    assert not cca.check_offsets([0, 3, 2, 10], 10, 8)     # decreasing
+    assert not cca.check_offsets([1, 3, 10], 10, 8)        # does not start at 0
+    assert not cca.check_offsets([0, 3, 10], 11, 8)        # wrong total
+    assert not cca.check_offsets([0, 3, 10], 10, 6)        # longer than max_seqlen
