@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""GDPA benchmark on one MI355X.
+
+Default workload: the stacked jagged workload - 4 residual GDPA layers with
+generated K/V, forward and backward, B=1024 samples with log-normal lengths
+(median 1024, max 8192, T = 1,438,675 tokens at seed 0), H=8, d=128, n_kv=256,
+context width 512, phi = SiLU.  One step runs every stage of the path: weight
+generation (K, V = C W), GDPA forward with the residual add, GDPA backward with
+dK/dV reduced per sample and dX = dX' + dQ, and the weight gradients C^T dK,
+C^T dV.
+
+`value` is GDPA forward+backward TFLOP/s over the whole step (algorithmic
+FLOPs 12*T*H*n*d per layer, the weight-generation time counted in the
+denominator, its FLOPs not in the numerator).  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config {2,3,4,5}] [--phi softmax|silu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = "GDPA fwd / fwd+bwd TFLOP/s and % of bf16 MFMA peak, jagged batch, 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
+    ap.add_argument("--phi", default=None, choices=[None, "softmax", "silu"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per launch
+# ---------------------------------------------------------------------------
+
+def gdpa_units(kind, T, B, H, d, n, phi, residual=False):
+    """(FLOPs, HBM bytes) per launch: each tensor moved once, bf16 data, fp32 lse/dvec."""
+    tok = T * H * d * 2
+    kv = B * n * H * d * 2
+    if kind == "gdpa_fwd":
+        flops = 4.0 * T * H * n * d
+        byts = 2 * tok + 2 * kv + (tok if residual else 0) + (T * H * 4 if phi == "softmax" else 0)
+    else:
+        flops = 8.0 * T * H * n * d
+        byts = 3 * tok + 4 * kv
+        if phi == "softmax":
+            byts += tok + 2 * T * H * 4  # O for rowsum(dO*O), lse, dvec round trip
+    return flops, byts
+
+
+def gemm_units(M, N, K):
+    return 2.0 * M * N * K, 2.0 * (M * K + K * N + M * N)
+
+
+class Marks:
+    """HIP events around library calls on the current stream, per category."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.open = {}
+        self.pairs = {}
+        self.enabled = False
+
+    def __call__(self, name, start):
+        if not self.enabled:
+            return
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        if start:
+            self.open[name] = ev
+        else:
+            self.pairs.setdefault(name, []).append((self.open.pop(name), ev))
+
+    def totals_ms(self):
+        return {k: sum(a.elapsed_time(b) for a, b in v) for k, v in self.pairs.items()}
+
+    def counts(self):
+        return {k: len(v) for k, v in self.pairs.items()}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the same inputs
+# ---------------------------------------------------------------------------
+
+def blas_threads():
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        n = [i["num_threads"] for i in info if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def pick_samples(lengths, per_token_flops, budget_flops, cap):
+    chosen, acc = [], 0.0
+    for b, L in enumerate(lengths):
+        if L == 0:
+            continue
+        chosen.append(b)
+        acc += L * per_token_flops
+        if acc >= budget_flops or len(chosen) >= cap:
+            break
+    return chosen
+
+
+def cpu_baseline_stacked(inp, cfg):
+    import numpy as np
+    from oracle import gdpa_oracle as orc
+    per_tok = 12.0 * cfg.layers * cfg.heads * cfg.n_kv * cfg.head_dim
+    samples = pick_samples(inp.lengths, per_tok, 1.2e11, 8)
+    off = inp.offsets.numpy().astype(np.int64)
+    rows = np.concatenate([np.arange(off[b], off[b + 1]) for b in samples])
+    sub_off = np.concatenate([[0], np.cumsum([inp.lengths[b] for b in samples])])
+    x0 = inp.x0[rows]
+    g = inp.do[rows]
+    ctx = inp.ctx[samples]
+    t0 = time.perf_counter()
+    xs = orc.stacked_forward(x0, sub_off, ctx, inp.w_k, inp.w_v, cfg.heads, cfg.n_kv, "silu")
+    orc.stacked_backward(xs, sub_off, ctx, inp.w_k, inp.w_v, g, cfg.heads, cfg.n_kv, "silu")
+    dt = time.perf_counter() - t0
+    tokens = int(sub_off[-1])
+    flops = per_tok * tokens
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"stacked {cfg.layers}-layer SiLU fwd+bwd incl. weight generation on samples "
+                      f"{samples[0]}..{samples[-1]} ({len(samples)} of {cfg.batch}, {tokens} tokens); "
+                      f"GDPA FLOPs {flops / 1e9:.1f} G in {dt:.1f} s (numpy float64)",
+            "seconds": round(dt, 2)}
+
+
+def cpu_baseline_single(inp, cfg, phi):
+    import numpy as np
+    from oracle import gdpa_oracle as orc
+    per_tok = (12.0 if cfg.backward else 4.0) * cfg.heads * cfg.n_kv * cfg.head_dim
+    samples = pick_samples(inp.lengths, per_tok, 2.5e11, cfg.batch)
+    t0 = time.perf_counter()
+    orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=samples)
+    if cfg.backward:
+        orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi, samples=samples)
+    dt = time.perf_counter() - t0
+    tokens = int(sum(inp.lengths[b] for b in samples))
+    flops = per_tok * tokens
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{'fwd+bwd' if cfg.backward else 'fwd'} {phi} on {len(samples)} of {cfg.batch} "
+                      f"samples ({tokens} tokens); {flops / 1e9:.1f} GFLOP in {dt:.1f} s (numpy float64)",
+            "seconds": round(dt, 2)}
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        msg = ("bench.py runs on one GPU only: GDPA shards by sample with no exchange in the "
+               "op itself, and this build measures the one-GPU share. Use --gpus 1.")
+        print(msg, file=sys.stderr)
+        print(json.dumps({"error": msg, "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import context_cross_attention_amd as cca
+    import gdpa_inputs as gi
+    from context_cross_attention_amd.stacked import StackedGdpa
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cca.load()
+    dev = torch.device("cuda:0")
+    cfg = gi.CONFIGS[args.config]
+    phi = args.phi or cfg.phis[0]
+    marks = Marks(torch)
+
+    t_gen = time.perf_counter()
+    if cfg.layers:
+        inp = gi.make_stacked_inputs(cfg, seed=args.seed)
+        T = int(inp.offsets[-1])
+        x0 = inp.x0.to(dev)
+        g = inp.do.to(dev)
+        off = inp.offsets.to(dev)
+        ctx = inp.ctx.to(dev)
+        wk = [w.to(dev) for w in inp.w_k]
+        wv = [w.to(dev) for w in inp.w_v]
+        model = StackedGdpa(off, ctx, wk, wv, cfg.heads, cfg.n_kv, T, phi="silu")
+
+        def step():
+            model.forward(x0, marks)
+            model.backward(g, marks)
+    else:
+        inp = gi.make_gdpa_inputs(cfg, seed=args.seed)
+        T = inp.total_tokens
+        q, off, k, v = (t.to(dev) for t in (inp.q, inp.offsets, inp.k, inp.v))
+        do = inp.do.to(dev) if inp.do is not None else None
+        o = torch.empty_like(q)
+        lse = torch.empty((T, cfg.heads), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+
+        def step():
+            marks("gdpa_fwd", True)
+            cca.fwd(q, off, k, v, phi=phi, out=o, lse=lse, workspace=ws)
+            marks("gdpa_fwd", False)
+            if cfg.backward:
+                marks("gdpa_bwd", True)
+                cca.bwd(q, off, k, v, o, lse, do, phi=phi, dq=dq, dk=dk, dv=dv)
+                marks("gdpa_bwd", False)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    print(f"# inputs ready in {t_gen:.1f} s: T={T}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks.enabled = True
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    marks.enabled = False
+    ms_per_step = wall * 1e3 / args.steps
+
+    B, H, d, n = cfg.batch, cfg.heads, cfg.head_dim, cfg.n_kv
+    layers = max(cfg.layers, 1)
+    fwd_f, fwd_b = gdpa_units("gdpa_fwd", T, B, H, d, n, phi, residual=bool(cfg.layers))
+    bwd_f, bwd_b = gdpa_units("gdpa_bwd", T, B, H, d, n, phi)
+    gdpa_flops = layers * (fwd_f + (bwd_f if cfg.backward else 0.0))
+    wg_flops = 0.0
+    units = {"gdpa_fwd": (fwd_f, fwd_b), "gdpa_bwd": (bwd_f, bwd_b)}
+    if cfg.layers:
+        cols = n * H * d
+        f1, b1 = gemm_units(B, cols, cfg.ctx_dim)
+        f2, b2 = gemm_units(cfg.ctx_dim, cols, B)
+        units["weightgen_fwd"] = (2 * f1, 2 * b1)   # K and V per marked region
+        units["weightgen_bwd"] = (2 * f2, 2 * b2)
+        wg_flops = layers * 2 * (f1 + f2)
+    value = gdpa_flops / (ms_per_step * 1e-3) / 1e12
+
+    totals = marks.totals_ms()
+    counts = marks.counts()
+    per_launch = {k: totals[k] / counts[k] for k in totals}
+    breakdown = {k: round(totals[k] / args.steps, 4) for k in totals}
+    dom = max(totals, key=lambda k: totals[k])
+    f_dom, b_dom = units[dom]
+    t_dom = per_launch[dom] * 1e-3
+    t_mfma, t_hbm = f_dom / (PEAK_BF16_TFLOPS * 1e12), b_dom / (PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(b_dom / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(f_dom / t_dom / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["launch_ms"] = round(per_launch[dom], 4)
+    roof["algorithmic_per_launch"] = {"flops": f_dom, "bytes": b_dom}
+    roof["other_bound_frac"] = round((f_dom / t_dom / 1e12) / PEAK_BF16_TFLOPS, 4) if roof["bound"] == "hbm" \
+        else round((b_dom / t_dom / 1e9) / PEAK_HBM_GBS, 4)
+
+    if cfg.layers:
+        workload = (f"stacked GDPA {cfg.layers} layers fwd+bwd incl. weight generation: B={B} samples, "
+                    f"lengths log-normal (median {cfg.lengths[1]}, max {cfg.lengths[2]}), T={T}, H={H}, "
+                    f"d={d}, n_kv={n}, ctx_dim={cfg.ctx_dim}, phi=SiLU, residual between layers")
+    else:
+        workload = f"GDPA {'fwd+bwd' if cfg.backward else 'fwd'}: {cfg.name}, phi={phi}, T={T}"
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws; lengths, values and weights as in gdpa_inputs.py)",
+        "config": {"workload": workload, "global_batch": B, "tokens": T, "heads": H, "head_dim": d,
+                   "n_kv": n, "layers": cfg.layers or 1, "phi": phi, "seed": args.seed},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "gdpa_tflop_per_step": round(gdpa_flops / 1e12, 3),
+        "e2e_tflops_incl_weightgen": round((gdpa_flops + wg_flops) / (ms_per_step * 1e-3) / 1e12, 2),
+        "breakdown_ms_per_step": breakdown,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline_stacked(inp, cfg) if cfg.layers else cpu_baseline_single(inp, cfg, phi)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

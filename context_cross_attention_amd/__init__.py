@@ -24,6 +24,7 @@ PHI = {"softmax": 0, "silu": 1}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 FWD_RESIDUAL = 0x1
 BWD_ACCUM_DQ = 0x2
+BWD_RESIDUAL = 0x4
 
 STATUS = {0: "GDPA_OK", 1: "GDPA_ERR_INVALID_ARGUMENT", 2: "GDPA_ERR_UNSUPPORTED",
           3: "GDPA_ERR_WORKSPACE_TOO_SMALL", 4: "GDPA_ERR_HIP"}
@@ -177,12 +178,13 @@ def fwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
 def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         o: Optional[torch.Tensor], lse: Optional[torch.Tensor], do: torch.Tensor,
         phi: str = "softmax", scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
-        accumulate_dq: bool = False, dk: Optional[torch.Tensor] = None,
+        accumulate_dq: bool = False, residual: bool = False, dk: Optional[torch.Tensor] = None,
         dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """GDPA backward of sum(O * dO).  Returns (dq, dk, dv).
 
     For softmax, o and lse are the forward's outputs; for SiLU they are unused.
     With accumulate_dq, dq (which may be `do` itself) receives dq + dQ.
+    With residual, dq receives do + dQ: the gradient of O = Q + GDPA(Q).
     """
     lib = load()
     B, n, H, d = k.shape
@@ -203,6 +205,8 @@ def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         if dq is None:
             raise ValueError("accumulate_dq needs dq")
         flags |= BWD_ACCUM_DQ
+    if residual:
+        flags |= BWD_RESIDUAL
     if dq is None:
         dq = torch.empty_like(q)
     dk = torch.empty_like(k) if dk is None else dk

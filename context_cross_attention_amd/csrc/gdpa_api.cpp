@@ -34,7 +34,8 @@ gdpa_status check_problem(const gdpa_problem* p) {
   if ((int64_t)p->total_tokens * p->heads > INT32_MAX) return GDPA_ERR_INVALID_ARGUMENT;
   if ((int64_t)p->batch * p->n_kv * p->heads > INT32_MAX) return GDPA_ERR_INVALID_ARGUMENT;
   if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) return GDPA_ERR_UNSUPPORTED;
-  if (p->flags & ~(uint32_t)(GDPA_FWD_RESIDUAL | GDPA_BWD_ACCUM_DQ)) return GDPA_ERR_UNSUPPORTED;
+  if (p->flags & ~(uint32_t)(GDPA_FWD_RESIDUAL | GDPA_BWD_ACCUM_DQ | GDPA_BWD_RESIDUAL))
+    return GDPA_ERR_UNSUPPORTED;
   return GDPA_OK;
 }
 
@@ -90,7 +91,7 @@ gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* 
   if (p->total_tokens > 0 && (q == nullptr || o == nullptr)) return GDPA_ERR_INVALID_ARGUMENT;
   const bool resid = (p->flags & GDPA_FWD_RESIDUAL) != 0;
   if (resid && residual == nullptr && p->total_tokens > 0) return GDPA_ERR_INVALID_ARGUMENT;
-  if (p->flags & GDPA_BWD_ACCUM_DQ) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->flags & (GDPA_BWD_ACCUM_DQ | GDPA_BWD_RESIDUAL)) return GDPA_ERR_INVALID_ARGUMENT;
   if (resid && residual == o && residual != q) return GDPA_ERR_INVALID_ARGUMENT;
   if (o != nullptr && (o == q || o == k || o == v)) return GDPA_ERR_INVALID_ARGUMENT;
   const size_t need = fwd_workspace(p);
@@ -136,7 +137,9 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
     return GDPA_ERR_INVALID_ARGUMENT;
   if (p->flags & GDPA_FWD_RESIDUAL) return GDPA_ERR_INVALID_ARGUMENT;
   const bool accum = (p->flags & GDPA_BWD_ACCUM_DQ) != 0;
-  if (dq != nullptr && dq == d_o && !accum) return GDPA_ERR_INVALID_ARGUMENT;
+  const bool dq_resid = (p->flags & GDPA_BWD_RESIDUAL) != 0;
+  if (accum && dq_resid) return GDPA_ERR_INVALID_ARGUMENT;
+  if (dq != nullptr && dq == d_o && !accum && !dq_resid) return GDPA_ERR_INVALID_ARGUMENT;
   if (dk == dv || dk == k || dk == v || dv == k || dv == v) return GDPA_ERR_INVALID_ARGUMENT;
   const BwdPlan pl = bwd_plan(p);
   if (workspace == nullptr || workspace_bytes < pl.total) return GDPA_ERR_WORKSPACE_TOO_SMALL;
@@ -162,7 +165,7 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
   a.H = p->heads;
   a.n_chunks = pl.chunks;
   a.scale = p->scale;
-  a.accum_dq = accum ? 1 : 0;
+  a.dq_base = accum ? (const void*)dq : (dq_resid ? d_o : nullptr);
 
   const size_t TH = (size_t)p->total_tokens * p->heads;
   hipError_t e = hipSuccess;
@@ -181,7 +184,7 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
   }
   e = gdpa::launch_bwd_bf16(a, p->head_dim, p->phi, pl.waves, s);
   if (e != hipSuccess) return hip_status(e);
-  if (pl.need_acc) e = gdpa::launch_dq_finalize(a.dq_acc, dq, TH * p->head_dim, accum, s);
+  if (pl.need_acc) e = gdpa::launch_dq_finalize(a.dq_acc, a.dq_base, dq, TH * p->head_dim, s);
   return hip_status(e);
 }
 

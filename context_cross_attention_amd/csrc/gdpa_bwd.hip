@@ -187,10 +187,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
         if (t < rows) {
           const size_t idx = (size_t)(seq0 + tq + t) * rs + (size_t)h * D + d;
           if (nch == 1) {
-            uint16_t* dqp = (uint16_t*)a.dq + idx;
             float v = acc[r];
-            if (a.accum_dq) v += bf2f(*dqp);
-            *dqp = __builtin_bit_cast(uint16_t, f2bf(v));
+            if (a.dq_base != nullptr) v += bf2f(((const uint16_t*)a.dq_base)[idx]);
+            ((uint16_t*)a.dq)[idx] = __builtin_bit_cast(uint16_t, f2bf(v));
           } else {
             atomicAdd(a.dq_acc + idx, acc[r]);
           }
@@ -265,9 +264,11 @@ __global__ __launch_bounds__(128) void bwd_f32_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < D; ++e) acc[e] = fmaf(ds, kj[e], acc[e]);
   }
-  float* dqp = (float*)a.dq + (size_t)t * rs + (size_t)h * D;
+  const size_t row = (size_t)t * rs + (size_t)h * D;
+  const float* basep = a.dq_base != nullptr ? (const float*)a.dq_base + row : nullptr;
+  float* dqp = (float*)a.dq + row;
 #pragma unroll
-  for (int e = 0; e < D; ++e) dqp[e] = acc[e] + (a.accum_dq ? dqp[e] : 0.f);
+  for (int e = 0; e < D; ++e) dqp[e] = acc[e] + (basep != nullptr ? basep[e] : 0.f);
 }
 
 // dK, dV: one thread per (sample, context row, head, 32-column slice).
@@ -354,7 +355,7 @@ template <int D>
 static hipError_t bwd_f32_d(const BwdArgs& a, int phi, hipStream_t s) {
   const long nq = (long)a.T * a.H;
   const long nkv = (long)a.B * a.n * a.H * (D / 32);
-  // dK/dV first: with an accumulated dQ the dQ buffer may be the dO buffer itself.
+  // dK/dV first: the dQ buffer may be the dO buffer itself.
   if (nkv > 0) {
     const dim3 g((unsigned)((nkv + 127) / 128)), blk(128);
     if (phi == 0) hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, 0>), g, blk, 0, s, a);

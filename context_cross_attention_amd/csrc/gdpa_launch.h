@@ -42,7 +42,7 @@ struct BwdArgs {
   int B, T, n, H;
   int n_chunks;       // work-groups per (sample, head)
   float scale;
-  int accum_dq;
+  const void* dq_base;  // dq = dq_base + dQ when non-null (may alias dq or d_o)
 };
 
 // Scheduling and small passes (gdpa_sched.hip).
@@ -52,7 +52,7 @@ hipError_t launch_longest_first(const int32_t* offsets, int B, int32_t* order, h
 hipError_t launch_softmax_dvec(const void* o, const void* d_o, int rows, int d, bool bf16,
                                float* dvec, hipStream_t s);
 hipError_t launch_zero_f32(float* p, size_t count, hipStream_t s);
-hipError_t launch_dq_finalize(const float* acc, void* dq, size_t count, bool accumulate,
+hipError_t launch_dq_finalize(const float* acc, const void* base, void* dq, size_t count,
                               hipStream_t s);
 
 // Forward (gdpa_fwd.hip).

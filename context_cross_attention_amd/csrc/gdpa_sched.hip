@@ -129,13 +129,13 @@ __global__ void zero_f32_kernel(float* __restrict__ p, size_t count) {
   }
 }
 
-// dq = bf16(acc (+ dq)) elementwise.
-__global__ void dq_finalize_kernel(const float* __restrict__ acc, uint16_t* __restrict__ dq,
-                                   size_t count, int accumulate) {
+// dq = bf16(acc (+ base)) elementwise; base may alias dq.
+__global__ void dq_finalize_kernel(const float* __restrict__ acc, const uint16_t* base,
+                                   uint16_t* dq, size_t count) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
   float v = acc[i];
-  if (accumulate) v += bf2f(dq[i]);
+  if (base != nullptr) v += bf2f(base[i]);
   dq[i] = __builtin_bit_cast(uint16_t, f2bf(v));
 }
 
@@ -181,11 +181,11 @@ hipError_t launch_zero_f32(float* p, size_t count, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_dq_finalize(const float* acc, void* dq, size_t count, bool accumulate,
+hipError_t launch_dq_finalize(const float* acc, const void* base, void* dq, size_t count,
                               hipStream_t s) {
   if (count == 0) return hipSuccess;
   hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
-                     acc, (uint16_t*)dq, count, accumulate ? 1 : 0);
+                     acc, (const uint16_t*)base, (uint16_t*)dq, count);
   return hipGetLastError();
 }
 

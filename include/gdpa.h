@@ -65,9 +65,12 @@ typedef enum { GDPA_F32 = 0, GDPA_BF16 = 1 } gdpa_dtype;
 
 /* gdpa_fwd: O = residual + GDPA(...) instead of O = GDPA(...). `residual` may alias `q`. */
 #define GDPA_FWD_RESIDUAL 0x1u
-/* gdpa_bwd: dQ += result instead of dQ = result.  With this flag `dq` may alias `d_o`
- * (the stacked-layer backward dX_l = dX_{l+1} + dQ_l, done in place). */
+/* gdpa_bwd: dQ += result instead of dQ = result.  With this flag `dq` may alias `d_o`. */
 #define GDPA_BWD_ACCUM_DQ 0x2u
+/* gdpa_bwd: dQ = dO + result, the gradient of O = Q + GDPA(Q) with respect to Q
+ * (a residual layer whose queries are its input tokens).  `dq` may alias `d_o`.
+ * Not combined with GDPA_BWD_ACCUM_DQ. */
+#define GDPA_BWD_RESIDUAL 0x4u
 
 typedef struct {
   int32_t batch;         /* B >= 1 */
@@ -79,7 +82,7 @@ typedef struct {
   int32_t phi;           /* gdpa_phi */
   float scale;           /* finite; applied to the scores before phi */
   int32_t dtype;         /* gdpa_dtype of Q, K, V, O, residual, dO, dQ, dK, dV */
-  uint32_t flags;        /* GDPA_FWD_RESIDUAL, GDPA_BWD_ACCUM_DQ */
+  uint32_t flags;        /* GDPA_FWD_RESIDUAL, GDPA_BWD_ACCUM_DQ, GDPA_BWD_RESIDUAL */
 } gdpa_problem;
 
 /* Bytes of device workspace gdpa_fwd (backward = 0) or gdpa_bwd (backward = 1)
@@ -98,8 +101,9 @@ gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* 
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward of sum(O * dO).  In: q, k, v, d_o, and for softmax also o and lse
- * from gdpa_fwd (ignored for SiLU, may be NULL).  Out: dq [T,H,d] (overwritten,
- * or accumulated with GDPA_BWD_ACCUM_DQ), dk, dv [B,n,H,d] (overwritten; each is
+ * from gdpa_fwd (ignored for SiLU, may be NULL).  Out: dq [T,H,d] (overwritten;
+ * accumulated with GDPA_BWD_ACCUM_DQ; dO added with GDPA_BWD_RESIDUAL), dk, dv
+ * [B,n,H,d] (overwritten; each is
  * the sum over the sample's own tokens, zero for an empty sample).  With SiLU,
  * o and lse are not read and may be NULL. */
 gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
