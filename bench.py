@@ -55,7 +55,8 @@ def gdpa_units(kind, T, B, H, d, n, phi, residual=False):
     kv = B * n * H * d * 2
     if kind == "gdpa_fwd":
         flops = 4.0 * T * H * n * d
-        byts = 2 * tok + 2 * kv + (tok if residual else 0) + (T * H * 4 if phi == "softmax" else 0)
+        # the residual of a stacked layer is the query tensor itself: counted once
+        byts = 2 * tok + 2 * kv + (T * H * 4 if phi == "softmax" else 0)
     else:
         flops = 8.0 * T * H * n * d
         byts = 3 * tok + 4 * kv

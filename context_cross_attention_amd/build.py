@@ -29,7 +29,8 @@ CFLAGS = [
     "-munsafe-fp-atomics",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
-SOURCES = ["gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_bwd.hip", "gdpa_gemm.hip", "gdpa_api.cpp"]
+SOURCES = ["gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_fwd_res.hip", "gdpa_bwd.hip", "gdpa_gemm.hip",
+           "gdpa_api.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -6,7 +6,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/gdpa.h"
+#include "gdpa.h"
 #include "gdpa_launch.h"
 
 namespace {
@@ -40,7 +40,7 @@ gdpa_status check_problem(const gdpa_problem* p) {
 }
 
 // Workspace layouts (each region 256-byte aligned).
-//   forward : tile_start [B+1] int32
+//   forward : tile_start [B+1] int32 (streaming kernel) | order [B] int32 (resident kernel)
 //   backward: order [B] int32 | dvec [T*H] fp32 (softmax) | dq_acc [T*H*d] fp32 (bf16,
 //             when the context rows span several work-groups)
 struct BwdPlan {
@@ -70,7 +70,7 @@ BwdPlan bwd_plan(const gdpa_problem* p) {
 }
 
 size_t fwd_workspace(const gdpa_problem* p) {
-  return align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
+  return align_up(sizeof(int32_t) * ((size_t)p->batch + 1)) + align_up(sizeof(int32_t) * (size_t)p->batch);
 }
 
 }  // namespace
@@ -115,6 +115,12 @@ gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* 
   a.scale = p->scale;
   if (p->dtype == GDPA_F32) return hip_status(gdpa::launch_fwd_f32(a, p->head_dim, p->phi, resid, s));
 
+  if (gdpa::fwd_res_supported(p->head_dim, p->n_kv)) {
+    int32_t* order = (int32_t*)((char*)workspace + align_up(sizeof(int32_t) * ((size_t)p->batch + 1)));
+    hipError_t e = gdpa::launch_longest_first(offsets, p->batch, order, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(gdpa::launch_fwd_res(a, order, p->head_dim, p->phi, resid, s));
+  }
   int32_t* tile_start = (int32_t*)workspace;
   hipError_t e = gdpa::launch_tile_scan(offsets, p->batch, gdpa::kFwdTileRows, tile_start, s);
   if (e != hipSuccess) return hip_status(e);

@@ -25,12 +25,21 @@
 
 namespace gdpa {
 
+// Storage row of token t (0..31) of a query tile: inside each group of 8 rows,
+// tokens 0..3 go to even rows and 4..7 to odd rows.
+__device__ __forceinline__ int qpos(int t) { return (t & ~7) | ((t & 3) << 1) | ((t >> 2) & 1); }
+
 template <int D, int PHI, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   constexpr int NJ = 32 * NW;          // context rows per work-group
   constexpr int BQ = kBwdRowsPerWave;  // query rows per step
   constexpr int KS = D / 16, DT = D / 32, LD = D + 8, CH = D / 8;
   constexpr int LDT = BQ + 8;          // dS^T row stride
+  // LDS bank layout (32 banks of 4 bytes).  Row strides D + 8 and BQ + 8 are 4 mod 32
+  // dwords (20 for BQ + 8), so 16-byte reads by 8 consecutive rows are conflict
+  // free, and transpose loads over rows spaced by 2 are too.  Q and dO tile rows
+  // are stored at qpos(t), which spreads each run of 4 consecutive tokens over
+  // rows 2 apart while keeping any 8 consecutive tokens on distinct banks.
   constexpr int NT = NW * 64;
   constexpr int DQ_TILES = (BQ / 16) * (D / 16);
   constexpr int TPW = DQ_TILES / NW;   // 16x16 dQ tiles per wave
@@ -56,11 +65,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   const uint16_t* Kg = (const uint16_t*)a.k + ((size_t)b * n * H + h) * D;
   const uint16_t* Vg = (const uint16_t*)a.v + ((size_t)b * n * H + h) * D;
 
-  // K chunk, row-major, into LDS (zero rows past n).
-  for (int idx = tid; idx < NJ * CH; idx += NT) {
-    const int j = idx / CH, c = idx % CH;
-    const u32x4 v = (j0 + j < n) ? gload16(Kg + (size_t)(j0 + j) * rs + 8 * c) : u32x4{};
-    lds_write16(&Kc[j * LD + 8 * c], v);
+  // K chunk, row-major, into LDS (zero rows past n); loads first, then writes.
+  {
+    constexpr int KI = NJ * CH / NT;
+    u32x4 kr[KI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int idx = i * NT + tid, j = idx / CH, c = idx % CH;
+      kr[i] = (j0 + j < n) ? gload16(Kg + (size_t)(j0 + j) * rs + 8 * c) : u32x4{};
+    }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int idx = i * NT + tid, j = idx / CH, c = idx % CH;
+      lds_write16(&Kc[j * LD + 8 * c], kr[i]);
+    }
   }
   // The wave's V rows as B operand of dP = dO V^T: lane (j + 32 g), items d = 16 ks + 8 g + i.
   const int jl = 32 * wave + lr;  // local context row of this lane
@@ -80,40 +98,68 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
 
   // Transpose-read addressing for the dV / dK products (row order of the C tile,
   // as in the forward kernel) and for the dQ product (contiguous rows, 16x16x32).
-  const int trG = lane >> 4;
-  const int tr_off = (4 * (trG >> 1) + ((lane & 15) >> 2)) * LD + 16 * (trG & 1) + 4 * (lane & 3);
-  const int q16_row = 8 * trG + ((lane & 15) >> 2), q16_col = 4 * (lane & 3);
+  const int trG = lane >> 4, trr = (lane & 15) >> 2;
+  // dV / dK B operand: lane 16 G + 4 r + c reads token row 16 kk + 4 (G / 2) + r
+  // (second read + 8), columns 32 dt + 16 (G % 2) + 4 c.
+  const int tr_tok = 4 * (trG >> 1) + trr, tr_col = 16 * (trG & 1) + 4 * (lane & 3);
+  // dQ operands (16x16x32): lane 16 G + 4 r + c reads context row 8 G + 2 r (second
+  // read + 1), columns base + 4 c; item i <-> context row 8 G + 2 (i % 4) + i / 4.
+  const int q16_row = 8 * trG + 2 * trr, q16_col = 4 * (lane & 3);
 
   const float sl2 = a.scale * kLog2e;
   const uint16_t* Qg = (const uint16_t*)a.q + (size_t)h * D;
   const uint16_t* dOg = (const uint16_t*)a.d_o + (size_t)h * D;
 
+  // Each thread stages SPT 16-byte chunks of the Q and dO tiles per step; the
+  // next step's chunks are loaded while the current step computes.
+  constexpr int SPT = (BQ * CH + NT - 1) / NT;
+  u32x4 q_next[SPT], do_next[SPT];
+  float lse_next = INFINITY, dvec_next = 0.f;
+  auto load_step = [&](int tq) {
+    const int rows_ = min(BQ, L - tq);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int idx = i * NT + tid, t = idx / CH, c = idx % CH;
+      const bool ok = idx < BQ * CH && t < rows_;
+      const size_t off = (size_t)(seq0 + tq + t) * rs + 8 * c;
+      q_next[i] = ok ? gload16(Qg + off) : u32x4{};
+      do_next[i] = ok ? gload16(dOg + off) : u32x4{};
+    }
+    if (PHI == 0 && tid < BQ) {
+      const bool ok = tid < rows_;
+      const size_t r = (size_t)(seq0 + tq + tid) * H + h;
+      lse_next = ok ? a.lse[r] * kLog2e : INFINITY;
+      dvec_next = ok ? a.dvec[r] : 0.f;
+    }
+  };
+  if (L > 0) load_step(0);
+
   for (int tq = 0; tq < L; tq += BQ) {
     const int rows = min(BQ, L - tq);
     __syncthreads();  // previous step is done with Qs, dOs, dSt
-    for (int idx = tid; idx < BQ * CH; idx += NT) {
-      const int t = idx / CH, c = idx % CH;
-      const bool ok = t < rows;
-      const size_t off = (size_t)(seq0 + tq + t) * rs + 8 * c;
-      lds_write16(&Qs[t * LD + 8 * c], ok ? gload16(Qg + off) : u32x4{});
-      lds_write16(&dOs[t * LD + 8 * c], ok ? gload16(dOg + off) : u32x4{});
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int idx = i * NT + tid, t = idx / CH, c = idx % CH;
+      if (idx < BQ * CH) {
+        lds_write16(&Qs[qpos(t) * LD + 8 * c], q_next[i]);
+        lds_write16(&dOs[qpos(t) * LD + 8 * c], do_next[i]);
+      }
     }
     if (PHI == 0 && tid < BQ) {
-      const bool ok = tid < rows;
-      const size_t r = (size_t)(seq0 + tq + tid) * H + h;
-      lse_s[tid] = ok ? a.lse[r] * kLog2e : INFINITY;
-      dvec_s[tid] = ok ? a.dvec[r] : 0.f;
+      lse_s[tid] = lse_next;
+      dvec_s[tid] = dvec_next;
     }
     __syncthreads();
+    if (tq + BQ < L) load_step(tq + BQ);
 
     // S = Q K^T and dP = dO V^T for the wave's 32 context rows.
     f32x16 S = f32x16{}, dP = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 qa = lds_read8(&Qs[lr * LD + 16 * ks + 8 * g]);
+      const bf16x8 qa = lds_read8(&Qs[qpos(lr) * LD + 16 * ks + 8 * g]);
       const bf16x8 kb = lds_read8(&Kc[jl * LD + 16 * ks + 8 * g]);
       S = mfma32(qa, kb, S);
-      const bf16x8 da = lds_read8(&dOs[lr * LD + 16 * ks + 8 * g]);
+      const bf16x8 da = lds_read8(&dOs[qpos(lr) * LD + 16 * ks + 8 * g]);
       dP = mfma32(da, vf[ks], dP);
     }
 
@@ -154,12 +200,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
     for (int kk = 0; kk < 2; ++kk) {
       const bf16x8 pa = pack_c8(P, kk);
       const bf16x8 sa = pack_c8(dS, kk);
+      const int r0 = qpos(16 * kk + tr_tok) * LD + tr_col, r1 = qpos(16 * kk + 8 + tr_tok) * LD + tr_col;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int o = 16 * kk * LD + tr_off + 32 * dt;
-        const bf16x8 dob = cat8(lds_read_tr4(&dOs[o]), lds_read_tr4(&dOs[o + 8 * LD]));
+        const bf16x8 dob = cat8(lds_read_tr4(&dOs[r0 + 32 * dt]), lds_read_tr4(&dOs[r1 + 32 * dt]));
         dV[dt] = mfma32(pa, dob, dV[dt]);
-        const bf16x8 qb = cat8(lds_read_tr4(&Qs[o]), lds_read_tr4(&Qs[o + 8 * LD]));
+        const bf16x8 qb = cat8(lds_read_tr4(&Qs[r0 + 32 * dt]), lds_read_tr4(&Qs[r1 + 32 * dt]));
         dK[dt] = mfma32(sa, qb, dK[dt]);
       }
     }
@@ -174,9 +220,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
 #pragma unroll 4
       for (int js = 0; js < NJ; js += 32) {
         const int ra = (js + q16_row) * LDT + t0 + q16_col;
-        const bf16x8 av = cat8(lds_read_tr4(&dSt[ra]), lds_read_tr4(&dSt[ra + 4 * LDT]));
+        const bf16x8 av = cat8(lds_read_tr4(&dSt[ra]), lds_read_tr4(&dSt[ra + LDT]));
         const int rb = (js + q16_row) * LD + d0 + q16_col;
-        const bf16x8 bv = cat8(lds_read_tr4(&Kc[rb]), lds_read_tr4(&Kc[rb + 4 * LD]));
+        const bf16x8 bv = cat8(lds_read_tr4(&Kc[rb]), lds_read_tr4(&Kc[rb + LD]));
         acc = mfma16(av, bv, acc);
       }
       // Lane (d + 16 q), register r: token t0 + 4 q + r, column d0 + lane % 16.

@@ -22,11 +22,16 @@ namespace gdpa {
 
 template <int D, int PHI, bool RESID>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
-  constexpr int BM = kFwdTileRows, BN = 64, KS = D / 16, DT = D / 32, LD = D + 8;
+  constexpr int BM = kFwdTileRows, BN = 64, KS = D / 16, DT = D / 32;
+  // Row strides (elements), chosen for the 32-bank LDS: K rows are read 16 bytes
+  // per lane by 8 consecutive rows at a time (stride = 4 mod 32 dwords); V rows are
+  // read by transpose loads, 4 consecutive rows x 32 bytes per 16 lanes (stride =
+  // 8 or 24 mod 32 dwords).
+  constexpr int LD = D + 8, LDV = D + 16;
   constexpr int CH = D / 8;                   // 16-byte chunks per K/V row
   constexpr int SI = (BN * CH + 255) / 256;   // staging chunks per thread per tensor
   __shared__ __align__(16) uint16_t Ks[BN * LD];
-  __shared__ __align__(16) uint16_t Vs[BN * LD];
+  __shared__ __align__(16) uint16_t Vs[BN * LDV];
 
   const int H = a.H, B = a.B, n = a.n;
   const int total = a.tile_start[B];
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       const int idx = i * 256 + tid, j = idx / CH, c = idx % CH;
       if (idx < BN * CH) {
         lds_write16(&Ks[j * LD + 8 * c], kreg[i]);
-        lds_write16(&Vs[j * LD + 8 * c], vreg[i]);
+        lds_write16(&Vs[j * LDV + 8 * c], vreg[i]);
       }
     }
   };
@@ -79,7 +84,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   // (d + 32 g) then holds V[j][d] for j = 4 g + i (i < 4) and 8 + 4 g + i - 4,
   // matching the row order of the S^T C tile.
   const int trG = lane >> 4;
-  const int tr_off = (4 * (trG >> 1) + ((lane & 15) >> 2)) * LD + 16 * (trG & 1) + 4 * (lane & 3);
+  const int tr_off = (4 * (trG >> 1) + ((lane & 15) >> 2)) * LDV + 16 * (trG & 1) + 4 * (lane & 3);
 
   f32x16 O[DT];
 #pragma unroll
@@ -150,11 +155,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const bf16x8 p = pack_c8(S[mt], kk);
-        const uint16_t* vb = &Vs[(32 * mt + 16 * kk) * LD + tr_off];
+        const uint16_t* vb = &Vs[(32 * mt + 16 * kk) * LDV + tr_off];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const bf16x4 lo = lds_read_tr4(vb + 32 * dt);
-          const bf16x4 hi = lds_read_tr4(vb + 8 * LD + 32 * dt);
+          const bf16x4 hi = lds_read_tr4(vb + 8 * LDV + 32 * dt);
           O[dt] = mfma32(cat8(lo, hi), p, O[dt]);
         }
       }

@@ -1,0 +1,277 @@
+// GDPA forward with the sample's K and V resident in LDS (bf16, n * d <= 32768).
+//
+// Same contraction as gdpa_fwd.hip (Kunlun paper summary, section 2.2, GDPA
+// bullet), organised for the case where one (sample, head)'s context fits in
+// LDS: K [n][d] row-major and V^T [d][n] (transposed, with the context rows
+// permuted into the order of the S^T C tile) are loaded once per work-group and
+// every query row of the sample streams past them.  All MFMA operand reads are
+// 16-byte LDS reads with conflict-free strides; there are no barriers in the
+// main loop: each of the 8 waves walks its own 32-row query chunks and
+// prefetches the next chunk's Q while computing the current one.
+//
+// One work-group per (sample, head), launched longest sample first.
+#include "gdpa_device.h"
+#include "gdpa_launch.h"
+
+namespace gdpa {
+
+// Position of context row j inside V^T rows: the S^T C tile holds, in lane group g,
+// register r, row 8 (r / 4) + 4 g + r % 4 of a 32-row tile; a B-operand k-step kk
+// takes registers 8 kk .. 8 kk + 7.  Storing j = 32 t + 16 kk + 8 a + 4 g + c at
+// 32 t + 16 kk + 8 g + 4 a + c makes each lane's 8 operand values contiguous.
+__device__ __forceinline__ int vt_pos(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
+
+// Position of head column d inside K rows (the same bit swap): lane group g of a
+// k-step then reads columns 16 ks + 4 g .. + 3 and 16 ks + 8 + 4 g .. + 3 as one
+// 16-byte operand, which are exactly the output columns that lane holds in the
+// O^T C tile - so a residual equal to Q can be added from the Q registers.
+__device__ __forceinline__ int kcol(int d) { return vt_pos(d); }
+
+// RESID: 0 none, 1 residual is the query tensor, 2 a separate residual tensor.
+template <int D, int NMAX, int PHI, int RESID>
+__global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const int32_t* __restrict__ order) {
+  constexpr int NW = 8, NT = NW * 64, KS = D / 16, DT = D / 32, CH = D / 8;
+  constexpr int LDK = D + 8;      // K rows: 4 mod 32 dwords -> 8 consecutive rows conflict free
+  constexpr int LDV = NMAX + 8;   // V^T rows: likewise for 8 consecutive d rows
+  __shared__ __align__(16) uint16_t Kc[NMAX * LDK];
+  __shared__ __align__(16) uint16_t Vt[D * LDV];
+
+  const int H = a.H, n = a.n;
+  const int npad = (n + 63) & ~63;
+  const int item = blockIdx.x;
+  const int rank = item / H, h = item - rank * H;
+  const int b = order[rank];
+  const int seq0 = a.offsets[b], L = a.offsets[b + 1] - seq0;
+  if (L == 0) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const size_t rs = (size_t)H * D;
+  const uint16_t* Kg = (const uint16_t*)a.k + ((size_t)b * n * H + h) * D;
+  const uint16_t* Vg = (const uint16_t*)a.v + ((size_t)b * n * H + h) * D;
+
+  // Stage K row-major and V^T.  Every load is unconditional (row index clamped
+  // into the sample) so the compiler keeps them in flight together; padding rows
+  // are zeroed afterwards with selects.
+  const int nlast = n - 1;
+  {
+    constexpr int KI = NMAX * CH / NT;   // K chunks per thread (upper bound)
+    u32x4 kr[KI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int idx = i * NT + tid, j = idx / CH, c = idx % CH;
+      kr[i] = gload16(Kg + (size_t)min(j, nlast) * rs + 8 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int idx = i * NT + tid, j = idx / CH, c = idx % CH;
+      if (j < npad) {
+        const u32x4 v = j < n ? kr[i] : u32x4{};
+        // Columns 8c .. 8c+3 and 8c+4 .. 8c+7 go to their permuted positions.
+        lds_write8(&Kc[j * LDK + kcol(8 * c)], u32x2{v[0], v[1]});
+        lds_write8(&Kc[j * LDK + kcol(8 * c + 4)], u32x2{v[2], v[3]});
+      }
+    }
+  }
+  // V^T: a task is 4 context rows x 8 columns; consecutive lanes take
+  // consecutive row groups so the 8-byte LDS writes land on distinct banks.
+  {
+    constexpr int VI = NMAX / 4 * CH / NT;  // tasks per thread (upper bound)
+    const int nq = npad / 4;
+    u32x4 vr[VI][4];
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int idx = i * NT + tid, jq = idx % nq, dc = min(idx / nq, CH - 1), j0 = 4 * jq;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) vr[i][c] = gload16(Vg + (size_t)min(j0 + c, nlast) * rs + 8 * dc);
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int idx = i * NT + tid, jq = idx % nq, dc = idx / nq, j0 = 4 * jq;
+      if (dc >= CH) continue;
+      const int pos = vt_pos(j0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (j0 + c >= n) vr[i][c] = u32x4{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = 16 * (e & 1);
+        const uint32_t h0 = (vr[i][0][e >> 1] >> sh) & 0xffffu, h1 = (vr[i][1][e >> 1] >> sh) & 0xffffu;
+        const uint32_t h2 = (vr[i][2][e >> 1] >> sh) & 0xffffu, h3 = (vr[i][3][e >> 1] >> sh) & 0xffffu;
+        lds_write8(&Vt[(8 * dc + e) * LDV + pos], u32x2{h0 | (h1 << 16), h2 | (h3 << 16)});
+      }
+    }
+  }
+  __syncthreads();
+
+  const float sl2 = a.scale * kLog2e, nsl2 = -sl2;
+  const int nchunks = (L + 31) / 32;
+  // Query rows past the sample are read from its last row (clamped, always a
+  // valid address) and never stored: each lane's row is independent.  With the
+  // K column permutation, k-step ks of lane group g takes columns
+  // 16 ks + 4 g .. + 3 and 16 ks + 8 + 4 g .. + 3.
+  const uint16_t* Qg = (const uint16_t*)a.q + (size_t)h * D + 4 * g;
+  auto load_q = [&](int ch, bf16x8* dst) {
+    const int t = min(32 * ch + lr, L - 1);
+    const uint16_t* qp = Qg + (size_t)(seq0 + t) * rs;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x2 lo = *(const u32x2*)(qp + 16 * ks), hi = *(const u32x2*)(qp + 16 * ks + 8);
+      dst[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+  };
+
+  // One 32-row chunk with Q already in qc; prefetches the Q of chunk ch + NW into qn.
+  auto do_chunk = [&](int ch, const bf16x8* qc, bf16x8* qn) {
+    const int t = 32 * ch + lr;
+    const bool tvalid = t < L;
+    load_q(ch + NW, qn);
+    const size_t obase = (size_t)(seq0 + min(t, L - 1)) * rs + (size_t)h * D + 4 * g;
+    f32x16 O[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // S^T for the 32 context rows j0 .. j0 + 31.
+    auto scores = [&](int j0, f32x16& S) {
+      S = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        S = mfma32(lds_read8(&Kc[(j0 + lr) * LDK + 16 * ks + 8 * g]), qc[ks], S);
+    };
+    // phi of one 32-row tile, then O^T += V^T P^T.
+    auto mix = [&](int j0, f32x16& S) {
+      if (PHI == 0) {
+        const bool tail = j0 + 32 > n;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float s = S[r] * sl2;
+          if (tail && j0 + 8 * (r >> 2) + 4 * g + (r & 3) >= n) s = -INFINITY;
+          S[r] = s;
+          mx = fmaxf(mx, s);
+        }
+        mx = fmaxf(mx, wave_xor32(mx));
+        // Rescale O only when some row's running max moved (wave-uniform test).
+        if (__any(mx > m_run)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float corr = fast_exp2(m_run - m_new);
+          l_run *= corr;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) O[dt] *= corr;
+          m_run = m_new;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(S[r] - m_run);
+          l_run += p;
+          S[r] = p;
+        }
+      } else {
+        // SiLU(s) with s = scale * S: with t = -log2(e) * s, silu(s) = -ln(2) * t / (1 + 2^t).
+        // The constant -ln(2) is applied once to O after the last tile.
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float t = S[r] * nsl2;
+          S[r] = t * fast_rcp(1.0f + fast_exp2(t));
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 p = pack_c8(S, kk);
+        const uint16_t* vb = &Vt[lr * LDV + j0 + 16 * kk + 8 * g];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[dt] = mfma32(lds_read8(vb + 32 * dt * LDV), p, O[dt]);
+      }
+    };
+
+    // Software pipeline: the MFMAs for the next tile's scores are issued before
+    // this tile's phi, so the VALU work overlaps matrix-core time.
+    const int ntile = npad / 32;
+    f32x16 Sa, Sb;
+    scores(0, Sa);
+    for (int jt = 0; jt < ntile; jt += 2) {
+      scores(32 * (jt + 1), Sb);          // npad is a multiple of 64: tile jt + 1 exists
+      mix(32 * jt, Sa);
+      if (jt + 2 < ntile) scores(32 * (jt + 2), Sa);
+      mix(32 * (jt + 1), Sb);
+    }
+    if (PHI == 1) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt] *= -kLn2;
+    }
+
+    if (PHI == 0) {
+      const float l_tot = l_run + wave_xor32(l_run);
+      const float inv = 1.0f / l_tot;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt] *= inv;
+      if (tvalid && g == 0 && a.lse != nullptr)
+        a.lse[(size_t)(seq0 + t) * H + h] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+    if (tvalid) {
+      uint16_t* op = (uint16_t*)a.o + obase;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float v0 = O[dt][4 * q4 + 0], v1 = O[dt][4 * q4 + 1];
+          float v2 = O[dt][4 * q4 + 2], v3 = O[dt][4 * q4 + 3];
+          if (RESID == 1) {
+            // Residual is Q itself: O column 32 dt + 8 q4 + 4 g + c is item
+            // 4 (q4 % 2) + c of the k-step 2 dt + q4 / 2 fragment of this lane.
+            const bf16x8 qv = qc[2 * dt + (q4 >> 1)];
+            const int o = 4 * (q4 & 1);
+            v0 += (float)qv[o + 0]; v1 += (float)qv[o + 1];
+            v2 += (float)qv[o + 2]; v3 += (float)qv[o + 3];
+          } else if (RESID == 2) {
+            const u32x2 rr = *(const u32x2*)((const uint16_t*)a.residual + obase + 32 * dt + 8 * q4);
+            v0 += __uint_as_float(rr[0] << 16);
+            v1 += __uint_as_float(rr[0] & 0xffff0000u);
+            v2 += __uint_as_float(rr[1] << 16);
+            v3 += __uint_as_float(rr[1] & 0xffff0000u);
+          }
+          bf16x4 ov;
+          ov[0] = f2bf(v0); ov[1] = f2bf(v1); ov[2] = f2bf(v2); ov[3] = f2bf(v3);
+          *(bf16x4*)(op + 32 * dt + 8 * q4) = ov;
+        }
+    }
+  };
+
+  // Two register sets for Q alternate between "current" and "prefetch".
+  bf16x8 qa[KS], qb[KS];
+  load_q(wave, qa);
+  for (int ch = wave; ch < nchunks; ch += 2 * NW) {
+    do_chunk(ch, qa, qb);
+    if (ch + NW < nchunks) do_chunk(ch + NW, qb, qa);
+  }
+}
+
+bool fwd_res_supported(int d, int n) { return (long)n * d <= 32768 && (d == 32 || d == 64 || d == 128); }
+
+template <int D, int NMAX, int PHI>
+static void fwd_res_launch(const FwdArgs& a, const int32_t* order, int resid, hipStream_t s) {
+  const dim3 g((unsigned)((long)a.B * a.H)), blk(512);
+  if (resid == 0) hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 0>), g, blk, 0, s, a, order);
+  else if (resid == 1) hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 1>), g, blk, 0, s, a, order);
+  else hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 2>), g, blk, 0, s, a, order);
+}
+
+template <int D, int NMAX>
+static hipError_t fwd_res_d(const FwdArgs& a, const int32_t* order, int phi, bool resid, hipStream_t s) {
+  const int mode = !resid ? 0 : (a.residual == a.q ? 1 : 2);
+  if (phi == 0) fwd_res_launch<D, NMAX, 0>(a, order, mode, s);
+  else fwd_res_launch<D, NMAX, 1>(a, order, mode, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_res(const FwdArgs& a, const int32_t* order, int d, int phi, bool resid,
+                          hipStream_t s) {
+  if ((long)a.B * a.H == 0) return hipSuccess;
+  switch (d) {
+    case 32: return fwd_res_d<32, 1024>(a, order, phi, resid, s);
+    case 64: return fwd_res_d<64, 512>(a, order, phi, resid, s);
+    case 128: return fwd_res_d<128, 256>(a, order, phi, resid, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdpa

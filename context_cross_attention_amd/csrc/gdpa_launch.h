@@ -61,6 +61,11 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int phi, bool residual, int 
                            hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, int phi, bool residual, hipStream_t s);
 
+// Forward with the context resident in LDS (gdpa_fwd_res.hip), for n * d <= 32768.
+bool fwd_res_supported(int d, int n);
+hipError_t launch_fwd_res(const FwdArgs& a, const int32_t* order, int d, int phi, bool residual,
+                          hipStream_t s);
+
 // Backward (gdpa_bwd.hip).
 int bwd_bf16_waves(int d, int n);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, hipStream_t s);
