@@ -170,7 +170,7 @@ def make_gdpa_inputs(cfg: GdpaConfig, seed: int = 0, sharp: bool = False,
 class StackedInputs:
     """Stacked residual GDPA workload with generated K/V.
 
-    x0, do: [T, H*d]; ctx: [B, ctx_dim]; w_k[l], w_v[l]: [ctx_dim, n*H*d].
+    x0, do: [T, H*d]; ctx: [B, ctx_dim]; w_k[l], w_v[l]: [n*H*d, ctx_dim] (output-major).
     """
     cfg: GdpaConfig
     lengths: np.ndarray
@@ -200,8 +200,8 @@ def make_stacked_inputs(cfg: GdpaConfig, seed: int = 0) -> StackedInputs:
     a = xavier_uniform_bound(C, n * H * d)
     w_k, w_v = [], []
     for _ in range(cfg.layers):
-        w_k.append(draw_uniform(rng, (C, n * H * d), cfg.dtype, a))
-        w_v.append(draw_uniform(rng, (C, n * H * d), cfg.dtype, a))
+        w_k.append(draw_uniform(rng, (n * H * d, C), cfg.dtype, a))
+        w_v.append(draw_uniform(rng, (n * H * d, C), cfg.dtype, a))
     do = draw_normal(rng, (T, H * d), cfg.dtype)
     return StackedInputs(cfg, lengths, torch.from_numpy(off.astype(np.int32)), x0, ctx, w_k, w_v, do)
 

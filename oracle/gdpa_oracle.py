@@ -210,9 +210,15 @@ def gdpa_backward(q, offsets, k, v, do, phi: str = "softmax", scale: Optional[fl
 # ---------------------------------------------------------------------------
 
 def weight_generation(ctx, w, n: int, H: int, d: int) -> np.ndarray:
-    """K (or V) = (C W).reshape(B, n, H, d) for context C [B, c] and W [c, n*H*d]."""
+    """K (or V) = (C W^T).reshape(B, n, H, d) for context C [B, c] and an
+    output-major weight W [n*H*d, c] (a linear layer's weight layout)."""
     ctx, w = as_f64(ctx), as_f64(w)
-    return (ctx @ w).reshape(ctx.shape[0], n, H, d)
+    return (ctx @ w.T).reshape(ctx.shape[0], n, H, d)
+
+
+def weight_gradient(ctx, d_out) -> np.ndarray:
+    """dW [cols, c] = d_out[B, cols]^T C[B, c]: gradient of C W^T with respect to W."""
+    return as_f64(d_out).T @ as_f64(ctx)
 
 
 def stacked_forward(x0, offsets, ctx, w_k: List, w_v: List, heads: int, n: int,
@@ -236,7 +242,8 @@ def stacked_backward(xs: List[np.ndarray], offsets, ctx, w_k: List, w_v: List, d
     """Backward of stacked_forward for loss sum(X_L * dO).
 
     dX_l = dX_{l+1} + dQ_l (the residual passes the gradient through unchanged);
-    dW^l = C^T dK_l.reshape(B, -1) (and likewise for V).  Returns (dX_0, [dW_K], [dW_V]).
+    dW^l = dK_l.reshape(B, -1)^T C (and likewise for V), in W's [n*H*d, c] layout.
+    Returns (dX_0, [dW_K], [dW_V]).
     """
     ctx = as_f64(ctx)
     dx = as_f64(do)
@@ -250,7 +257,7 @@ def stacked_backward(xs: List[np.ndarray], offsets, ctx, w_k: List, w_v: List, d
         vl = weight_generation(ctx, w_v[l], n, heads, d)
         gq, gk, gv = gdpa_backward(xs[l].reshape(T, heads, d), offsets, kl, vl,
                                    dx.reshape(T, heads, d), phi, scale)
-        dwk[l] = ctx.T @ gk.reshape(B, -1)
-        dwv[l] = ctx.T @ gv.reshape(B, -1)
+        dwk[l] = gk.reshape(B, -1).T @ ctx
+        dwv[l] = gv.reshape(B, -1).T @ ctx
         dx = dx + gq.reshape(T, HD)
     return dx, dwk, dwv

@@ -33,6 +33,6 @@ def test_inputs_deterministic_and_shaped():
 def test_stacked_inputs():
     cfg = gi.small_config(gi.CONFIGS[5], batch=4, lengths=("uniform", 1, 5), layers=2)
     s = gi.make_stacked_inputs(cfg, seed=0)
-    assert len(s.w_k) == 2 and s.w_k[0].shape == (512, 256 * 8 * 128)
+    assert len(s.w_k) == 2 and s.w_k[0].shape == (256 * 8 * 128, 512)
     a = gi.xavier_uniform_bound(512, 256 * 8 * 128)
     assert float(s.w_k[0].float().abs().max()) <= a * 1.01

@@ -333,8 +333,8 @@ def stacked_problem(seed=18, lengths=(3, 0, 5), H=2, d=4, n=3, C=5, layers=2):
     T = int(off[-1])
     x0 = rng.standard_normal((T, H * d))
     ctx = rng.standard_normal((len(lengths), C))
-    wk = [rng.standard_normal((C, n * H * d)) * 0.3 for _ in range(layers)]
-    wv = [rng.standard_normal((C, n * H * d)) * 0.3 for _ in range(layers)]
+    wk = [rng.standard_normal((n * H * d, C)) * 0.3 for _ in range(layers)]
+    wv = [rng.standard_normal((n * H * d, C)) * 0.3 for _ in range(layers)]
     g = rng.standard_normal((T, H * d))
     return off, x0, ctx, wk, wv, g
 
@@ -351,8 +351,8 @@ def test_stacked_matches_torch_autograd():
     wvt = [torch.from_numpy(w.copy()).requires_grad_() for w in wv]
     x = xt
     for l in range(2):
-        kl = (ct @ wkt[l]).reshape(3, n, H, d)
-        vl = (ct @ wvt[l]).reshape(3, n, H, d)
+        kl = torch.nn.functional.linear(ct, wkt[l]).reshape(3, n, H, d)
+        vl = torch.nn.functional.linear(ct, wvt[l]).reshape(3, n, H, d)
         rows = []
         for b in range(3):
             xb = x[off[b]:off[b + 1]].reshape(-1, H, d).transpose(0, 1)
