@@ -251,7 +251,7 @@ def main():
     if cfg.layers:
         cols = n * H * d
         f1, b1 = gemm_units(B, cols, cfg.ctx_dim)
-        f2, b2 = gemm_units(cfg.ctx_dim, cols, B)
+        f2, b2 = gemm_units(cols, cfg.ctx_dim, B)
         units["weightgen_fwd"] = (2 * f1, 2 * b1)   # K and V per marked region
         units["weightgen_bwd"] = (2 * f2, 2 * b2)
         wg_flops = layers * 2 * (f1 + f2)

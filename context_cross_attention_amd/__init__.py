@@ -224,12 +224,12 @@ def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
 
 
 def weightgen_fwd(ctx: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None):
-    """out[B, cols] = ctx[B, c] @ w[c, cols] (bf16, fp32 accumulation)."""
+    """out[B, cols] = ctx[B, c] @ w[cols, c]^T (bf16, fp32 accumulation)."""
     lib = load()
     B, c = ctx.shape
-    cols = w.shape[1]
+    cols = w.shape[0]
     _require(ctx, "ctx", (B, c), torch.bfloat16, ctx.device)
-    _require(w, "w", (c, cols), torch.bfloat16, ctx.device)
+    _require(w, "w", (cols, c), torch.bfloat16, ctx.device)
     if out is None:
         out = torch.empty((B, cols), dtype=torch.bfloat16, device=ctx.device)
     _require(out, "out", (B, cols), torch.bfloat16, ctx.device)
@@ -239,15 +239,15 @@ def weightgen_fwd(ctx: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor
 
 
 def weightgen_bwd_w(ctx: torch.Tensor, d_out: torch.Tensor, d_w: Optional[torch.Tensor] = None):
-    """d_w[c, cols] = ctx[B, c]^T @ d_out[B, cols] (bf16, fp32 accumulation)."""
+    """d_w[cols, c] = d_out[B, cols]^T @ ctx[B, c] (bf16, fp32 accumulation)."""
     lib = load()
     B, c = ctx.shape
     cols = d_out.shape[1]
     _require(ctx, "ctx", (B, c), torch.bfloat16, ctx.device)
     _require(d_out, "d_out", (B, cols), torch.bfloat16, ctx.device)
     if d_w is None:
-        d_w = torch.empty((c, cols), dtype=torch.bfloat16, device=ctx.device)
-    _require(d_w, "d_w", (c, cols), torch.bfloat16, ctx.device)
+        d_w = torch.empty((cols, c), dtype=torch.bfloat16, device=ctx.device)
+    _require(d_w, "d_w", (cols, c), torch.bfloat16, ctx.device)
     _check(lib.gdpa_weightgen_bwd_w(B, c, cols, _ptr(ctx), _ptr(d_out), _ptr(d_w), _stream()),
            "gdpa_weightgen_bwd_w")
     return d_w

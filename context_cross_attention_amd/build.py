@@ -29,13 +29,17 @@ CFLAGS = [
     "-munsafe-fp-atomics",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
-SOURCES = ["gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_fwd_res.hip", "gdpa_bwd.hip", "gdpa_gemm.hip",
-           "gdpa_api.cpp"]
+SOURCES = ["gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_fwd_res.hip", "gdpa_bwd.hip", "gdpa_bwd_res.hip",
+           "gdpa_gemm.hip", "gdpa_api.cpp"]
+# Per-source extra flags.  The backward kernel keeps 256 fp32 accumulators per lane
+# in AGPRs for the whole sample; selecting the VGPR form of MFMA for everything else
+# (the per-step score tiles) keeps those accumulators resident instead of spilled.
+EXTRA_FLAGS = {}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

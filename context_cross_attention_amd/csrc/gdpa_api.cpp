@@ -52,7 +52,10 @@ struct BwdPlan {
 BwdPlan bwd_plan(const gdpa_problem* p) {
   BwdPlan pl;
   const size_t TH = (size_t)p->total_tokens * p->heads;
-  if (p->dtype == GDPA_BF16) {
+  if (p->dtype == GDPA_BF16 && gdpa::bwd_res_supported(p->head_dim, p->n_kv)) {
+    pl.waves = 4;
+    pl.chunks = 1;
+  } else if (p->dtype == GDPA_BF16) {
     pl.waves = gdpa::bwd_bf16_waves(p->head_dim, p->n_kv);
     const int nj = 32 * pl.waves;
     pl.chunks = (p->n_kv + nj - 1) / nj;
@@ -188,7 +191,10 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
     e = gdpa::launch_zero_f32(a.dq_acc, TH * p->head_dim, s);
     if (e != hipSuccess) return hip_status(e);
   }
-  e = gdpa::launch_bwd_bf16(a, p->head_dim, p->phi, pl.waves, s);
+  if (gdpa::bwd_res_supported(p->head_dim, p->n_kv))
+    e = gdpa::launch_bwd_res(a, p->phi, s);
+  else
+    e = gdpa::launch_bwd_bf16(a, p->head_dim, p->phi, pl.waves, s);
   if (e != hipSuccess) return hip_status(e);
   if (pl.need_acc) e = gdpa::launch_dq_finalize(a.dq_acc, a.dq_base, dq, TH * p->head_dim, s);
   return hip_status(e);
@@ -199,8 +205,8 @@ gdpa_status gdpa_weightgen_fwd(int32_t batch, int32_t ctx_dim, int64_t cols, con
   if (batch < 1 || ctx_dim < 1 || cols < 1 || ctx == nullptr || w == nullptr || out == nullptr)
     return GDPA_ERR_INVALID_ARGUMENT;
   if (cols % 8 != 0 || ctx_dim % 8 != 0) return GDPA_ERR_UNSUPPORTED;
-  if (cols / 128 >= INT32_MAX || batch / 128 >= 65535) return GDPA_ERR_UNSUPPORTED;
-  return hip_status(gdpa::launch_gemm_bf16(false, batch, cols, ctx_dim, ctx, w, out,
+  if ((cols / 256 + 1) * (batch / 128 + 1) >= INT32_MAX / 2) return GDPA_ERR_UNSUPPORTED;
+  return hip_status(gdpa::launch_gemm_bf16(false, false, batch, cols, ctx_dim, ctx, w, out,
                                            (hipStream_t)stream));
 }
 
@@ -209,8 +215,9 @@ gdpa_status gdpa_weightgen_bwd_w(int32_t batch, int32_t ctx_dim, int64_t cols, c
   if (batch < 1 || ctx_dim < 1 || cols < 1 || ctx == nullptr || d_out == nullptr || d_w == nullptr)
     return GDPA_ERR_INVALID_ARGUMENT;
   if (cols % 8 != 0 || ctx_dim % 8 != 0) return GDPA_ERR_UNSUPPORTED;
-  if (cols / 128 >= INT32_MAX || ctx_dim / 128 >= 65535) return GDPA_ERR_UNSUPPORTED;
-  return hip_status(gdpa::launch_gemm_bf16(true, ctx_dim, cols, batch, ctx, d_out, d_w,
+  if (cols >= INT32_MAX || (cols / 128 + 1) * (ctx_dim / 256 + 1) >= INT32_MAX / 2)
+    return GDPA_ERR_UNSUPPORTED;
+  return hip_status(gdpa::launch_gemm_bf16(true, true, (int)cols, ctx_dim, batch, d_out, ctx, d_w,
                                            (hipStream_t)stream));
 }
 

@@ -91,7 +91,7 @@ __device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 
 // Work-group id remapped so that the WGs of one XCD (hardware places WG i on
 // XCD i % 8) take a contiguous range of the work list; neighbouring work items
 // (the q-tiles of one sample and head) then share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+__device__ __forceinline__ int xcd_remap(int bid, int grid) {  // grid % 8 == 0
   const int per = grid >> 3;  // grid is a multiple of 8
   return (bid & 7) * per + (bid >> 3);
 }

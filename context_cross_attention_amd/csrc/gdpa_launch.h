@@ -71,9 +71,15 @@ int bwd_bf16_waves(int d, int n);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int d, int phi, hipStream_t s);
 
-// Weight-generation GEMM (gdpa_gemm.hip): C[M][N] = op(A) B, bf16 in/out, fp32 accumulate.
-// a_trans = false: A is [M][K]; a_trans = true: A is [K][M].  B is [K][N].
-hipError_t launch_gemm_bf16(bool a_trans, int M, int64_t N, int K, const void* A, const void* B,
-                            void* C, hipStream_t s);
+// Backward with one work-group per (sample, head) for d = 128, n <= 256 (gdpa_bwd_res.hip).
+bool bwd_res_supported(int d, int n);
+hipError_t launch_bwd_res(const BwdArgs& a, int phi, hipStream_t s);
+
+// Weight-generation GEMM (gdpa_gemm.hip): C[M][N] = sum_k A(m,k) B(n,k), bf16 in/out,
+// fp32 accumulate.  A is [M][K] (a_kmajor = false) or [K][M] (true); B is [N][K] or
+// [K][N].  Rows of the operands with k-major layout must be a multiple of 8; with
+// k-contiguous layout K must be a multiple of 8.
+hipError_t launch_gemm_bf16(bool a_kmajor, bool b_kmajor, int M, int64_t N, int K, const void* A,
+                            const void* B, void* C, hipStream_t s);
 
 }  // namespace gdpa

@@ -4,11 +4,11 @@ Each layer (Telegram review of the Kunlun paper, layer steps 1-2; paper summary
 section 2.2: GDPA "allows stable stacking of the PFFN", read here as a plain
 residual with no normalisation):
 
-    K_l = C W_K^l,  V_l = C W_V^l                 (weight generation, [B, n*H*d])
+    K_l = C W_K^l^T,  V_l = C W_V^l^T             (weight generation, W: [n*H*d, c])
     X_{l+1} = X_l + GDPA_phi(X_l; K_l, V_l)       (queries are the token states)
 
 Backward of sum(X_L * G):
-    dX_l = dX_{l+1} + dQ_l,   dW_K^l = C^T dK_l,   dW_V^l = C^T dV_l.
+    dX_l = dX_{l+1} + dQ_l,   dW_K^l = dK_l^T C,   dW_V^l = dV_l^T C.
 
 All buffers are allocated once; a step only sequences library calls on the
 current stream.  Only SiLU (the FFN form) is stacked: the softmax backward would
@@ -34,7 +34,7 @@ class StackedGdpa:
         self.L = len(w_k)
         self.B, self.c = ctx.shape
         self.H, self.n = heads, n_kv
-        self.d = w_k[0].shape[1] // (n_kv * heads)
+        self.d = w_k[0].shape[0] // (n_kv * heads)
         self.T = total_tokens
         self.phi, self.scale = phi, scale
         T, H, d, B, n = self.T, self.H, self.d, self.B, self.n

@@ -112,14 +112,15 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
 
 /* Weight generation (paper summary section 2.1, interaction block; Telegram
  * review, layer step 1: K and V are obtained from the context features), read
- * as one linear map per layer:  out[B, cols] = ctx[B, ctx_dim] * w[ctx_dim, cols],
- * bf16 in and out, fp32 accumulation.  With cols = n_kv*H*d the output is K or V
- * in the [B][n_kv][H][d] layout.  Requires cols % 8 == 0 and ctx_dim % 8 == 0. */
+ * as one linear map per layer with an output-major weight (the usual linear-layer
+ * layout):  out[B, cols] = ctx[B, ctx_dim] * w[cols, ctx_dim]^T, bf16 in and out,
+ * fp32 accumulation.  With cols = n_kv*H*d the output is K or V in the
+ * [B][n_kv][H][d] layout.  Requires cols % 8 == 0 and ctx_dim % 8 == 0. */
 gdpa_status gdpa_weightgen_fwd(int32_t batch, int32_t ctx_dim, int64_t cols, const void* ctx,
                                const void* w, void* out, void* stream);
 
-/* Gradient of the weight-generation map w.r.t. w:  d_w[ctx_dim, cols] = ctx^T * d_out
- * (overwritten), bf16 in and out, fp32 accumulation over the batch. */
+/* Gradient of the weight-generation map w.r.t. w:  d_w[cols, ctx_dim] = d_out^T * ctx
+ * (overwritten; same layout as w), bf16 in and out, fp32 accumulation over the batch. */
 gdpa_status gdpa_weightgen_bwd_w(int32_t batch, int32_t ctx_dim, int64_t cols, const void* ctx,
                                  const void* d_out, void* d_w, void* stream);
 

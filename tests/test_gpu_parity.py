@@ -79,11 +79,13 @@ def test_bf16_explicit_scale(gdpa_lib):
     run_case(gdpa_lib, custom_config((90, 140), H=2, d=128, n=128, phi="silu"), "silu", scale=0.5)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_residual_and_accumulated_dq(gdpa_lib, dtype):
-    """O = X + GDPA(X) and dX += dQ computed in place in the dO buffer."""
+@pytest.mark.parametrize("dtype,d,n", [("bf16", 64, 96), ("f32", 64, 96), ("bf16", 128, 200)])
+@pytest.mark.parametrize("mode", ["accumulate", "residual"])
+def test_residual_and_accumulated_dq(gdpa_lib, dtype, d, n, mode):
+    """O = X + GDPA(X), and dX = dO + dQ written in place over dO, either by
+    accumulating into a dq buffer that already holds dO or by the residual flag."""
     cca = gdpa_lib
-    cfg = custom_config((100, 0, 260, 7), H=2, d=64, n=96, dtype=dtype, phi="silu")
+    cfg = custom_config((100, 0, 260, 7), H=2, d=d, n=n, dtype=dtype, phi="silu")
     inp = gi.make_gdpa_inputs(cfg, seed=3)
     q, off, k, v, do = device_inputs(inp)
     o, _ = cca.fwd(q, off, k, v, phi="silu", residual=q)
@@ -92,7 +94,10 @@ def test_residual_and_accumulated_dq(gdpa_lib, dtype):
     assert max_abs_rel(o, o_ref) <= TOL[dtype]
     dq_ref, dk_ref, dv_ref = orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, "silu")
     dx = do.clone()
-    dq, dk, dv = cca.bwd(q, off, k, v, None, None, dx, phi="silu", dq=dx, accumulate_dq=True)
+    if mode == "accumulate":
+        dq, dk, dv = cca.bwd(q, off, k, v, None, None, dx, phi="silu", dq=dx, accumulate_dq=True)
+    else:
+        dq, dk, dv = cca.bwd(q, off, k, v, None, None, dx, phi="silu", dq=dx, residual=True)
     torch.cuda.synchronize()
     assert dq.data_ptr() == dx.data_ptr()
     assert max_abs_rel(dx, dq_ref + orc.as_f64(inp.do)) <= TOL[dtype]
