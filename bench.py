@@ -11,13 +11,25 @@ C^T dV.
 
 `value` is GDPA forward+backward TFLOP/s over the whole step (algorithmic
 FLOPs 12*T*H*n*d per layer, the weight-generation time counted in the
-denominator, its FLOPs not in the numerator).  Prints one JSON line.
+denominator, its FLOPs not in the numerator).  `gdpa_only_tflops` divides the
+same FLOPs by the GDPA kernels' own time.  Prints one JSON line.
+
+`roofline` describes the kernel with the largest share of the step: achieved
+algorithmic bytes (or FLOPs) per launch over its average launch time, timed
+with HIP events on the stream the library launches on.  `roofline.traffic` is
+the HBM traffic per launch measured by rocprofv3 counters (FETCH_SIZE and
+WRITE_SIZE, each scaled by the same counter's reading for a plain device copy
+of known size, see --calibrate-copy); it is read from the committed summary in
+profiles/ and reported only while the kernel sources still hash to the value
+recorded there.
 
     python bench.py [--steps K] [--warmup W] [--config {2,3,4,5}] [--phi softmax|silu]
+    python bench.py --calibrate-copy MIB   # plain copy of MIB MiB, for counter scaling
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -42,7 +54,47 @@ def parse():
     ap.add_argument("--phi", default=None, choices=[None, "softmax", "silu"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
+
+
+CSRC = os.path.join(ROOT, "context_cross_attention_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stacked_b1024_h8_d128_n256.json")
+
+
+def kernel_source_hash():
+    """sha256 over the library's kernel sources, to tie counter readings to a kernel version."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
 # ---------------------------------------------------------------------------
@@ -127,7 +179,7 @@ def cpu_baseline_stacked(inp, cfg):
     import numpy as np
     from oracle import gdpa_oracle as orc
     per_tok = 12.0 * cfg.layers * cfg.heads * cfg.n_kv * cfg.head_dim
-    samples = pick_samples(inp.lengths, per_tok, 1.2e11, 8)
+    samples = pick_samples(inp.lengths, per_tok, 3.0e11, 16)
     off = inp.offsets.numpy().astype(np.int64)
     rows = np.concatenate([np.arange(off[b], off[b + 1]) for b in samples])
     sub_off = np.concatenate([[0], np.cumsum([inp.lengths[b] for b in samples])])
@@ -177,6 +229,10 @@ def main():
         print(msg, file=sys.stderr)
         print(json.dumps({"error": msg, "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
 
     import numpy as np
     import torch
@@ -272,7 +328,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(f_dom / t_dom / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom)
     roof["kernel"] = dom
     roof["launch_ms"] = round(per_launch[dom], 4)
     roof["algorithmic_per_launch"] = {"flops": f_dom, "bytes": b_dom}
@@ -302,6 +358,8 @@ def main():
         "config": {"workload": workload, "global_batch": B, "tokens": T, "heads": H, "head_dim": d,
                    "n_kv": n, "layers": cfg.layers or 1, "phi": phi, "seed": args.seed},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "gdpa_only_tflops": round(gdpa_flops / (sum(totals.get(k, 0.0) for k in ("gdpa_fwd", "gdpa_bwd"))
+                                               / args.steps * 1e-3) / 1e12, 2),
         "gdpa_tflop_per_step": round(gdpa_flops / 1e12, 3),
         "e2e_tflops_incl_weightgen": round((gdpa_flops + wg_flops) / (ms_per_step * 1e-3) / 1e12, 2),
         "breakdown_ms_per_step": breakdown,
