@@ -9,17 +9,24 @@
 //     accumulators (32 x 128 each) for the whole sample, with their K and V rows
 //     in registers as MFMA B operands.  Rows past n are zero.
 //   * K^T is resident in LDS ([d][j]) for the dQ product.
-//   * Per 32-row query step the work-group stages Q and dO both row-major (A
-//     operands of S = Q K^T and dP = dO V^T) and transposed with the tokens in
-//     C-tile order (B operands of dK += dS^T Q and dV += P^T dO), and writes dS
-//     row-major (operand of dQ).  Every MFMA operand read is a 16-byte,
-//     bank-conflict-free LDS read; there are no transpose loads in the loop.
+//   * Q and dO (and, for softmax, the row LSE and rowsum(dO O)) of each 32-row
+//     query step reach LDS by asynchronous global->LDS copies issued by waves
+//     4..7 two steps ahead into a 3-slot ring (row-major, 16-byte chunks XOR-
+//     swizzled by row so that 8 consecutive rows of one chunk hit distinct banks):
+//     no registers hold staged data and HBM latency is covered by two steps of
+//     compute.  The row-major tiles are the A operands of S = Q K^T and
+//     dP = dO V^T; each step also writes them transposed with the tokens in
+//     C-tile order (B operands of dK += dS^T Q and dV += P^T dO), zero past the
+//     sample's last row, and writes dS row-major (operand of dQ).  Every MFMA
+//     operand read is a 16-byte, bank-conflict-free LDS read; there are no
+//     transpose loads in the loop.
 //   * Waves 0..3 then compute dQ^T for head columns 32 w .. 32 w + 31 over all
 //     context rows (dQ^T = K^T dS^T), whose C tile gives each lane four
 //     consecutive columns of one token: 8-byte stores, residual dO added in fp32.
 //   * The score scale is applied once, to dQ per step and to dK at the end.
-//   * Global loads are unconditional (rows clamped into the sample); the next
-//     step's Q / dO are loaded during the dK / dV and dQ products of this one.
+//   * Global addresses are clamped into the sample (copies past its last step
+//     re-read valid rows into the free slot, which keeps every wave's count of
+//     outstanding copies fixed for its s_waitcnt).
 // Work-groups are launched longest sample first.
 #include "gdpa_device.h"
 #include "gdpa_launch.h"
@@ -44,18 +51,20 @@ __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0
 template <int PHI, int DQB>
 __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   constexpr int D = 128, NT = 512, NJ = 256, BQ = 32, KS = D / 16, DT = D / 32;
-  constexpr int LDQ = D + 8;    // Qs, dOs rows (68 dwords: 8 consecutive rows conflict free)
   constexpr int LDT = BQ + 8;   // Qt, dOt rows (20 dwords: likewise)
   constexpr int LDJ = NJ + 8;   // Kt and dS rows (132 dwords)
   constexpr int LDE = D;        // bf16 dK / dV rows in the epilogue
-  static_assert(BQ * D / 8 == NT, "one 16-byte staging chunk per thread and tensor");
+  // Ring slot: Q tile [32][128] and dO tile (bf16, 256-byte rows of sixteen 16-byte
+  // chunks, chunk c of row t stored at position c ^ (t & 7)), then LSE[32] and
+  // rowsum(dO O)[32] (fp32, softmax only).
+  constexpr int NSLOT = 3, TILE_B = BQ * D * 2, SLOT_B = 2 * TILE_B + 2 * BQ * 4;
+  constexpr int DMA_OPS = PHI == 0 ? 5 : 4;  // copies per step issued by each of waves 4..7
+  static_assert(BQ * D / 8 == NT, "one 16-byte chunk per thread and tensor");
   __shared__ __align__(16) uint16_t Kt[D * LDJ];
-  __shared__ __align__(16) uint16_t Qs[BQ * LDQ];
-  __shared__ __align__(16) uint16_t dOs[BQ * LDQ];
+  __shared__ __align__(16) uint8_t ring[NSLOT * SLOT_B];
   __shared__ __align__(16) uint16_t Qt[D * LDT];
   __shared__ __align__(16) uint16_t dOt[D * LDT];
   __shared__ __align__(16) uint16_t dSs[BQ * LDJ];
-  __shared__ __align__(16) float lse_s[BQ], dvec_s[BQ];
   static_assert(8 * 32 * LDE <= D * LDJ, "epilogue tiles must fit in Kt");
 
   const int H = a.H, n = a.n;
@@ -101,43 +110,57 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   }
 
   const float scale = a.scale, sl2 = scale * kLog2e, c1 = -scale * kLog2e;
-  const uint16_t* Qg = (const uint16_t*)a.q + (size_t)h * D;
-  const uint16_t* dOg = (const uint16_t*)a.d_o + (size_t)h * D;
 
-  // Staging: thread tid -> token t = tid % 32, column chunk c = tid / 32 (consecutive
-  // lanes take consecutive tokens).
-  const int st_t = tid % BQ, st_c = tid / BQ;
-  u32x4 qn, dn;
-  float lse_n = 0.f, dvec_n = 0.f;
-  auto load_step = [&](int tq) {
-    const size_t off = (size_t)(seq0 + min(tq + st_t, L - 1)) * rs + 8 * st_c;
-    qn = gload16(Qg + off);
-    dn = gload16(dOg + off);
-    if (PHI == 0) {
-      const size_t r = (size_t)(seq0 + min(tq + (tid & (BQ - 1)), L - 1)) * H + h;
-      lse_n = a.lse[r] * kLog2e;
-      dvec_n = a.dvec[r];
+  // Ring copies for step `st` (waves 4..7): wave w copies rows 8 (w - 4) .. + 7 of the Q
+  // and dO tiles, four rows (1 KiB) per instruction; lane i takes row 4 k + i / 16 and
+  // ring position i % 16, i.e. chunk (i % 16) ^ (row & 7) of the global row.
+  const int nsteps = (L + BQ - 1) / BQ;
+  auto issue = [&](int st) {
+    const int tq = st * BQ;
+    const uint32_t sb = lds_addr(ring) + (uint32_t)((st % NSLOT) * SLOT_B);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int row = 8 * (wave - 4) + 4 * k + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 7);
+      const size_t off = (size_t)(seq0 + min(tq + row, L - 1)) * rs + (size_t)h * D + 8 * c;
+      const uint32_t lo = (uint32_t)((8 * (wave - 4) + 4 * k) * 256);
+      dma16(__builtin_amdgcn_readfirstlane(sb + lo), (const uint16_t*)a.q + off);
+      dma16(__builtin_amdgcn_readfirstlane(sb + TILE_B + lo), (const uint16_t*)a.d_o + off);
+    }
+    if (PHI == 0) {  // lanes 0..31: LSE of rows 0..31; lanes 32..63: rowsum(dO O)
+      const size_t r = (size_t)(seq0 + min(tq + lr, L - 1)) * H + h;
+      dma4(__builtin_amdgcn_readfirstlane(sb + 2 * TILE_B), g == 0 ? (const void*)(a.lse + r) : (const void*)(a.dvec + r));
     }
   };
-  if (L > 0) load_step(0);
+  if (L > 0 && wave >= 4) {
+    issue(0);
+    issue(1);
+  }
 
-  for (int tq = 0; tq < L; tq += BQ) {
-    const int rows = min(BQ, L - tq);
-    __syncthreads();  // previous step finished with the step buffers
+  for (int s = 0; s < nsteps; ++s) {
+    const int tq = s * BQ, rows = min(BQ, L - tq);
+    const uint8_t* slot = ring + (s % NSLOT) * SLOT_B;
+    const uint16_t* Qs = (const uint16_t*)slot;
+    const uint16_t* dOs = (const uint16_t*)(slot + TILE_B);
+    const float* lse_s = (const float*)(slot + 2 * TILE_B);
+    const float* dvec_s = lse_s + BQ;
+    const int lx = opaque(lr), gx = opaque(g), tx = opaque(tid);
+    // This wave's copies for step s are complete once only the next step's remain.
+    if (wave >= 4) wait_vmcnt<DMA_OPS>();
+    __syncthreads();  // step s in LDS; step s - 1 finished with Qt, dOt, dSs and its slot
+    if (wave >= 4) issue(s + 2);
     {
-      const bool ok = st_t < rows;
-      const u32x4 qv = ok ? qn : u32x4{}, dv = ok ? dn : u32x4{};
-      lds_write16(&Qs[st_t * LDQ + 8 * st_c], qv);
-      lds_write16(&dOs[st_t * LDQ + 8 * st_c], dv);
-      const int p = tok_pos(st_t);
+      // Transposed copies: thread -> token t = tid % 32, chunk c = tid / 32.
+      const int t = tx % BQ, c = tx / BQ;
+      const int o = t * D + 8 * (c ^ (t & 7));
+      const bool ok = t < rows;
+      const u32x4 qv = ok ? *(const GDPA_LDS u32x4*)&Qs[o] : u32x4{};
+      const u32x4 dv = ok ? *(const GDPA_LDS u32x4*)&dOs[o] : u32x4{};
+      const int p = tok_pos(t);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        Qt[(8 * st_c + e) * LDT + p] = half_of(qv, e);
-        dOt[(8 * st_c + e) * LDT + p] = half_of(dv, e);
-      }
-      if (PHI == 0 && tid < BQ) {
-        lse_s[tid] = tid < rows ? lse_n : INFINITY;
-        dvec_s[tid] = tid < rows ? dvec_n : 0.f;
+        Qt[(8 * c + e) * LDT + p] = half_of(qv, e);
+        dOt[(8 * c + e) * LDT + p] = half_of(dv, e);
       }
     }
     __syncthreads();
@@ -146,7 +169,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
     f32x16 S = f32x16{}, dP = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int o = lr * LDQ + 16 * ks + 8 * g;
+      const int o = lx * D + 8 * ((2 * ks + gx) ^ (lx & 7));
       S = mfma32(lds_read8(&Qs[o]), kf[ks], S);
       dP = mfma32(lds_read8(&dOs[o]), vf[ks], dP);
     }
@@ -160,7 +183,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * q4 + c;
-          float p = fast_exp2(fmaf(S[r], sl2, -ls[c]));
+          float p = fast_exp2(fmaf(S[r], sl2, -ls[c] * kLog2e));
           if (!jvalid) p = 0.f;
           S[r] = p;
           dP[r] = p * (dP[r] - dvv[c]);
@@ -188,8 +211,6 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       for (int i = 0; i < 8; ++i)
         dSs[(16 * kk + 8 * (i >> 2) + 4 * g + (i & 3)) * LDJ + j] = half_of(sw, i);
     }
-    // The next step's Q / dO are loaded here, where S and dP are no longer live.
-    if (tq + BQ < L) load_step(tq + BQ);
     // dV += P^T dO, dK += dS^T Q over the 32 tokens.
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -216,7 +237,8 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
           float v0 = dq[4 * q4] * scale, v1 = dq[4 * q4 + 1] * scale;
           float v2 = dq[4 * q4 + 2] * scale, v3 = dq[4 * q4 + 3] * scale;
           u32x2 base = u32x2{0u, 0u};
-          if (DQB == 1) base = *(const GDPA_LDS u32x2*)&dOs[lr * LDQ + 32 * wave + 8 * q4 + 4 * g];
+          if (DQB == 1)
+            base = *(const GDPA_LDS u32x2*)&dOs[lr * D + 8 * ((4 * wave + q4) ^ (lr & 7)) + 4 * g];
           if (DQB == 2) base = *(const u32x2*)(dst + 8 * q4);
           if (DQB != 0) {
             v0 += lo_f(base[0]);
@@ -237,6 +259,9 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
 
   // dK (times the scale) and dV through LDS (Kt's space, once every wave is done
   // with it) as bf16 32 x 128 tiles per wave, then 16-byte stores of rows j < n.
+  // The copies issued for the two steps past the end land before the work-group
+  // releases its LDS.
+  if (wave >= 4) wait_vmcnt<0>();
   __syncthreads();
   uint16_t* Ew = Kt + wave * 32 * LDE;
 #pragma unroll

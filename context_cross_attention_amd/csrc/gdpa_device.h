@@ -88,6 +88,42 @@ __device__ __forceinline__ float fast_sigmoid(float s) {
 
 __device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// The value of x, hidden from the optimiser: per-lane index arithmetic derived from
+// it inside a loop is recomputed there (a few VALU instructions) instead of being
+// hoisted into registers held across the loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Byte address of an LDS location, as the hardware sees it (M0 / DS addresses).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const GDPA_LDS void*)p;
+}
+
+// Asynchronous copy global -> LDS of 16 bytes per lane: lane i's 16 bytes from
+// `src` land at LDS byte address `lds_base + 16 i` (lds_base wave-uniform).  No
+// VGPR receives data; completion is tracked by the wave's vmcnt like any vector
+// memory load, so the caller waits with s_waitcnt vmcnt before a barrier that
+// publishes the data.  M0 is not used by the compiler in the kernels that call
+// this (checked in their assembly), so it is set here without being restored.
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void* src) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_base), "v"(src) : "memory");
+}
+// Same with 4 bytes per lane (lane i -> lds_base + 4 i).
+__device__ __forceinline__ void dma4(uint32_t lds_base, const void* src) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds_base), "v"(src) : "memory");
+}
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited for); N < 64 (vmcnt is split
+// over bits 3:0 and 15:14 of the immediate).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Work-group id remapped so that the WGs of one XCD (hardware places WG i on
 // XCD i % 8) take a contiguous range of the work list; neighbouring work items
 // (the q-tiles of one sample and head) then share that XCD's L2.
