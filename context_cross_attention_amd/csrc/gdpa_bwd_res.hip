@@ -40,6 +40,14 @@ namespace {
 // t = 16 kk + 8 a + 4 g + c goes to 16 kk + 8 g + 4 a + c.
 __device__ __forceinline__ int tok_pos(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
 
+// dQ^T = K^T dS^T: the A operand's row i = 8 a + 4 b + c of each 32-column block is
+// head column kt_row(i) = 16 b + 4 a + c, so that C-tile lane group g holds the 16
+// consecutive columns 16 g .. 16 g + 15 in register order (two 16-byte stores).
+// K^T stores the 16-byte chunk q of row d at chunk q ^ (4 (d / 16 % 2)) so that the rows
+// {0..3, 16..19} + 4 k read by 8 consecutive lanes fall in distinct banks.
+__device__ __forceinline__ int kt_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+__device__ __forceinline__ int kt_col(int j, int d) { return 8 * ((j >> 3) ^ (((d >> 4) & 1) << 2)) + (j & 7); }
+
 __device__ __forceinline__ uint16_t half_of(const u32x4& v, int i) {
   return (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
 }
@@ -98,7 +106,10 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       kf[ks] = as_bf16x8(kr[ks]);
       vf[ks] = as_bf16x8(vr[ks]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) Kt[(16 * ks + 8 * g + i) * LDJ + j] = half_of(kr[ks], i);
+      for (int i = 0; i < 8; ++i) {
+        const int d = 16 * ks + 8 * g + i;
+        Kt[d * LDJ + kt_col(j, d)] = half_of(kr[ks], i);
+      }
     }
   }
 
@@ -225,33 +236,34 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
     if (wave < 4) {
       // dQ^T[32 w .. 32 w + 31, tokens] = K^T dS^T over all 256 context rows.
       f32x16 dq = f32x16{};
-      const int oa = (32 * wave + lr) * LDJ + 8 * g, ob = lr * LDJ + 8 * g;
+      // Row kr of K^T, columns 16 ks + 8 g .. + 7: the chunk swizzle moves them by
+      // +-32 (sign from bit 1 of ks) on rows with bit 4 set, so two base addresses plus
+      // immediate offsets cover all k-steps.
+      const int lxd = opaque(lr);
+      const int kr = 32 * wave + kt_row(lxd);
+      const int sw = ((kr >> 4) & 1) * 32;
+      const int oa_p = kr * LDJ + 8 * g + sw, oa_m = kr * LDJ + 8 * g - sw;
+      const int ob = lxd * LDJ + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < NJ / 16; ++ks)
-        dq = mfma32(lds_read8(&Kt[oa + 16 * ks]), lds_read8(&dSs[ob + 16 * ks]), dq);
-      // Lane (t + 32 g), register r: column 32 w + 8 (r / 4) + 4 g + r % 4 of token t = lr.
+        dq = mfma32(lds_read8(&Kt[((ks >> 1) & 1 ? oa_m : oa_p) + 16 * ks]), lds_read8(&dSs[ob + 16 * ks]), dq);
+      // Lane (t + 32 g), register r: column 32 w + 16 g + r of token t = lr.
       if (lr < rows) {
-        uint16_t* dst = (uint16_t*)a.dq + (size_t)(seq0 + tq + lr) * rs + (size_t)h * D + 32 * wave + 4 * g;
+        uint16_t* dst = (uint16_t*)a.dq + (size_t)(seq0 + tq + lr) * rs + (size_t)h * D + 32 * wave + 16 * g;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float v0 = dq[4 * q4] * scale, v1 = dq[4 * q4 + 1] * scale;
-          float v2 = dq[4 * q4 + 2] * scale, v3 = dq[4 * q4 + 3] * scale;
-          u32x2 base = u32x2{0u, 0u};
+        for (int hh = 0; hh < 2; ++hh) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = dq[8 * hh + e] * scale;
+          u32x4 base = u32x4{0u, 0u, 0u, 0u};
           if (DQB == 1)
-            base = *(const GDPA_LDS u32x2*)&dOs[lr * D + 8 * ((4 * wave + q4) ^ (lr & 7)) + 4 * g];
-          if (DQB == 2) base = *(const u32x2*)(dst + 8 * q4);
+            base = *(const GDPA_LDS u32x4*)&dOs[lr * D + 8 * ((4 * wave + 2 * g + hh) ^ (lr & 7))];
+          if (DQB == 2) base = gload16(dst + 8 * hh);
           if (DQB != 0) {
-            v0 += lo_f(base[0]);
-            v1 += hi_f(base[0]);
-            v2 += lo_f(base[1]);
-            v3 += hi_f(base[1]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += bf2f(half_of(base, e));
           }
-          bf16x4 o4;
-          o4[0] = f2bf(v0);
-          o4[1] = f2bf(v1);
-          o4[2] = f2bf(v2);
-          o4[3] = f2bf(v3);
-          *(bf16x4*)(dst + 8 * q4) = o4;
+          *(bf16x8*)(dst + 8 * hh) = pack8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
         }
       }
     }

@@ -21,11 +21,17 @@ namespace gdpa {
 // 32 t + 16 kk + 8 g + 4 a + c makes each lane's 8 operand values contiguous.
 __device__ __forceinline__ int vt_pos(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
 
-// Position of head column d inside K rows (the same bit swap): lane group g of a
-// k-step then reads columns 16 ks + 4 g .. + 3 and 16 ks + 8 + 4 g .. + 3 as one
-// 16-byte operand, which are exactly the output columns that lane holds in the
-// O^T C tile - so a residual equal to Q can be added from the Q registers.
-__device__ __forceinline__ int kcol(int d) { return vt_pos(d); }
+// Head columns.  The contraction over d of S^T = K Q^T takes, in k-step ks and lane
+// group g, the 8 consecutive columns 32 (ks / 2) + 16 g + 8 (ks % 2) .. + 7 (one
+// 16-byte read of a K row, one 16-byte load of a Q row).  In O^T += V^T P^T the
+// A operand's row i = 8 a + 4 b + c of each 32-column block is column
+// vt_row(i) = 16 b + 4 a + c, so that C-tile lane group g holds the 16 consecutive
+// columns 16 g .. 16 g + 15 in register order: two 16-byte stores per block, and
+// the residual Q columns of the same lane are exactly its Q operand items.
+__device__ __forceinline__ int vt_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+// V^T is stored with the 16-byte chunk q of row d at chunk q ^ (4 (d / 16 % 2)), so that
+// the 8 rows {0..3, 16..19} + 4 k read by 8 consecutive lanes fall in distinct banks.
+__device__ __forceinline__ int vt_chunk(int q, int d) { return q ^ (((d >> 4) & 1) << 2); }
 
 // RESID: 0 none, 1 residual is the query tensor, 2 a separate residual tensor.
 template <int D, int NMAX, int PHI, int RESID>
@@ -64,10 +70,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
     for (int i = 0; i < KI; ++i) {
       const int idx = i * NT + tid, j = idx / CH, c = idx % CH;
       if (j < npad) {
-        const u32x4 v = j < n ? kr[i] : u32x4{};
-        // Columns 8c .. 8c+3 and 8c+4 .. 8c+7 go to their permuted positions.
-        lds_write8(&Kc[j * LDK + kcol(8 * c)], u32x2{v[0], v[1]});
-        lds_write8(&Kc[j * LDK + kcol(8 * c + 4)], u32x2{v[2], v[3]});
+        lds_write16(&Kc[j * LDK + 8 * c], j < n ? kr[i] : u32x4{});
       }
     }
   }
@@ -96,7 +99,8 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         const int sh = 16 * (e & 1);
         const uint32_t h0 = (vr[i][0][e >> 1] >> sh) & 0xffffu, h1 = (vr[i][1][e >> 1] >> sh) & 0xffffu;
         const uint32_t h2 = (vr[i][2][e >> 1] >> sh) & 0xffffu, h3 = (vr[i][3][e >> 1] >> sh) & 0xffffu;
-        lds_write8(&Vt[(8 * dc + e) * LDV + pos], u32x2{h0 | (h1 << 16), h2 | (h3 << 16)});
+        const int d = 8 * dc + e;
+        lds_write8(&Vt[d * LDV + 8 * vt_chunk(pos >> 3, d) + (pos & 7)], u32x2{h0 | (h1 << 16), h2 | (h3 << 16)});
       }
     }
   }
@@ -105,18 +109,14 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
   const float sl2 = a.scale * kLog2e, nsl2 = -sl2;
   const int nchunks = (L + 31) / 32;
   // Query rows past the sample are read from its last row (clamped, always a
-  // valid address) and never stored: each lane's row is independent.  With the
-  // K column permutation, k-step ks of lane group g takes columns
-  // 16 ks + 4 g .. + 3 and 16 ks + 8 + 4 g .. + 3.
-  const uint16_t* Qg = (const uint16_t*)a.q + (size_t)h * D + 4 * g;
+  // valid address) and never stored: each lane's row is independent.  k-step ks of
+  // lane group g takes columns 32 (ks / 2) + 16 g + 8 (ks % 2) .. + 7.
+  const uint16_t* Qg = (const uint16_t*)a.q + (size_t)h * D + 16 * g;
   auto load_q = [&](int ch, bf16x8* dst) {
     const int t = min(32 * ch + lr, L - 1);
     const uint16_t* qp = Qg + (size_t)(seq0 + t) * rs;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x2 lo = *(const u32x2*)(qp + 16 * ks), hi = *(const u32x2*)(qp + 16 * ks + 8);
-      dst[ks] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
+    for (int ks = 0; ks < KS; ++ks) dst[ks] = as_bf16x8(gload16(qp + 32 * (ks >> 1) + 8 * (ks & 1)));
   };
 
   // One 32-row chunk with Q already in qc; prefetches the Q of chunk ch + NW into qn.
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
     const int t = 32 * ch + lr;
     const bool tvalid = t < L;
     load_q(ch + NW, qn);
-    const size_t obase = (size_t)(seq0 + min(t, L - 1)) * rs + (size_t)h * D + 4 * g;
+    const size_t obase = (size_t)(seq0 + min(t, L - 1)) * rs + (size_t)h * D + 16 * g;
     f32x16 O[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
       S = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        S = mfma32(lds_read8(&Kc[(j0 + lr) * LDK + 16 * ks + 8 * g]), qc[ks], S);
+        S = mfma32(lds_read8(&Kc[(j0 + lr) * LDK + 32 * (ks >> 1) + 16 * g + 8 * (ks & 1)]), qc[ks], S);
     };
     // phi of one 32-row tile, then O^T += V^T P^T.
     auto mix = [&](int j0, f32x16& S) {
@@ -177,7 +177,8 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const bf16x8 p = pack_c8(S, kk);
-        const uint16_t* vb = &Vt[lr * LDV + j0 + 16 * kk + 8 * g];
+        const int vr = vt_row(lr);  // V^T row within each 32-column block
+        const uint16_t* vb = &Vt[vr * LDV + 8 * vt_chunk((j0 >> 3) + 2 * kk + g, vr)];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) O[dt] = mfma32(lds_read8(vb + 32 * dt * LDV), p, O[dt]);
       }
@@ -208,30 +209,26 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         a.lse[(size_t)(seq0 + t) * H + h] = (m_run + __log2f(l_tot)) * kLn2;
     }
     if (tvalid) {
+      // Lane group g holds columns 32 dt + 16 g + r in register r (see vt_row).
       uint16_t* op = (uint16_t*)a.o + obase;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float v0 = O[dt][4 * q4 + 0], v1 = O[dt][4 * q4 + 1];
-          float v2 = O[dt][4 * q4 + 2], v3 = O[dt][4 * q4 + 3];
+        for (int hh = 0; hh < 2; ++hh) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = O[dt][8 * hh + e];
           if (RESID == 1) {
-            // Residual is Q itself: O column 32 dt + 8 q4 + 4 g + c is item
-            // 4 (q4 % 2) + c of the k-step 2 dt + q4 / 2 fragment of this lane.
-            const bf16x8 qv = qc[2 * dt + (q4 >> 1)];
-            const int o = 4 * (q4 & 1);
-            v0 += (float)qv[o + 0]; v1 += (float)qv[o + 1];
-            v2 += (float)qv[o + 2]; v3 += (float)qv[o + 3];
+            // Residual is Q itself: the same columns are items of the Q operand.
+            const bf16x8 qv = qc[2 * dt + hh];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += (float)qv[e];
           } else if (RESID == 2) {
-            const u32x2 rr = *(const u32x2*)((const uint16_t*)a.residual + obase + 32 * dt + 8 * q4);
-            v0 += __uint_as_float(rr[0] << 16);
-            v1 += __uint_as_float(rr[0] & 0xffff0000u);
-            v2 += __uint_as_float(rr[1] << 16);
-            v3 += __uint_as_float(rr[1] & 0xffff0000u);
+            const u32x4 rr = gload16((const uint16_t*)a.residual + obase + 32 * dt + 8 * hh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += bf2f((uint16_t)(rr[e >> 1] >> (16 * (e & 1))));
           }
-          bf16x4 ov;
-          ov[0] = f2bf(v0); ov[1] = f2bf(v1); ov[2] = f2bf(v2); ov[3] = f2bf(v3);
-          *(bf16x4*)(op + 32 * dt + 8 * q4) = ov;
+          *(bf16x8*)(op + 32 * dt + 8 * hh) = pack8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
         }
     }
   };
