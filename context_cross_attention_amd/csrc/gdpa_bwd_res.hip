@@ -11,18 +11,20 @@
 //   * K^T is resident in LDS ([d][j]) for the dQ product.
 //   * Q and dO (and, for softmax, the row LSE and rowsum(dO O)) of each 32-row
 //     query step reach LDS by asynchronous global->LDS copies issued by waves
-//     4..7 two steps ahead into a 3-slot ring (row-major, 16-byte chunks XOR-
-//     swizzled by row so that 8 consecutive rows of one chunk hit distinct banks):
-//     no registers hold staged data and HBM latency is covered by two steps of
-//     compute.  The row-major tiles are the A operands of S = Q K^T and
-//     dP = dO V^T; each step also writes them transposed with the tokens in
-//     C-tile order (B operands of dK += dS^T Q and dV += P^T dO), zero past the
-//     sample's last row, and writes dS row-major (operand of dQ).  Every MFMA
+//     4..7 two steps ahead into a 3-slot ring: no registers hold staged data and
+//     HBM latency is covered by two steps of compute.  Each copying wave brings in
+//     one 32-column block of both tiles (rows of 64 bytes, 16-byte chunks XOR-
+//     swizzled by row pair so that 8 consecutive rows of one chunk hit distinct
+//     banks).  The row-major tiles are the A operands of S = Q K^T and dP = dO V^T.
+//   * The same wave writes its block transposed, with the tokens in C-tile order
+//     (B operands of dK += dS^T Q and dV += P^T dO; zero past the sample's last
+//     row), for the next step while waves 0..3 compute dQ: it waits only for its
+//     own copies, and the transposition costs the step no barrier.  Every MFMA
 //     operand read is a 16-byte, bank-conflict-free LDS read; there are no
 //     transpose loads in the loop.
 //   * Waves 0..3 then compute dQ^T for head columns 32 w .. 32 w + 31 over all
-//     context rows (dQ^T = K^T dS^T), whose C tile gives each lane four
-//     consecutive columns of one token: 8-byte stores, residual dO added in fp32.
+//     context rows (dQ^T = K^T dS^T), whose C tile (rows permuted) gives each lane
+//     16 consecutive columns of one token: 16-byte stores, residual added in fp32.
 //   * The score scale is applied once, to dQ per step and to dK at the end.
 //   * Global addresses are clamped into the sample (copies past its last step
 //     re-read valid rows into the free slot, which keeps every wave's count of
@@ -62,9 +64,9 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   constexpr int LDT = BQ + 8;   // Qt, dOt rows (20 dwords: likewise)
   constexpr int LDJ = NJ + 8;   // Kt and dS rows (132 dwords)
   constexpr int LDE = D;        // bf16 dK / dV rows in the epilogue
-  // Ring slot: Q tile [32][128] and dO tile (bf16, 256-byte rows of sixteen 16-byte
-  // chunks, chunk c of row t stored at position c ^ (t & 7)), then LSE[32] and
-  // rowsum(dO O)[32] (fp32, softmax only).
+  // Ring slot: Q tile and dO tile (bf16, each 4 blocks of 32 rows x 64 bytes: block G
+  // holds head columns 32 G .. 32 G + 31 of every token, the 16-byte chunk q of row t at
+  // position q ^ ((t / 2) % 4)), then LSE[32] and rowsum(dO O)[32] (fp32, softmax only).
   constexpr int NSLOT = 3, TILE_B = BQ * D * 2, SLOT_B = 2 * TILE_B + 2 * BQ * 4;
   constexpr int DMA_OPS = PHI == 0 ? 5 : 4;  // copies per step issued by each of waves 4..7
   static_assert(BQ * D / 8 == NT, "one 16-byte chunk per thread and tensor");
@@ -122,30 +124,58 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
 
   const float scale = a.scale, sl2 = scale * kLog2e, c1 = -scale * kLog2e;
 
-  // Ring copies for step `st` (waves 4..7): wave w copies rows 8 (w - 4) .. + 7 of the Q
-  // and dO tiles, four rows (1 KiB) per instruction; lane i takes row 4 k + i / 16 and
-  // ring position i % 16, i.e. chunk (i % 16) ^ (row & 7) of the global row.
+  // Ring copies for step `st` (waves 4..7): wave w copies block G = w - 4 (columns
+  // 32 G .. 32 G + 31 of all 32 rows) of the Q and dO tiles, 16 rows (1 KiB) per
+  // instruction; lane i takes row 16 k + i / 4 and position i % 4.
   const int nsteps = (L + BQ - 1) / BQ;
+  auto slot_off = [](int t, int cl) { return t * 32 + 8 * (cl ^ ((t >> 1) & 3)); };  // halves
   auto issue = [&](int st) {
-    const int tq = st * BQ;
-    const uint32_t sb = lds_addr(ring) + (uint32_t)((st % NSLOT) * SLOT_B);
+    const int tq = st * BQ, G = wave - 4;
+    const uint32_t sb = lds_addr(ring) + (uint32_t)((st % NSLOT) * SLOT_B + G * 2048);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int row = 8 * (wave - 4) + 4 * k + (lane >> 4);
-      const int c = (lane & 15) ^ (row & 7);
-      const size_t off = (size_t)(seq0 + min(tq + row, L - 1)) * rs + (size_t)h * D + 8 * c;
-      const uint32_t lo = (uint32_t)((8 * (wave - 4) + 4 * k) * 256);
-      dma16(__builtin_amdgcn_readfirstlane(sb + lo), (const uint16_t*)a.q + off);
-      dma16(__builtin_amdgcn_readfirstlane(sb + TILE_B + lo), (const uint16_t*)a.d_o + off);
+      const int t = 16 * k + (lane >> 2);
+      const int c = 4 * G + ((lane & 3) ^ ((t >> 1) & 3));
+      const size_t off = (size_t)(seq0 + min(tq + t, L - 1)) * rs + (size_t)h * D + 8 * c;
+      dma16(__builtin_amdgcn_readfirstlane(sb + 1024 * k), (const uint16_t*)a.q + off);
+      dma16(__builtin_amdgcn_readfirstlane(sb + TILE_B + 1024 * k), (const uint16_t*)a.d_o + off);
     }
-    if (PHI == 0) {  // lanes 0..31: LSE of rows 0..31; lanes 32..63: rowsum(dO O)
+    if (PHI == 0) {  // lanes 0..31: LSE of rows 0..31; lanes 32..63: rowsum(dO O) (every copying wave)
       const size_t r = (size_t)(seq0 + min(tq + lr, L - 1)) * H + h;
-      dma4(__builtin_amdgcn_readfirstlane(sb + 2 * TILE_B), g == 0 ? (const void*)(a.lse + r) : (const void*)(a.dvec + r));
+      dma4(__builtin_amdgcn_readfirstlane(lds_addr(ring) + (uint32_t)((st % NSLOT) * SLOT_B + 2 * TILE_B)),
+           g == 0 ? (const void*)(a.lse + r) : (const void*)(a.dvec + r));
     }
   };
+
+  // Transposed copies of the block a copying wave brought in itself (so it only waits
+  // for its own copies): lane -> token t = lane % 32, local chunks lane / 32 and + 2;
+  // rows past the sample are zero.
+  auto transpose = [&](int st) {
+    const int tq = st * BQ, rows = min(BQ, L - tq), G = wave - 4;
+    const uint16_t* Qs = (const uint16_t*)(ring + (st % NSLOT) * SLOT_B) + G * 1024;
+    const uint16_t* dOs = Qs + TILE_B / 2;
+    const int t = opaque(lr), p = tok_pos(t);
+    const bool ok = t < rows;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int cl = (lane >> 5) + 2 * u, c = 4 * G + cl;
+      const int o = slot_off(t, cl);
+      const u32x4 qv = ok ? *(const GDPA_LDS u32x4*)&Qs[o] : u32x4{};
+      const u32x4 dv = ok ? *(const GDPA_LDS u32x4*)&dOs[o] : u32x4{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        Qt[(8 * c + e) * LDT + p] = half_of(qv, e);
+        dOt[(8 * c + e) * LDT + p] = half_of(dv, e);
+      }
+    }
+  };
+
+  // Waves 4..7: copies for steps 0 and 1, then step 0's transposed tiles.
   if (L > 0 && wave >= 4) {
     issue(0);
     issue(1);
+    wait_vmcnt<DMA_OPS>();  // this wave's copies for step 0 landed (step 1's may remain)
+    transpose(0);
   }
 
   for (int s = 0; s < nsteps; ++s) {
@@ -155,32 +185,17 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
     const uint16_t* dOs = (const uint16_t*)(slot + TILE_B);
     const float* lse_s = (const float*)(slot + 2 * TILE_B);
     const float* dvec_s = lse_s + BQ;
-    const int lx = opaque(lr), gx = opaque(g), tx = opaque(tid);
-    // This wave's copies for step s are complete once only the next step's remain.
-    if (wave >= 4) wait_vmcnt<DMA_OPS>();
-    __syncthreads();  // step s in LDS; step s - 1 finished with Qt, dOt, dSs and its slot
-    if (wave >= 4) issue(s + 2);
-    {
-      // Transposed copies: thread -> token t = tid % 32, chunk c = tid / 32.
-      const int t = tx % BQ, c = tx / BQ;
-      const int o = t * D + 8 * (c ^ (t & 7));
-      const bool ok = t < rows;
-      const u32x4 qv = ok ? *(const GDPA_LDS u32x4*)&Qs[o] : u32x4{};
-      const u32x4 dv = ok ? *(const GDPA_LDS u32x4*)&dOs[o] : u32x4{};
-      const int p = tok_pos(t);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        Qt[(8 * c + e) * LDT + p] = half_of(qv, e);
-        dOt[(8 * c + e) * LDT + p] = half_of(dv, e);
-      }
-    }
+    const int lx = opaque(lr), gx = opaque(g);
+    // Step s's slot landed (waited for by waves 4..7 before they built Qt / dOt for it)
+    // and Qt / dOt hold step s; step s - 1 is finished with dSs and its slot.
     __syncthreads();
+    if (wave >= 4) issue(s + 2);
 
     // S and dP for this wave's 32 context rows (M = tokens, N = context rows).
     f32x16 S = f32x16{}, dP = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int o = lx * D + 8 * ((2 * ks + gx) ^ (lx & 7));
+      const int o = (ks >> 1) * 1024 + slot_off(lx, (2 * ks + gx) & 3);
       S = mfma32(lds_read8(&Qs[o]), kf[ks], S);
       dP = mfma32(lds_read8(&dOs[o]), vf[ks], dP);
     }
@@ -231,8 +246,13 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
         dV[dt] = mfma32(pa[kk], lds_read8(&dOt[o]), dV[dt]);
         dK[dt] = mfma32(sa[kk], lds_read8(&Qt[o]), dK[dt]);
       }
-    __syncthreads();  // dS complete
+    __syncthreads();  // dS complete; Qt and dOt are free
 
+    if (wave >= 4 && s + 1 < nsteps) {
+      // Next step's transposed tiles, overlapping the dQ product of waves 0..3.
+      wait_vmcnt<DMA_OPS>();  // this wave's copies for step s + 1 landed (step s + 2's may remain)
+      transpose(s + 1);
+    }
     if (wave < 4) {
       // dQ^T[32 w .. 32 w + 31, tokens] = K^T dS^T over all 256 context rows.
       f32x16 dq = f32x16{};
@@ -257,7 +277,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
           for (int e = 0; e < 8; ++e) v[e] = dq[8 * hh + e] * scale;
           u32x4 base = u32x4{0u, 0u, 0u, 0u};
           if (DQB == 1)
-            base = *(const GDPA_LDS u32x4*)&dOs[lr * D + 8 * ((4 * wave + 2 * g + hh) ^ (lr & 7))];
+            base = *(const GDPA_LDS u32x4*)&dOs[wave * 1024 + slot_off(lxd, 2 * g + hh)];
           if (DQB == 2) base = gload16(dst + 8 * hh);
           if (DQB != 0) {
 #pragma unroll
