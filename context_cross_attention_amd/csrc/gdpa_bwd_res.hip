@@ -14,8 +14,8 @@
 //     4..7 two steps ahead into a 3-slot ring: no registers hold staged data and
 //     HBM latency is covered by two steps of compute.  Each copying wave brings in
 //     one 32-column block of both tiles (rows of 64 bytes, 16-byte chunks XOR-
-//     swizzled by row pair so that 8 consecutive rows of one chunk hit distinct
-//     banks).  The row-major tiles are the A operands of S = Q K^T and dP = dO V^T.
+//     swizzled by row quad so that 16 consecutive rows of one chunk, one 16-lane
+//     phase of a ds_read_b128, hit distinct banks).  The row-major tiles are the A operands of S = Q K^T and dP = dO V^T.
 //   * The same wave writes its block transposed, with the tokens in C-tile order
 //     (B operands of dK += dS^T Q and dV += P^T dO; zero past the sample's last
 //     row), for the next step while waves 0..3 compute dQ: it waits only for its
@@ -45,10 +45,12 @@ __device__ __forceinline__ int tok_pos(int t) { return (t & ~12) | ((t & 4) << 1
 // dQ^T = K^T dS^T: the A operand's row i = 8 a + 4 b + c of each 32-column block is
 // head column kt_row(i) = 16 b + 4 a + c, so that C-tile lane group g holds the 16
 // consecutive columns 16 g .. 16 g + 15 in register order (two 16-byte stores).
-// K^T stores the 16-byte chunk q of row d at chunk q ^ (4 (d / 16 % 2)) so that the rows
-// {0..3, 16..19} + 4 k read by 8 consecutive lanes fall in distinct banks.
+// K^T rows are 528 bytes apart, so row d starts at bank group d % 16 (16-byte groups of
+// the 64 4-byte banks); the 16-byte chunk q of row d is stored at chunk
+// q ^ (8 (d / 16 % 2)) so that the rows {0..3, 16..19, 4..7, 20..23} + 8 k read by one
+// 16-lane phase of a ds_read_b128 fall in distinct bank groups.
 __device__ __forceinline__ int kt_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
-__device__ __forceinline__ int kt_col(int j, int d) { return 8 * ((j >> 3) ^ (((d >> 4) & 1) << 2)) + (j & 7); }
+__device__ __forceinline__ int kt_col(int j, int d) { return 8 * ((j >> 3) ^ (((d >> 4) & 1) << 3)) + (j & 7); }
 
 __device__ __forceinline__ uint16_t half_of(const u32x4& v, int i) {
   return (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   constexpr int LDE = D;        // bf16 dK / dV rows in the epilogue
   // Ring slot: Q tile and dO tile (bf16, each 4 blocks of 32 rows x 64 bytes: block G
   // holds head columns 32 G .. 32 G + 31 of every token, the 16-byte chunk q of row t at
-  // position q ^ ((t / 2) % 4)), then LSE[32] and rowsum(dO O)[32] (fp32, softmax only).
+  // position q ^ ((t / 4) % 4)), then LSE[32] and rowsum(dO O)[32] (fp32, softmax only).
   constexpr int NSLOT = 3, TILE_B = BQ * D * 2, SLOT_B = 2 * TILE_B + 2 * BQ * 4;
   constexpr int DMA_OPS = PHI == 0 ? 5 : 4;  // copies per step issued by each of waves 4..7
   static_assert(BQ * D / 8 == NT, "one 16-byte chunk per thread and tensor");
@@ -128,14 +130,14 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   // 32 G .. 32 G + 31 of all 32 rows) of the Q and dO tiles, 16 rows (1 KiB) per
   // instruction; lane i takes row 16 k + i / 4 and position i % 4.
   const int nsteps = (L + BQ - 1) / BQ;
-  auto slot_off = [](int t, int cl) { return t * 32 + 8 * (cl ^ ((t >> 1) & 3)); };  // halves
+  auto slot_off = [](int t, int cl) { return t * 32 + 8 * (cl ^ ((t >> 2) & 3)); };  // halves
   auto issue = [&](int st) {
     const int tq = st * BQ, G = wave - 4;
     const uint32_t sb = lds_addr(ring) + (uint32_t)((st % NSLOT) * SLOT_B + G * 2048);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int t = 16 * k + (lane >> 2);
-      const int c = 4 * G + ((lane & 3) ^ ((t >> 1) & 3));
+      const int c = 4 * G + ((lane & 3) ^ ((t >> 2) & 3));
       const size_t off = (size_t)(seq0 + min(tq + t, L - 1)) * rs + (size_t)h * D + 8 * c;
       dma16(__builtin_amdgcn_readfirstlane(sb + 1024 * k), (const uint16_t*)a.q + off);
       dma16(__builtin_amdgcn_readfirstlane(sb + TILE_B + 1024 * k), (const uint16_t*)a.d_o + off);
@@ -257,16 +259,16 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       // dQ^T[32 w .. 32 w + 31, tokens] = K^T dS^T over all 256 context rows.
       f32x16 dq = f32x16{};
       // Row kr of K^T, columns 16 ks + 8 g .. + 7: the chunk swizzle moves them by
-      // +-32 (sign from bit 1 of ks) on rows with bit 4 set, so two base addresses plus
+      // +-64 (sign from bit 2 of ks) on rows with bit 4 set, so two base addresses plus
       // immediate offsets cover all k-steps.
       const int lxd = opaque(lr);
       const int kr = 32 * wave + kt_row(lxd);
-      const int sw = ((kr >> 4) & 1) * 32;
+      const int sw = ((kr >> 4) & 1) * 64;
       const int oa_p = kr * LDJ + 8 * g + sw, oa_m = kr * LDJ + 8 * g - sw;
       const int ob = lxd * LDJ + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < NJ / 16; ++ks)
-        dq = mfma32(lds_read8(&Kt[((ks >> 1) & 1 ? oa_m : oa_p) + 16 * ks]), lds_read8(&dSs[ob + 16 * ks]), dq);
+        dq = mfma32(lds_read8(&Kt[((ks >> 2) & 1 ? oa_m : oa_p) + 16 * ks]), lds_read8(&dSs[ob + 16 * ks]), dq);
       // Lane (t + 32 g), register r: column 32 w + 16 g + r of token t = lr.
       if (lr < rows) {
         uint16_t* dst = (uint16_t*)a.dq + (size_t)(seq0 + tq + lr) * rs + (size_t)h * D + 32 * wave + 16 * g;

@@ -29,9 +29,11 @@ __device__ __forceinline__ int vt_pos(int j) { return (j & ~12) | ((j & 4) << 1)
 // columns 16 g .. 16 g + 15 in register order: two 16-byte stores per block, and
 // the residual Q columns of the same lane are exactly its Q operand items.
 __device__ __forceinline__ int vt_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
-// V^T is stored with the 16-byte chunk q of row d at chunk q ^ (4 (d / 16 % 2)), so that
-// the 8 rows {0..3, 16..19} + 4 k read by 8 consecutive lanes fall in distinct banks.
-__device__ __forceinline__ int vt_chunk(int q, int d) { return q ^ (((d >> 4) & 1) << 2); }
+// V^T rows are 16 bytes (mod 256) apart, so row d starts at bank group d % 16 (16-byte
+// groups of the 64 4-byte banks); the 16-byte chunk q of row d is stored at chunk
+// q ^ (8 (d / 16 % 2)) so that the rows {0..3, 16..19, 4..7, 20..23} + 8 k read by one
+// 16-lane phase of a ds_read_b128 fall in distinct bank groups.
+__device__ __forceinline__ int vt_chunk(int q, int d) { return q ^ (((d >> 4) & 1) << 3); }
 
 // RESID: 0 none, 1 residual is the query tensor, 2 a separate residual tensor.
 template <int D, int NMAX, int PHI, int RESID>
