@@ -74,8 +74,9 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   static_assert(BQ * D / 8 == NT, "one 16-byte chunk per thread and tensor");
   __shared__ __align__(16) uint16_t Kt[D * LDJ];
   __shared__ __align__(16) uint8_t ring[NSLOT * SLOT_B];
-  __shared__ __align__(16) uint16_t Qt[D * LDT];
-  __shared__ __align__(16) uint16_t dOt[D * LDT];
+  __shared__ __align__(16) uint16_t QdT[2 * D * LDT];  // Q^T then dO^T (one base address)
+  uint16_t* const Qt = QdT;
+  uint16_t* const dOt = QdT + D * LDT;
   __shared__ __align__(16) uint16_t dSs[BQ * LDJ];
   static_assert(8 * 32 * LDE <= D * LDJ, "epilogue tiles must fit in Kt");
 
@@ -195,9 +196,12 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
 
     // S and dP for this wave's 32 context rows (M = tokens, N = context rows).
     f32x16 S = f32x16{}, dP = f32x16{};
+    // k-step ks reads chunk (2 ks + g) % 4 of block ks / 2: two base offsets (even and
+    // odd ks) plus immediates.
+    const int oe = slot_off(lx, gx), oo = slot_off(lx, gx + 2);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int o = (ks >> 1) * 1024 + slot_off(lx, (2 * ks + gx) & 3);
+      const int o = (ks >> 1) * 1024 + ((ks & 1) ? oo : oe);
       S = mfma32(lds_read8(&Qs[o]), kf[ks], S);
       dP = mfma32(lds_read8(&dOs[o]), vf[ks], dP);
     }

@@ -200,9 +200,10 @@ __global__ __launch_bounds__(NT_T, 1) void gemm_nt_kernel(int M, long N, int K,
 // staged tiles are k rows of 256 m (or n) values, so the MFMA operands (8 consecutive
 // k per lane) are read with ds_read_b64_tr_b16: in each 16-lane group, lane 4 r + c
 // addresses row k + r, columns c0 + 4 c .. + 3, and lane i receives column c0 + i of
-// rows k .. k + 3.  A row's 16-byte chunks are stored at positions q ^ (2 (k % 4)), so
-// the four rows and two chunks read by one group fall in distinct banks.  Rows past
-// K are clamped and their items zeroed.
+// rows k .. k + 3.  A row's 16-byte chunks are stored at positions q ^ (4 (k % 4)):
+// rows are 512 bytes apart (same bank alignment), and the 32 lanes of one read phase
+// (four rows x four chunks, 256 bytes) then cover all 64 four-byte banks once.  Rows
+// past K are clamped and their items zeroed.
 namespace {
 constexpr int TN_K = 64, TN_T = 512;
 constexpr int TN_ROW_B = 256 * 2;              // bytes per staged k row (512)
@@ -211,7 +212,7 @@ constexpr int TN_STAGE_B = 2 * TN_TILE_B;
 constexpr int TN_IPW = TN_K / 8 / 2;           // copy instructions per wave per tile (2 rows each): 4
 constexpr int TN_STORES = 16;
 constexpr int TN_CW_B = 32 * 64 * 2;
-__device__ __forceinline__ int tn_pos(int q, int k) { return q ^ (2 * (k & 3)); }
+__device__ __forceinline__ int tn_pos(int q, int k) { return q ^ (4 * (k & 3)); }
 }  // namespace
 
 __global__ __launch_bounds__(TN_T, 1) void gemm_tn_kernel(int M, long N, int K,
