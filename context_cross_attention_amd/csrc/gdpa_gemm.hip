@@ -234,10 +234,12 @@ __global__ __launch_bounds__(TN_T, 1) void gemm_tn_kernel(int M, long N, int K,
     int tile, k, m0;
     long n0;
   };
+  // Tiles sharing m (the same dK columns, the large operand) are consecutive, so the
+  // work-groups of one XCD read each dK block from HBM once and share it through L2.
   auto locate = [&](Pos& p) {
     const int t = first + min(p.tile, my_tiles - 1) * stride;
-    p.m0 = (t % mt) * 256;
-    p.n0 = (long)(t / mt) * 256;
+    p.n0 = (long)(t % nt) * 256;
+    p.m0 = (t / nt) * 256;
   };
   auto advance = [&](Pos& p) {
     if (++p.k == nk) {
