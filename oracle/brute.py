@@ -6,7 +6,8 @@ pin the vectorised oracle on tiny jagged batches (lengths including 0).
 
 Definition (Kunlun paper summary, section 2.2, GDPA bullet): for every token t of
 sample b and head h, s_j = scale * sum_e Q[t,h,e] K[b,j,h,e]; p = phi(s) over the
-sample's n rows; O[t,h,e] = sum_j p_j V[b,j,h,e].
+sample's n rows (a row softmax, or an elementwise SiLU, ReLU, GELU or identity);
+O[t,h,e] = sum_j p_j V[b,j,h,e].
 """
 from __future__ import annotations
 
@@ -49,6 +50,12 @@ def brute_forward(q, offsets, k, v, phi, scale):
                     lse[t][h] = m + math.log(z)
                 elif phi == "silu":
                     p = [x * _sigmoid(x) for x in s]
+                elif phi == "relu":
+                    p = [x if x > 0 else 0.0 for x in s]
+                elif phi == "gelu":
+                    p = [0.5 * x * (1.0 + math.erf(x / math.sqrt(2.0))) for x in s]
+                elif phi == "identity":
+                    p = list(s)
                 else:
                     raise ValueError(phi)
                 for e in range(d):

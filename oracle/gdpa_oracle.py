@@ -13,14 +13,16 @@ jagged batch with sample b owning rows offsets[b]:offsets[b+1] of Q[T,H,d] and
 per-sample K[b], V[b] of shape [n,H,d], per head h:
 
     S = scale * X Kb^T            (X = Q rows of b, head h; Kb = K[b,:,h,:])
-    P = phi(S)                    (row softmax over the n context rows, or SiLU)
+    P = phi(S)                    (row softmax over the n context rows, or elementwise)
     O = P Vb
 
 The pages give no formula for the score map, the scale, masking or the
 normalisation.  Readings taken (each listed with its reason in the design notes):
-  * phi is a row softmax over the sample's n rows, or the elementwise SiLU
-    s*sigmoid(s), which is the FFN form silu(x K^T) V;
-  * scale defaults to 1/sqrt(d) for softmax and 1.0 for SiLU;
+  * phi is a row softmax over the sample's n rows, or an elementwise map: SiLU
+    s*sigmoid(s) (the FFN form silu(x K^T) V), ReLU max(s, 0) (derivative 0 at
+    s = 0), GELU s*Phi(s) with Phi the standard normal CDF (the exact erf form),
+    or the identity (then GDPA is the bilinear map (x K^T) V);
+  * scale defaults to 1/sqrt(d) for softmax and 1.0 for the elementwise maps;
   * no mask: each token sees all n rows of its own sample and nothing else;
   * d_v = d_qk = d, K and V are distinct per head;
   * no FFN bias.
@@ -34,8 +36,9 @@ import math
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
+from scipy.special import erf as _erf
 
-PHIS = ("softmax", "silu")
+PHIS = ("softmax", "silu", "relu", "gelu", "identity")
 
 
 def as_f64(x) -> np.ndarray:
@@ -52,10 +55,11 @@ def as_f64(x) -> np.ndarray:
 
 
 def default_scale(phi: str, d: int) -> float:
-    """1/sqrt(d) for softmax (standard attention), 1.0 for SiLU (the plain FFN form)."""
+    """1/sqrt(d) for softmax (standard attention), 1.0 for the elementwise maps (the plain
+    FFN form)."""
     if phi == "softmax":
         return 1.0 / math.sqrt(d)
-    if phi == "silu":
+    if phi in PHIS:
         return 1.0
     raise ValueError(f"phi must be one of {PHIS}, got {phi!r}")
 
@@ -81,6 +85,40 @@ def silu_grad(s: np.ndarray) -> np.ndarray:
     return g * (1.0 + s * (1.0 - g))
 
 
+def relu(s: np.ndarray) -> np.ndarray:
+    """max(s, 0)."""
+    return np.maximum(s, 0.0)
+
+
+def relu_grad(s: np.ndarray) -> np.ndarray:
+    """1 for s > 0, else 0 (the subgradient 0 is taken at s = 0)."""
+    return (s > 0).astype(np.float64)
+
+
+def normal_cdf(s: np.ndarray) -> np.ndarray:
+    """Phi(s) = (1 + erf(s / sqrt 2)) / 2."""
+    return 0.5 * (1.0 + _erf(s / math.sqrt(2.0)))
+
+
+def gelu(s: np.ndarray) -> np.ndarray:
+    """GELU(s) = s Phi(s) (the exact form, not the tanh approximation)."""
+    return s * normal_cdf(s)
+
+
+def gelu_grad(s: np.ndarray) -> np.ndarray:
+    """d/ds [s Phi(s)] = Phi(s) + s exp(-s^2 / 2) / sqrt(2 pi)."""
+    return normal_cdf(s) + s * np.exp(-0.5 * s * s) / math.sqrt(2.0 * math.pi)
+
+
+# Elementwise score maps: (value, derivative), looked up by name at call time.
+ELEMENTWISE = {
+    "silu": (lambda s: silu(s), lambda s: silu_grad(s)),
+    "relu": (lambda s: relu(s), lambda s: relu_grad(s)),
+    "gelu": (lambda s: gelu(s), lambda s: gelu_grad(s)),
+    "identity": (lambda s: s, lambda s: np.ones_like(s)),
+}
+
+
 def row_softmax(s: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """Softmax over the last axis and its log-sum-exp (natural log)."""
     m = s.max(axis=-1, keepdims=True)
@@ -103,8 +141,8 @@ def gdpa_forward_bh(x: np.ndarray, kb: np.ndarray, vb: np.ndarray, phi: str,
     if phi == "softmax":
         p, lse = row_softmax(s)
         return p @ vb, lse
-    if phi == "silu":
-        return silu(s) @ vb, None
+    if phi in ELEMENTWISE:
+        return ELEMENTWISE[phi][0](s) @ vb, None
     raise ValueError(phi)
 
 
@@ -114,7 +152,7 @@ def gdpa_backward_bh(x: np.ndarray, kb: np.ndarray, vb: np.ndarray, do: np.ndarr
 
     Chain rule through O = P V, P = phi(S), S = scale x kb^T:
       dV = P^T dO;  dP = dO V^T;
-      softmax: dS = P * (dP - rowsum(dO * O));  SiLU: dS = dP * silu'(S);
+      softmax: dS = P * (dP - rowsum(dO * O));  elementwise: dS = dP * phi'(S);
       dX = scale dS kb;  dK = scale dS^T x.
     """
     s = scale * (x @ kb.T)
@@ -124,9 +162,10 @@ def gdpa_backward_bh(x: np.ndarray, kb: np.ndarray, vb: np.ndarray, do: np.ndarr
         o = p @ vb
         dvec = (do * o).sum(axis=-1, keepdims=True)
         ds = p * (dp - dvec)
-    elif phi == "silu":
-        p = silu(s)
-        ds = dp * silu_grad(s)
+    elif phi in ELEMENTWISE:
+        f, fg = ELEMENTWISE[phi]
+        p = f(s)
+        ds = dp * fg(s)
     else:
         raise ValueError(phi)
     dv = p.T @ do

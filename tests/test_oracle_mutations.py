@@ -58,6 +58,20 @@ def test_mutant_silu_grad_is_caught(monkeypatch):
     assert _torch_pin("silu") > 1e-3
 
 
+def test_mutant_gelu_grad_is_caught(monkeypatch):
+    monkeypatch.setattr(orc, "gelu_grad", lambda s: orc.normal_cdf(s))  # density term dropped
+    assert fd_check("gelu", None) > 1e-3
+    assert _torch_pin("gelu") > 1e-3
+
+
+def test_mutant_relu_is_caught(monkeypatch):
+    monkeypatch.setattr(orc, "relu", lambda s: np.abs(s))  # |s| instead of max(s, 0)
+    off, q, k, v = rand_problem(4, (4, 2), H=1, d=4, n=3, sharp=True)
+    o, _ = orc.gdpa_forward(q, off, k, v, "relu", 0.5)
+    ob, _ = brute_forward(q.tolist(), off.tolist(), k.tolist(), v.tolist(), "relu", 0.5)
+    assert rel_err(o, np.array(ob)) > 1e-3
+
+
 def test_mutant_softmax_axis_is_caught(monkeypatch):
     off, q, k, v = rand_problem(3, (4, 2), H=1, d=4, n=3, sharp=True)
     monkeypatch.setattr(orc, "row_softmax", _wrong_softmax)

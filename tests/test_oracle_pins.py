@@ -2,7 +2,7 @@
 
 Each check ties the oracle to something independent: a scalar brute force, a
 library routine the definition reduces to (torch's scaled-dot-product attention,
-torch's SiLU and linear layers, torch autograd), a closed form, an algebraic
+torch's SiLU / ReLU / GELU and linear layers, torch autograd), a closed form, an algebraic
 invariant or central finite differences.  GDPA definition: Kunlun paper summary,
 section 2.2 (GDPA bullet) and Telegram review, layer steps 1-2.
 """
@@ -41,7 +41,11 @@ def rel_err(a, b):
 # Brute force on tiny inputs
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("phi", ["softmax", "silu"])
+ALL_PHIS = ["softmax", "silu", "relu", "gelu", "identity"]
+TORCH_ACT = {"silu": F.silu, "relu": F.relu, "gelu": F.gelu, "identity": lambda x: x}
+
+
+@pytest.mark.parametrize("phi", ALL_PHIS)
 @pytest.mark.parametrize("scale", [0.5, 1.0])
 @pytest.mark.parametrize("lengths", [(3,), (2, 0, 5), (0, 1, 4), (5, 5, 1)])
 def test_brute_force_tiny(phi, scale, lengths):
@@ -58,11 +62,62 @@ def test_brute_force_tiny(phi, scale, lengths):
 # SiLU form: the per-sample two-layer FFN silu(x K^T) V
 # ---------------------------------------------------------------------------
 
-def ffn_torch(x, kb, vb, scale=1.0):
-    """Two bias-free linear layers with SiLU between, in torch fp64."""
+def ffn_torch(x, kb, vb, scale=1.0, act=F.silu):
+    """Two bias-free linear layers with an activation between, in torch fp64."""
     x, kb, vb = (torch.from_numpy(a) for a in (x, kb, vb))
-    hid = F.silu(F.linear(x, kb) * scale)
+    hid = act(F.linear(x, kb) * scale)
     return F.linear(hid, vb.T.contiguous()).numpy()
+
+
+@pytest.mark.parametrize("phi", ["relu", "gelu"])
+def test_elementwise_equals_two_layer_ffn(phi):
+    # torch's relu and (exact, erf-form) gelu between two bias-free linear layers.
+    off, q, k, v = rand_problem(31, (7, 0, 13, 4), H=3, d=8, n=6, sharp=True)
+    for scale in (1.0, 0.6):
+        o, lse = orc.gdpa_forward(q, off, k, v, phi, scale)
+        assert lse is None
+        for b in range(4):
+            for h in range(3):
+                r = slice(off[b], off[b + 1])
+                ref = ffn_torch(q[r, h, :], k[b, :, h, :], v[b, :, h, :], scale, TORCH_ACT[phi])
+                assert rel_err(o[r, h, :], ref) <= 1e-13
+
+
+def test_identity_is_bilinear():
+    # phi = identity: O = scale (X K^T) V = scale X (K^T V) (associativity), linear in X.
+    off, q, k, v = rand_problem(32, (6, 0, 3), H=2, d=5, n=4, sharp=True)
+    o, _ = orc.gdpa_forward(q, off, k, v, "identity", 0.7)
+    for b in range(3):
+        for h in range(2):
+            r = slice(off[b], off[b + 1])
+            ref = 0.7 * (q[r, h, :] @ (k[b, :, h, :].T @ v[b, :, h, :]))
+            if ref.size:
+                assert np.abs(o[r, h, :] - ref).max() <= 1e-13 * max(1.0, np.abs(ref).max())
+    o2, _ = orc.gdpa_forward(2.5 * q, off, k, v, "identity", 0.7)
+    assert rel_err(o2, 2.5 * o) <= 1e-14
+
+
+def test_relu_gelu_special_cases():
+    rng = np.random.default_rng(33)
+    d = 5
+    x = rng.standard_normal((6, d))
+    eye = np.eye(d)
+    vb = rng.standard_normal((d, 3))
+    # K = I: O = phi(X) V with torch's own activations.
+    for phi in ("relu", "gelu"):
+        o, _ = orc.gdpa_forward_bh(x, eye, vb, phi, 1.0)
+        ref = TORCH_ACT[phi](torch.from_numpy(x)).numpy() @ vb
+        assert rel_err(o, ref) <= 1e-14
+    # GELU: Phi(s) + Phi(-s) = 1, so gelu(s) - gelu(-s) = s.
+    s = np.linspace(-6.0, 6.0, 241)
+    assert np.abs(orc.gelu(s) - orc.gelu(-s) - s).max() <= 1e-14
+    assert orc.gelu(np.array([0.0]))[0] == 0.0
+    # ReLU is positively homogeneous: a scale c > 0 scales the output.
+    kb = rng.standard_normal((4, d))
+    vb4 = rng.standard_normal((4, d))
+    o1, _ = orc.gdpa_forward_bh(x, kb, vb4, "relu", 0.5)
+    o2, _ = orc.gdpa_forward_bh(x, kb, vb4, "relu", 1.5)
+    assert rel_err(o2, 3.0 * o1) <= 1e-14
 
 
 def test_silu_equals_two_layer_ffn():
@@ -228,14 +283,14 @@ def fd_check(phi, scale, seed=7, h=1e-6):
     return worst
 
 
-@pytest.mark.parametrize("phi", ["softmax", "silu"])
+@pytest.mark.parametrize("phi", ALL_PHIS)
 @pytest.mark.parametrize("scale", [None, 0.6])
 def test_backward_finite_differences(phi, scale):
     assert fd_check(phi, scale) <= 1e-6
 
 
 def torch_grads(q, off, k, v, g, phi, scale):
-    """Autograd of the jagged op built from torch library ops (SDPA / linear + SiLU)."""
+    """Autograd of the jagged op built from torch library ops (SDPA / matmul + activation)."""
     qt = torch.from_numpy(q.copy()).requires_grad_()
     kt = torch.from_numpy(k.copy()).requires_grad_()
     vt = torch.from_numpy(v.copy()).requires_grad_()
@@ -248,14 +303,14 @@ def torch_grads(q, off, k, v, g, phi, scale):
         if phi == "softmax":
             ob = F.scaled_dot_product_attention(xb, kb, vb, scale=scale)
         else:
-            ob = F.silu(torch.matmul(xb, kb.transpose(1, 2)) * scale) @ vb
+            ob = TORCH_ACT[phi](torch.matmul(xb, kb.transpose(1, 2)) * scale) @ vb
         outs.append(ob.transpose(0, 1))
     o = torch.cat(outs, 0)
     (o * torch.from_numpy(g)).sum().backward()
     return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
 
 
-@pytest.mark.parametrize("phi", ["softmax", "silu"])
+@pytest.mark.parametrize("phi", ALL_PHIS)
 def test_backward_matches_torch_autograd(phi):
     lengths = (5, 0, 17, 1, 9)
     off, q, k, v = rand_problem(8, lengths, H=3, d=8, n=6, sharp=True)
@@ -301,7 +356,7 @@ def test_silu_backward_linear_in_v_and_do():
 # Jagged-batch semantics
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("phi", ["softmax", "silu"])
+@pytest.mark.parametrize("phi", ALL_PHIS)
 def test_jagged_equals_independent_samples(phi):
     lengths = (4, 0, 9, 1)
     off, q, k, v = rand_problem(16, lengths, H=2, d=4, n=3, sharp=True)
