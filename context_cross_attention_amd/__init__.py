@@ -20,7 +20,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdpa.so")
 
-PHI = {"softmax": 0, "silu": 1}
+PHI = {"softmax": 0, "silu": 1, "relu": 2, "gelu": 3, "identity": 4}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}
 FWD_RESIDUAL = 0x1
 BWD_ACCUM_DQ = 0x2
@@ -99,7 +99,7 @@ def _stream():
 
 
 def default_scale(phi: str, d: int) -> float:
-    """1/sqrt(d) for softmax, 1 for SiLU (the plain FFN form)."""
+    """1/sqrt(d) for softmax, 1 for the elementwise maps (the plain FFN form)."""
     return 1.0 / math.sqrt(d) if phi == "softmax" else 1.0
 
 
@@ -182,7 +182,7 @@ def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """GDPA backward of sum(O * dO).  Returns (dq, dk, dv).
 
-    For softmax, o and lse are the forward's outputs; for SiLU they are unused.
+    For softmax, o and lse are the forward's outputs; for the elementwise maps they are unused.
     With accumulate_dq, dq (which may be `do` itself) receives dq + dQ.
     With residual, dq receives do + dQ: the gradient of O = Q + GDPA(Q).
     """

@@ -11,6 +11,11 @@
 
 namespace {
 
+static_assert(GDPA_PHI_SOFTMAX == gdpa::kPhiSoftmax && GDPA_PHI_SILU == gdpa::kPhiSilu &&
+                  GDPA_PHI_RELU == gdpa::kPhiRelu && GDPA_PHI_GELU == gdpa::kPhiGelu &&
+                  GDPA_PHI_IDENTITY == gdpa::kPhiIdentity,
+              "ABI score-map values are the kernels' template parameters");
+
 thread_local int g_last_hip_error = 0;
 
 constexpr size_t kAlign = 256;
@@ -27,7 +32,7 @@ gdpa_status check_problem(const gdpa_problem* p) {
   if (p->batch < 1 || p->total_tokens < 0 || p->max_seqlen < 0 || p->n_kv < 1 || p->heads < 1 ||
       p->head_dim < 1)
     return GDPA_ERR_INVALID_ARGUMENT;
-  if (p->phi != GDPA_PHI_SOFTMAX && p->phi != GDPA_PHI_SILU) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->phi < GDPA_PHI_SOFTMAX || p->phi > GDPA_PHI_IDENTITY) return GDPA_ERR_INVALID_ARGUMENT;
   if (p->dtype != GDPA_F32 && p->dtype != GDPA_BF16) return GDPA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(p->scale)) return GDPA_ERR_INVALID_ARGUMENT;
   // Element counts index with 32-bit token and row numbers and 64-bit offsets.

@@ -8,7 +8,7 @@
 // time.  So dK and dV are reduced per sample without atomics.  Per 32-row query
 // tile (Q and dO staged in LDS, row-major):
 //   S  = Q K^T,  dP = dO V^T      (M = tokens, N = the wave's context rows)
-//   P  = phi(S); dS = softmax: P (dP - rowsum(dO O)),  SiLU: dP silu'(S)
+//   P  = phi(S); dS = softmax: P (dP - rowsum(dO O)),  elementwise maps: dP phi'(S)
 //   dV += P^T dO, dK += scale dS^T Q   (A = P^T / dS^T straight from the C tile,
 //                                       B = dO / Q columns via LDS transpose reads)
 //   dQ  = scale dS K over all the work-group's context rows: dS^T goes to LDS and
@@ -173,10 +173,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
         p = fast_exp2(S[r] * sl2 - lse_s[t]);
         ds = p * (dP[r] - dvec_s[t]);
       } else {
-        const float s = S[r] * a.scale;
-        const float sg = fast_sigmoid(s);
-        p = s * sg;
-        ds = dP[r] * sg * (1.0f + s * (1.0f - sg));
+        float gr;
+        p = phi_value_grad<PHI>(S[r] * a.scale, gr);
+        ds = dP[r] * gr;
       }
       if (!jvalid) {
         p = 0.f;
@@ -271,10 +270,20 @@ __device__ __forceinline__ void f32_ds(float s_raw, float dp, float scale, float
   if (PHI == 0) {
     p = expf(s - lse);
     ds = p * (dp - dvec);
-  } else {
+  } else if (PHI == kPhiSilu) {
     const float sg = 1.0f / (1.0f + expf(-s));
     p = s * sg;
     ds = dp * sg * (1.0f + s * (1.0f - sg));
+  } else if (PHI == kPhiRelu) {
+    p = fmaxf(s, 0.f);
+    ds = s > 0.f ? dp : 0.f;
+  } else if (PHI == kPhiGelu) {
+    const float cdf = 0.5f * (1.0f + erff(s * 0.70710678118654752f));
+    p = s * cdf;
+    ds = dp * (cdf + s * expf(-0.5f * s * s) * 0.39894228040143268f);
+  } else {
+    p = s;
+    ds = dp;
   }
 }
 
@@ -383,9 +392,10 @@ static hipError_t bwd_bf16_dw(const BwdArgs& a, int phi, hipStream_t s) {
   const long items = (long)a.B * a.H * a.n_chunks;
   if (items == 0) return hipSuccess;
   const dim3 g((unsigned)items), blk(NW * 64);
-  if (phi == 0) hipLaunchKernelGGL((bwd_bf16_kernel<D, 0, NW>), g, blk, 0, s, a);
-  else hipLaunchKernelGGL((bwd_bf16_kernel<D, 1, NW>), g, blk, 0, s, a);
-  return hipGetLastError();
+  return dispatch_phi(phi, [&](auto P) {
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, decltype(P)::value, NW>), g, blk, 0, s, a);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, hipStream_t s) {
@@ -404,15 +414,18 @@ static hipError_t bwd_f32_d(const BwdArgs& a, int phi, hipStream_t s) {
   // dK/dV first: the dQ buffer may be the dO buffer itself.
   if (nkv > 0) {
     const dim3 g((unsigned)((nkv + 127) / 128)), blk(128);
-    if (phi == 0) hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, 0>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, 1>), g, blk, 0, s, a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = dispatch_phi(phi, [&](auto P) {
+      hipLaunchKernelGGL((bwd_f32_dkdv_kernel<D, decltype(P)::value>), g, blk, 0, s, a);
+      return hipGetLastError();
+    });
     if (e != hipSuccess) return e;
   }
   if (nq > 0) {
     const dim3 g((unsigned)((nq + 127) / 128)), blk(128);
-    if (phi == 0) hipLaunchKernelGGL((bwd_f32_dq_kernel<D, 0>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((bwd_f32_dq_kernel<D, 1>), g, blk, 0, s, a);
+    return dispatch_phi(phi, [&](auto P) {
+      hipLaunchKernelGGL((bwd_f32_dq_kernel<D, decltype(P)::value>), g, blk, 0, s, a);
+      return hipGetLastError();
+    });
   }
   return hipGetLastError();
 }

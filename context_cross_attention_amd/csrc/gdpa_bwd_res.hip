@@ -221,7 +221,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
           dP[r] = p * (dP[r] - dvv[c]);
         }
       }
-    } else {
+    } else if (PHI == kPhiSilu) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float sg = fast_rcp(1.0f + fast_exp2(S[r] * c1));
@@ -229,6 +229,13 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
         const float p = sv * sg;
         S[r] = p;
         dP[r] = dP[r] * fmaf(sv - p, sg, sg);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float gr;
+        S[r] = phi_value_grad<PHI>(S[r] * scale, gr);
+        dP[r] *= gr;
       }
     }
     bf16x8 pa[2], sa[2];
@@ -330,14 +337,13 @@ hipError_t launch_bwd_res(const BwdArgs& a, int phi, hipStream_t s) {
   if (items == 0) return hipSuccess;
   const dim3 g((unsigned)items), blk(512);
   const int mode = a.dq_base == nullptr ? 0 : (a.dq_base == a.d_o ? 1 : 2);
-#define GDPA_BWD_RES(P, M) hipLaunchKernelGGL((bwd_res_kernel<P, M>), g, blk, 0, s, a)
-  if (phi == 0) {
-    if (mode == 0) GDPA_BWD_RES(0, 0); else if (mode == 1) GDPA_BWD_RES(0, 1); else GDPA_BWD_RES(0, 2);
-  } else {
-    if (mode == 0) GDPA_BWD_RES(1, 0); else if (mode == 1) GDPA_BWD_RES(1, 1); else GDPA_BWD_RES(1, 2);
-  }
-#undef GDPA_BWD_RES
-  return hipGetLastError();
+  return dispatch_phi(phi, [&](auto P) {
+    constexpr int PH = decltype(P)::value;
+    if (mode == 0) hipLaunchKernelGGL((bwd_res_kernel<PH, 0>), g, blk, 0, s, a);
+    else if (mode == 1) hipLaunchKernelGGL((bwd_res_kernel<PH, 1>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_res_kernel<PH, 2>), g, blk, 0, s, a);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace gdpa

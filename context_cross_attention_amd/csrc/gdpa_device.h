@@ -88,6 +88,57 @@ __device__ __forceinline__ float fast_sigmoid(float s) {
 
 __device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
 
+// Standard normal CDF Phi(s) and the density factor exp(-s^2 / 2), through
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2), t = 1 / (1 + p x), x >= 0
+// (Abramowitz and Stegun, Handbook of Mathematical Functions, formula 7.1.26;
+// |error| <= 1.5e-7), with x = |s| / sqrt(2).
+__device__ __forceinline__ float normal_cdf(float s, float& gauss) {
+  const float x = fabsf(s) * 0.70710678118654752f;
+  const float t = fast_rcp(fmaf(0.3275911f, x, 1.0f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f),
+               0.254829592f);
+  gauss = fast_exp2(-0.72134752044448170f * s * s);  // exp(-s^2 / 2)
+  const float tail = 0.5f * poly * gauss;             // (1 - erf(x)) / 2
+  return s >= 0.f ? 1.0f - tail : tail;
+}
+
+// Elementwise score maps (phi = 1 .. 4 of gdpa_launch.h): value, and value with its
+// derivative.  SiLU s sigmoid(s); ReLU max(s, 0) (derivative 0 at s = 0); GELU
+// s Phi(s) (the exact, erf form); identity.  Each maps 0 to 0, so zero-padded
+// context rows contribute nothing.
+template <int PHI>
+__device__ __forceinline__ float phi_value(float s) {
+  if (PHI == 1) return s * fast_sigmoid(s);
+  if (PHI == 2) return fmaxf(s, 0.f);
+  if (PHI == 3) {
+    float gauss;
+    return s * normal_cdf(s, gauss);
+  }
+  return s;
+}
+template <int PHI>
+__device__ __forceinline__ float phi_value_grad(float s, float& grad) {
+  if (PHI == 1) {
+    const float sg = fast_sigmoid(s);
+    const float p = s * sg;
+    grad = fmaf(s - p, sg, sg);  // sigmoid (1 + s (1 - sigmoid))
+    return p;
+  }
+  if (PHI == 2) {
+    grad = s > 0.f ? 1.0f : 0.0f;
+    return fmaxf(s, 0.f);
+  }
+  if (PHI == 3) {
+    float gauss;
+    const float cdf = normal_cdf(s, gauss);
+    grad = fmaf(s * gauss, 0.39894228040143268f, cdf);  // Phi(s) + s exp(-s^2/2) / sqrt(2 pi)
+    return s * cdf;
+  }
+  grad = 1.0f;
+  return s;
+}
+
 // The value of x, hidden from the optimiser: per-lane index arithmetic derived from
 // it inside a loop is recomputed there (a few VALU instructions) instead of being
 // hoisted into registers held across the loop.

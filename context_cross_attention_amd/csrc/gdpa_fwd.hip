@@ -7,7 +7,7 @@
 // through LDS in blocks of 64 context rows and shared by the 4 waves.  Per block:
 //   S^T = K Q^T       (32x32x16 bf16 MFMA; A = K rows from LDS, B = the wave's
 //                      Q rows, held in registers for the whole tile)
-//   P   = phi(S)      (in registers: online softmax in base 2, or SiLU)
+//   P   = phi(S)      (in registers: online softmax in base 2, or an elementwise map)
 //   O^T += V^T P^T    (A = V columns via LDS transpose reads, B = P straight
 //                      from the C layout of S^T, rounded to bf16)
 // Computing S^T rather than S puts one query row per lane, so the softmax row
@@ -140,14 +140,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
         }
       m_run = m_new;
     } else {
-      // SiLU; rows past n are zero in K and V, and silu(0) = 0.
+      // Elementwise maps; rows past n are zero in K and V, and phi(0) = 0.
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float s = S[mt][r] * a.scale;
-          S[mt][r] = s * fast_sigmoid(s);
-        }
+        for (int r = 0; r < 16; ++r) S[mt][r] = phi_value<PHI>(S[mt][r] * a.scale);
     }
 
 #pragma unroll
@@ -198,7 +195,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   }
 }
 
-// fp32: one thread per (token, head), online softmax / SiLU accumulation in fp32.
+// fp32: one thread per (token, head), online softmax or elementwise-map accumulation
+// in fp32 (the device library's expf / erff).
 template <int D, int PHI, bool RESID>
 __global__ __launch_bounds__(128) void fwd_f32_kernel(const FwdArgs a) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -231,7 +229,10 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const FwdArgs a) {
       for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vj[e], acc[e] * c);
       m = m_new;
     } else {
-      const float p = s / (1.0f + expf(-s));
+      float p = s;
+      if (PHI == kPhiSilu) p = s / (1.0f + expf(-s));
+      if (PHI == kPhiRelu) p = fmaxf(s, 0.f);
+      if (PHI == kPhiGelu) p = 0.5f * s * (1.0f + erff(s * 0.70710678118654752f));
 #pragma unroll
       for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vj[e], acc[e]);
     }
@@ -254,14 +255,12 @@ int fwd_bf16_grid(int T, int B, int H) {
 template <int D>
 static hipError_t fwd_bf16_d(const FwdArgs& a, int phi, bool resid, int grid, hipStream_t s) {
   const dim3 g(grid), blk(256);
-  if (phi == 0) {
-    if (resid) hipLaunchKernelGGL((fwd_bf16_kernel<D, 0, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<D, 0, false>), g, blk, 0, s, a);
-  } else {
-    if (resid) hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, false>), g, blk, 0, s, a);
-  }
-  return hipGetLastError();
+  return dispatch_phi(phi, [&](auto P) {
+    constexpr int PH = decltype(P)::value;
+    if (resid) hipLaunchKernelGGL((fwd_bf16_kernel<D, PH, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((fwd_bf16_kernel<D, PH, false>), g, blk, 0, s, a);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int phi, bool resid, int grid, hipStream_t s) {
@@ -278,14 +277,12 @@ template <int D>
 static hipError_t fwd_f32_d(const FwdArgs& a, int phi, bool resid, hipStream_t s) {
   const long items = (long)a.T * a.H;
   const dim3 g((unsigned)((items + 127) / 128)), blk(128);
-  if (phi == 0) {
-    if (resid) hipLaunchKernelGGL((fwd_f32_kernel<D, 0, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((fwd_f32_kernel<D, 0, false>), g, blk, 0, s, a);
-  } else {
-    if (resid) hipLaunchKernelGGL((fwd_f32_kernel<D, 1, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((fwd_f32_kernel<D, 1, false>), g, blk, 0, s, a);
-  }
-  return hipGetLastError();
+  return dispatch_phi(phi, [&](auto P) {
+    constexpr int PH = decltype(P)::value;
+    if (resid) hipLaunchKernelGGL((fwd_f32_kernel<D, PH, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((fwd_f32_kernel<D, PH, false>), g, blk, 0, s, a);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, int d, int phi, bool resid, hipStream_t s) {

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
   }
   __syncthreads();
 
-  const float sl2 = a.scale * kLog2e, nsl2 = -sl2;
+  const float scl = a.scale, sl2 = scl * kLog2e, nsl2 = -sl2;
   const int nchunks = (L + 31) / 32;
   // Query rows past the sample are read from its last row (clamped, always a
   // valid address) and never stored: each lane's row is independent.  k-step ks of
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
           l_run += p;
           S[r] = p;
         }
-      } else {
+      } else if (PHI == kPhiSilu) {
         // SiLU(s) with s = scale * S: with t = -log2(e) * s, silu(s) = -ln(2) * t / (1 + 2^t).
         // The constant -ln(2) is applied once to O after the last tile.
 #pragma unroll
@@ -175,6 +175,9 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
           const float t = S[r] * nsl2;
           S[r] = t * fast_rcp(1.0f + fast_exp2(t));
         }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[r] = phi_value<PHI>(S[r] * scl);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
       if (jt + 2 < ntile) scores(32 * (jt + 2), Sa);
       mix(32 * (jt + 1), Sb);
     }
-    if (PHI == 1) {
+    if (PHI == kPhiSilu) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) O[dt] *= -kLn2;
     }
@@ -257,9 +260,10 @@ static void fwd_res_launch(const FwdArgs& a, const int32_t* order, int resid, hi
 template <int D, int NMAX>
 static hipError_t fwd_res_d(const FwdArgs& a, const int32_t* order, int phi, bool resid, hipStream_t s) {
   const int mode = !resid ? 0 : (a.residual == a.q ? 1 : 2);
-  if (phi == 0) fwd_res_launch<D, NMAX, 0>(a, order, mode, s);
-  else fwd_res_launch<D, NMAX, 1>(a, order, mode, s);
-  return hipGetLastError();
+  return dispatch_phi(phi, [&](auto P) {
+    fwd_res_launch<D, NMAX, decltype(P)::value>(a, order, mode, s);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_fwd_res(const FwdArgs& a, const int32_t* order, int d, int phi, bool resid,

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gdpa {
 
 // Forward q-tile height of the bf16 MFMA kernel (4 waves x 32 rows).
@@ -12,6 +14,25 @@ constexpr int kFwdTileRows = 128;
 constexpr int kBwdRowsPerWave = 32;
 // Largest batch the on-device longest-first ordering sorts (larger: natural order).
 constexpr int kMaxSortBatch = 4096;
+
+// Score maps (the gdpa_phi values of the C ABI).  Softmax normalises over a row;
+// the others are elementwise (their values and derivatives are in gdpa_device.h).
+constexpr int kPhiSoftmax = 0, kPhiSilu = 1, kPhiRelu = 2, kPhiGelu = 3, kPhiIdentity = 4;
+constexpr int kPhiCount = 5;
+
+// Calls f(std::integral_constant<int, phi>{}) for a run-time phi (kernel templates
+// take phi as a compile-time parameter).
+template <class F>
+inline hipError_t dispatch_phi(int phi, F&& f) {
+  switch (phi) {
+    case kPhiSoftmax: return f(std::integral_constant<int, kPhiSoftmax>{});
+    case kPhiSilu: return f(std::integral_constant<int, kPhiSilu>{});
+    case kPhiRelu: return f(std::integral_constant<int, kPhiRelu>{});
+    case kPhiGelu: return f(std::integral_constant<int, kPhiGelu>{});
+    case kPhiIdentity: return f(std::integral_constant<int, kPhiIdentity>{});
+  }
+  return hipErrorInvalidValue;
+}
 
 struct FwdArgs {
   const int32_t* offsets;     // [B+1]

@@ -27,8 +27,8 @@ class StackedGdpa:
     def __init__(self, offsets: torch.Tensor, ctx: torch.Tensor, w_k: List[torch.Tensor],
                  w_v: List[torch.Tensor], heads: int, n_kv: int, total_tokens: int,
                  phi: str = "silu", scale: Optional[float] = None):
-        if phi != "silu":
-            raise NotImplementedError("stacked layers are built for the SiLU (FFN) form")
+        if phi == "softmax":
+            raise NotImplementedError("stacked layers use an elementwise map (the FFN form)")
         dev = ctx.device
         self.offsets, self.ctx, self.w_k, self.w_v = offsets, ctx, w_k, w_v
         self.L = len(w_k)

@@ -12,15 +12,17 @@
  * For every token t of sample b and head h:
  *
  *     s_j      = scale * < Q[t,h,:], K[b,j,h,:] >          j = 0 .. n_kv-1
- *     p        = phi(s)    (row softmax over j, or SiLU elementwise)
+ *     p        = phi(s)    (row softmax over j, or an elementwise map)
  *     O[t,h,:] = sum_j p_j V[b,j,h,:]
  *
- * With phi = SiLU and scale = 1 this is the per-sample two-layer FFN
- * silu(x K^T) V.  The pages give no formula for phi, the scale, masking or
- * normalisation; the readings taken are: no mask (a token sees every context
- * row of its own sample and nothing of other samples), softmax over the n_kv
- * context rows, scale chosen by the caller (1/sqrt(d) for softmax and 1 for
- * SiLU are the usual values), d_v = d_qk = d, no bias.
+ * With an elementwise phi and scale = 1 this is the per-sample two-layer FFN
+ * phi(x K^T) V (SiLU gives the FFN form; ReLU, GELU and the identity are the
+ * other common FFN activations).  The pages give no
+ * formula for phi, the scale, masking or normalisation; the readings taken are:
+ * no mask (a token sees every context row of its own sample and nothing of other
+ * samples), softmax over the n_kv context rows, scale chosen by the caller
+ * (1/sqrt(d) for softmax and 1 for the elementwise maps are the usual values),
+ * d_v = d_qk = d, no bias.
  *
  * Conventions shared by every call:
  *   - All tensor pointers are DEVICE pointers, caller-owned; the library never
@@ -60,7 +62,18 @@ typedef enum {
   GDPA_ERR_HIP = 4                /* a HIP launch or runtime call failed */
 } gdpa_status;
 
-typedef enum { GDPA_PHI_SOFTMAX = 0, GDPA_PHI_SILU = 1 } gdpa_phi;
+/* Score maps.  SOFTMAX: row softmax over the n_kv context rows.  Elementwise:
+ * SILU s / (1 + exp(-s)); RELU max(s, 0) (derivative taken as 0 at s = 0);
+ * GELU s Phi(s) with Phi the standard normal CDF (the exact erf form; the bf16
+ * kernels evaluate erf with a rational approximation of absolute error
+ * <= 1.5e-7); IDENTITY s (GDPA is then the bilinear map (x K^T) V). */
+typedef enum {
+  GDPA_PHI_SOFTMAX = 0,
+  GDPA_PHI_SILU = 1,
+  GDPA_PHI_RELU = 2,
+  GDPA_PHI_GELU = 3,
+  GDPA_PHI_IDENTITY = 4
+} gdpa_phi;
 typedef enum { GDPA_F32 = 0, GDPA_BF16 = 1 } gdpa_dtype;
 
 /* gdpa_fwd: O = residual + GDPA(...) instead of O = GDPA(...). `residual` may alias `q`. */
@@ -93,7 +106,7 @@ size_t gdpa_workspace_bytes(const gdpa_problem* p, int backward);
 
 /* Forward.  q [T,H,d], k, v [B,n,H,d] in; o [T,H,d] out (overwritten).
  * lse [T,H] float32: log-sum-exp of each score row (natural log) - written when
- * non-NULL and phi = softmax, required by gdpa_bwd for softmax; ignored for SiLU.
+ * non-NULL and phi = softmax, required by gdpa_bwd for softmax; ignored for the elementwise maps.
  * residual [T,H,d]: added to O when GDPA_FWD_RESIDUAL is set (may alias q;
  * must not alias o unless it is the same buffer as q and o is not q). */
 gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* q,
@@ -101,10 +114,10 @@ gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* 
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward of sum(O * dO).  In: q, k, v, d_o, and for softmax also o and lse
- * from gdpa_fwd (ignored for SiLU, may be NULL).  Out: dq [T,H,d] (overwritten;
+ * from gdpa_fwd (ignored for the elementwise maps, may be NULL).  Out: dq [T,H,d] (overwritten;
  * accumulated with GDPA_BWD_ACCUM_DQ; dO added with GDPA_BWD_RESIDUAL), dk, dv
  * [B,n,H,d] (overwritten; each is
- * the sum over the sample's own tokens, zero for an empty sample).  With SiLU,
+ * the sum over the sample's own tokens, zero for an empty sample).  With an elementwise map,
  * o and lse are not read and may be NULL. */
 gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
                      const void* v, const void* o, const float* lse, const void* d_o, void* dq,

@@ -39,13 +39,16 @@ def run_case(cca, cfg, phi, seed=0, sharp=False, scale=None, check_bwd=True):
 
 
 # fp32: the small fixed-length workload and ragged variants.
-@pytest.mark.parametrize("phi", ["softmax", "silu"])
+MORE_MAPS = ["relu", "gelu", "identity"]
+
+
+@pytest.mark.parametrize("phi", ["softmax", "silu"] + MORE_MAPS)
 def test_fp32_fixed_length_workload(gdpa_lib, phi):
     run_case(gdpa_lib, gi.small_config(gi.CONFIGS[1], backward=True), phi)
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
-@pytest.mark.parametrize("phi", ["softmax", "silu"])
+@pytest.mark.parametrize("phi", ["softmax", "silu"] + MORE_MAPS)
 def test_fp32_ragged(gdpa_lib, d, phi):
     cfg = custom_config((0, 1, 37, 130), H=2, d=d, n=5, dtype="f32", phi=phi)
     run_case(gdpa_lib, cfg, phi, sharp=True)
@@ -71,6 +74,37 @@ BF16_SHAPES = [
 def test_bf16_parity(gdpa_lib, shape, phi, sharp):
     lengths, H, d, n = shape
     run_case(gdpa_lib, custom_config(lengths, H, d, n, phi=phi), phi, sharp=sharp)
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES, ids=lambda s: f"H{s[1]}d{s[2]}n{s[3]}")
+@pytest.mark.parametrize("phi", MORE_MAPS)
+def test_bf16_parity_more_maps(gdpa_lib, shape, phi):
+    # Scores of order one ("sharp" inputs), where the maps are far from linear; both the
+    # resident-context kernels (d = 128, n <= 256) and the streaming ones are covered.
+    lengths, H, d, n = shape
+    run_case(gdpa_lib, custom_config(lengths, H, d, n, phi=phi), phi, sharp=True)
+
+
+@pytest.mark.parametrize("phi", MORE_MAPS)
+def test_bf16_more_maps_residual(gdpa_lib, phi):
+    # Stacked-layer form (residual forward, residual dQ) on the resident-context kernels.
+    cca = gdpa_lib
+    cfg = custom_config((100, 0, 260, 7), H=2, d=128, n=200, phi=phi)
+    inp = gi.make_gdpa_inputs(cfg, seed=3)
+    q, off, k, v, do = device_inputs(inp)
+    say(f"case: residual {phi}")
+    o, _ = cca.fwd(q, off, k, v, phi=phi, residual=q)
+    dx = do.clone()
+    dq, dk, dv = cca.bwd(q, off, k, v, None, None, dx, phi=phi, dq=dx, residual=True)
+    torch.cuda.synchronize()
+    o_ref, _ = orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi)
+    dq_ref, dk_ref, dv_ref = orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi)
+    errs = {"o": max_abs_rel(o.cpu(), o_ref + orc.as_f64(inp.q)),
+            "dq": max_abs_rel(dq.cpu(), dq_ref + orc.as_f64(inp.do)),
+            "dk": max_abs_rel(dk.cpu(), dk_ref), "dv": max_abs_rel(dv.cpu(), dv_ref)}
+    say("  errors:", {n_: f"{e:.2e}" for n_, e in errs.items()})
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (phi, name, e)
 
 
 def test_bf16_explicit_scale(gdpa_lib):
