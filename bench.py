@@ -4,10 +4,10 @@
 Default workload: the stacked jagged workload - 4 residual GDPA layers with
 generated K/V, forward and backward, B=1024 samples with log-normal lengths
 (median 1024, max 8192, T = 1,438,675 tokens at seed 0), H=8, d=128, n_kv=256,
-context width 512, phi = SiLU.  One step runs every stage of the path: weight
-generation (K, V = C W), GDPA forward with the residual add, GDPA backward with
-dK/dV reduced per sample and dX = dX' + dQ, and the weight gradients C^T dK,
-C^T dV.
+context width 512, phi = SiLU (--phi selects another elementwise map).  One step
+runs every stage of the path: weight generation (K, V = C W), GDPA forward with
+the residual add, GDPA backward with dK/dV reduced per sample and dX = dX' + dQ,
+and the weight gradients C^T dK, C^T dV.
 
 `value` is GDPA forward+backward TFLOP/s over the whole step (algorithmic
 FLOPs 12*T*H*n*d per layer, the weight-generation time counted in the
@@ -23,7 +23,7 @@ of known size, see --calibrate-copy); it is read from the committed summary in
 profiles/ and reported only while the kernel sources still hash to the value
 recorded there.
 
-    python bench.py [--steps K] [--warmup W] [--config {2,3,4,5}] [--phi softmax|silu]
+    python bench.py [--steps K] [--warmup W] [--config {2,3,4,5}] [--phi softmax|silu|relu|gelu|identity]
     python bench.py --calibrate-copy MIB   # plain copy of MIB MiB, for counter scaling
 """
 from __future__ import annotations
@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 4, 5])
-    ap.add_argument("--phi", default=None, choices=[None, "softmax", "silu"])
+    ap.add_argument("--phi", default=None, choices=[None, "softmax", "silu", "relu", "gelu", "identity"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -175,7 +175,7 @@ def pick_samples(lengths, per_token_flops, budget_flops, cap):
     return chosen
 
 
-def cpu_baseline_stacked(inp, cfg):
+def cpu_baseline_stacked(inp, cfg, phi):
     import numpy as np
     from oracle import gdpa_oracle as orc
     per_tok = 12.0 * cfg.layers * cfg.heads * cfg.n_kv * cfg.head_dim
@@ -187,13 +187,13 @@ def cpu_baseline_stacked(inp, cfg):
     g = inp.do[rows]
     ctx = inp.ctx[samples]
     t0 = time.perf_counter()
-    xs = orc.stacked_forward(x0, sub_off, ctx, inp.w_k, inp.w_v, cfg.heads, cfg.n_kv, "silu")
-    orc.stacked_backward(xs, sub_off, ctx, inp.w_k, inp.w_v, g, cfg.heads, cfg.n_kv, "silu")
+    xs = orc.stacked_forward(x0, sub_off, ctx, inp.w_k, inp.w_v, cfg.heads, cfg.n_kv, phi)
+    orc.stacked_backward(xs, sub_off, ctx, inp.w_k, inp.w_v, g, cfg.heads, cfg.n_kv, phi)
     dt = time.perf_counter() - t0
     tokens = int(sub_off[-1])
     flops = per_tok * tokens
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"stacked {cfg.layers}-layer SiLU fwd+bwd incl. weight generation on samples "
+            "sample": f"stacked {cfg.layers}-layer {phi} fwd+bwd incl. weight generation on samples "
                       f"{samples[0]}..{samples[-1]} ({len(samples)} of {cfg.batch}, {tokens} tokens); "
                       f"GDPA FLOPs {flops / 1e9:.1f} G in {dt:.1f} s (numpy float64)",
             "seconds": round(dt, 2)}
@@ -258,7 +258,9 @@ def main():
         ctx = inp.ctx.to(dev)
         wk = [w.to(dev) for w in inp.w_k]
         wv = [w.to(dev) for w in inp.w_v]
-        model = StackedGdpa(off, ctx, wk, wv, cfg.heads, cfg.n_kv, T, phi="silu")
+        if phi == "softmax":
+            sys.exit("the stacked workload uses an elementwise score map (the FFN form)")
+        model = StackedGdpa(off, ctx, wk, wv, cfg.heads, cfg.n_kv, T, phi=phi)
 
         def step():
             model.forward(x0, marks)
@@ -338,7 +340,7 @@ def main():
     if cfg.layers:
         workload = (f"stacked GDPA {cfg.layers} layers fwd+bwd incl. weight generation: B={B} samples, "
                     f"lengths log-normal (median {cfg.lengths[1]}, max {cfg.lengths[2]}), T={T}, H={H}, "
-                    f"d={d}, n_kv={n}, ctx_dim={cfg.ctx_dim}, phi=SiLU, residual between layers")
+                    f"d={d}, n_kv={n}, ctx_dim={cfg.ctx_dim}, phi={phi}, residual between layers")
     else:
         workload = f"GDPA {'fwd+bwd' if cfg.backward else 'fwd'}: {cfg.name}, phi={phi}, T={T}"
 
@@ -366,7 +368,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        cb = cpu_baseline_stacked(inp, cfg) if cfg.layers else cpu_baseline_single(inp, cfg, phi)
+        cb = cpu_baseline_stacked(inp, cfg, phi) if cfg.layers else cpu_baseline_single(inp, cfg, phi)
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 
