@@ -64,3 +64,34 @@ def brute_forward(q, offsets, k, v, phi, scale):
                         acc += p[j] * v[b][j][h][e]
                     o[t][h][e] = acc
     return o, lse
+
+
+def brute_swa_forward(q, offsets, k, v, window, scale):
+    """Sliding-window self-attention (token i of a sample attends to its tokens j with
+    i - window < j <= i), scalar loops; q, k, v: nested lists [T][H][d].
+    Returns (O [T][H][d], lse [T][H])."""
+    T = offsets[-1]
+    H = len(q[0]) if T else 0
+    d = len(q[0][0]) if T else 0
+    o = [[[0.0] * d for _ in range(H)] for _ in range(T)]
+    lse = [[0.0] * H for _ in range(T)]
+    for b in range(len(offsets) - 1):
+        for t in range(offsets[b], offsets[b + 1]):
+            lo = max(offsets[b], t - window + 1)
+            for h in range(H):
+                s = []
+                for u in range(lo, t + 1):
+                    acc = 0.0
+                    for e in range(d):
+                        acc += q[t][h][e] * k[u][h][e]
+                    s.append(scale * acc)
+                m = max(s)
+                wts = [math.exp(x - m) for x in s]
+                z = sum(wts)
+                lse[t][h] = m + math.log(z)
+                for e in range(d):
+                    acc = 0.0
+                    for idx, u in enumerate(range(lo, t + 1)):
+                        acc += wts[idx] / z * v[u][h][e]
+                    o[t][h][e] = acc
+    return o, lse
