@@ -39,6 +39,14 @@ class GdpaProblem(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
+class SwaProblem(ctypes.Structure):
+    """Mirror of gdpa_swa_problem in include/gdpa.h."""
+    _fields_ = [("batch", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("max_seqlen", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
 class GdpaError(RuntimeError):
     def __init__(self, status: int, where: str, hip_error: int = 0):
         msg = f"{where}: {STATUS.get(status, status)}"
@@ -51,8 +59,8 @@ class GdpaError(RuntimeError):
 _lib = None
 
 EXPORTS = ("gdpa_workspace_bytes", "gdpa_fwd", "gdpa_bwd", "gdpa_weightgen_fwd",
-           "gdpa_weightgen_bwd_w", "gdpa_check_offsets", "gdpa_status_str",
-           "gdpa_last_hip_error")
+           "gdpa_weightgen_bwd_w", "gdpa_swa_workspace_bytes", "gdpa_swa_fwd", "gdpa_swa_bwd",
+           "gdpa_check_offsets", "gdpa_status_str", "gdpa_last_hip_error")
 
 
 def load(path: str = LIB_PATH):
@@ -75,6 +83,13 @@ def load(path: str = LIB_PATH):
     lib.gdpa_weightgen_fwd.restype = ctypes.c_int
     lib.gdpa_weightgen_bwd_w.argtypes = [i32, i32, i64, vp, vp, vp, vp]
     lib.gdpa_weightgen_bwd_w.restype = ctypes.c_int
+    SP = ctypes.POINTER(SwaProblem)
+    lib.gdpa_swa_workspace_bytes.argtypes = [SP, ctypes.c_int]
+    lib.gdpa_swa_workspace_bytes.restype = sz
+    lib.gdpa_swa_fwd.argtypes = [SP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_swa_fwd.restype = ctypes.c_int
+    lib.gdpa_swa_bwd.argtypes = [SP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_swa_bwd.restype = ctypes.c_int
     lib.gdpa_check_offsets.argtypes = [vp, i32, i32, i32]
     lib.gdpa_check_offsets.restype = ctypes.c_int
     lib.gdpa_status_str.argtypes = [ctypes.c_int]
@@ -220,6 +235,69 @@ def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                       _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
                       _stream())
     _check(st, "gdpa_bwd")
+    return dq, dk, dv
+
+
+def _swa_problem(q: torch.Tensor, offsets: torch.Tensor, window: int, scale: Optional[float]):
+    T, H, d = q.shape
+    if q.dtype not in DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return SwaProblem(offsets.shape[0] - 1, T, T, H, d, int(window),
+                      1.0 / math.sqrt(d) if scale is None else float(scale), DTYPE[q.dtype], 0)
+
+
+def _swa_workspace(prob: SwaProblem, backward: bool, device, workspace: Optional[torch.Tensor]):
+    need = int(load().gdpa_swa_workspace_bytes(ctypes.byref(prob), 1 if backward else 0))
+    if workspace is not None and workspace.numel() >= need:
+        return workspace
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+
+def swa_fwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int,
+            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Sliding-window self-attention forward over the jagged batch: q, k, v [T,H,d] bf16,
+    token i of a sample attends to its tokens j with i - window < j <= i.  Returns (o, lse)."""
+    lib = load()
+    T, H, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, (T, H, d), q.dtype, dev)
+    _require(offsets, "offsets", (offsets.shape[0],), torch.int32, dev)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev) if lse is None else lse
+    _require(out, "out", (T, H, d), q.dtype, dev)
+    _require(lse, "lse", (T, H), torch.float32, dev)
+    prob = _swa_problem(q, offsets, window, scale)
+    ws = _swa_workspace(prob, False, dev, workspace)
+    _check(lib.gdpa_swa_fwd(ctypes.byref(prob), _ptr(offsets), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                            _ptr(lse), _ptr(ws), ws.numel(), _stream()), "gdpa_swa_fwd")
+    return out, lse
+
+
+def swa_bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            o: torch.Tensor, lse: torch.Tensor, do: torch.Tensor, window: int,
+            scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+            dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None):
+    """Sliding-window self-attention backward of sum(O * dO).  Returns (dq, dk, dv)."""
+    lib = load()
+    T, H, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _require(t, name, (T, H, d), q.dtype, dev)
+    _require(lse, "lse", (T, H), torch.float32, dev)
+    _require(offsets, "offsets", (offsets.shape[0],), torch.int32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _require(t, name, (T, H, d), q.dtype, dev)
+    prob = _swa_problem(q, offsets, window, scale)
+    ws = _swa_workspace(prob, True, dev, workspace)
+    _check(lib.gdpa_swa_bwd(ctypes.byref(prob), _ptr(offsets), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                            _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                            _stream()), "gdpa_swa_bwd")
     return dq, dk, dv
 
 

@@ -226,6 +226,143 @@ gdpa_status gdpa_weightgen_bwd_w(int32_t batch, int32_t ctx_dim, int64_t cols, c
                                            (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+gdpa_status check_swa(const gdpa_swa_problem* p) {
+  if (p == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->batch < 1 || p->total_tokens < 0 || p->max_seqlen < 0 || p->heads < 1 || p->head_dim < 1 ||
+      p->window < 1)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->dtype != GDPA_F32 && p->dtype != GDPA_BF16) return GDPA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->scale)) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)p->total_tokens * p->heads > INT32_MAX) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) return GDPA_ERR_UNSUPPORTED;
+  if (p->dtype != GDPA_BF16 || p->flags != 0) return GDPA_ERR_UNSUPPORTED;
+  return GDPA_OK;
+}
+
+struct SwaBwdPlan {
+  int waves, max_chunks;
+  size_t chunk_off, dvec_off, acc_off, total;
+};
+
+SwaBwdPlan swa_bwd_plan(const gdpa_swa_problem* p) {
+  SwaBwdPlan pl{};
+  pl.waves = gdpa::swa_bwd_waves(p->head_dim);
+  const int nj = 32 * pl.waves;
+  // sum_b ceil(L_b / nj) <= T / nj + B
+  pl.max_chunks = p->total_tokens / nj + p->batch;
+  const size_t TH = (size_t)p->total_tokens * p->heads;
+  size_t off = 0;
+  pl.chunk_off = off;
+  off += align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
+  pl.dvec_off = off;
+  off += align_up(sizeof(float) * TH);
+  pl.acc_off = off;
+  off += align_up(sizeof(float) * TH * p->head_dim);
+  pl.total = off;
+  return pl;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdpa_swa_workspace_bytes(const gdpa_swa_problem* p, int backward) {
+  if (check_swa(p) != GDPA_OK) return 0;
+  return backward ? swa_bwd_plan(p).total : align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
+}
+
+gdpa_status gdpa_swa_fwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* q,
+                         const void* k, const void* v, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const gdpa_status st = check_swa(p);
+  if (st != GDPA_OK) return st;
+  if (offsets == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->total_tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (o != nullptr && (o == q || o == k || o == v)) return GDPA_ERR_INVALID_ARGUMENT;
+  if (workspace == nullptr || workspace_bytes < gdpa_swa_workspace_bytes(p, 0))
+    return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  if (p->total_tokens == 0) return GDPA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  gdpa::FwdArgs a{};
+  a.offsets = offsets;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = p->batch;
+  a.T = p->total_tokens;
+  a.H = p->heads;
+  a.scale = p->scale;
+  a.window = p->window;
+  int32_t* tile_start = (int32_t*)workspace;
+  hipError_t e = gdpa::launch_tile_scan(offsets, p->batch, gdpa::kFwdTileRows, tile_start, s);
+  if (e != hipSuccess) return hip_status(e);
+  a.tile_start = tile_start;
+  const int grid = gdpa::fwd_bf16_grid(p->total_tokens, p->batch, p->heads);
+  return hip_status(gdpa::launch_fwd_swa(a, p->head_dim, grid, s));
+}
+
+gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* q,
+                         const void* k, const void* v, const void* o, const float* lse,
+                         const void* d_o, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const gdpa_status st = check_swa(p);
+  if (st != GDPA_OK) return st;
+  if (offsets == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->total_tokens > 0 &&
+      (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
+       d_o == nullptr || dq == nullptr || dk == nullptr || dv == nullptr))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  const void* outs[3] = {dq, dk, dv};
+  const void* ins[5] = {q, k, v, o, d_o};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (outs[i] != nullptr && outs[i] == ins[j]) return GDPA_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 3; ++j)
+      if (outs[i] != nullptr && outs[i] == outs[j]) return GDPA_ERR_INVALID_ARGUMENT;
+  }
+  const SwaBwdPlan pl = swa_bwd_plan(p);
+  if (workspace == nullptr || workspace_bytes < pl.total) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  if (p->total_tokens == 0) return GDPA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  gdpa::BwdArgs a{};
+  a.offsets = offsets;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.d_o = d_o;
+  a.lse = lse;
+  a.dvec = (const float*)(ws + pl.dvec_off);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dq_acc = (float*)(ws + pl.acc_off);
+  a.B = p->batch;
+  a.T = p->total_tokens;
+  a.H = p->heads;
+  a.n_chunks = 0;
+  a.scale = p->scale;
+  a.chunk_start = (const int32_t*)(ws + pl.chunk_off);
+  a.window = p->window;
+  const size_t TH = (size_t)p->total_tokens * p->heads;
+  hipError_t e = gdpa::launch_softmax_dvec(o, d_o, (int)TH, p->head_dim, true, (float*)(ws + pl.dvec_off), s);
+  if (e != hipSuccess) return hip_status(e);
+  e = gdpa::launch_tile_scan(offsets, p->batch, 32 * pl.waves, (int32_t*)(ws + pl.chunk_off), s);
+  if (e != hipSuccess) return hip_status(e);
+  e = gdpa::launch_zero_f32(a.dq_acc, TH * p->head_dim, s);
+  if (e != hipSuccess) return hip_status(e);
+  e = gdpa::launch_bwd_swa(a, p->head_dim, pl.max_chunks, s);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(gdpa::launch_dq_finalize(a.dq_acc, nullptr, dq, TH * p->head_dim, s));
+}
+
 gdpa_status gdpa_check_offsets(const int32_t* host_offsets, int32_t batch, int32_t total_tokens,
                                int32_t max_seqlen) {
   if (host_offsets == nullptr || batch < 1 || total_tokens < 0 || max_seqlen < 0)

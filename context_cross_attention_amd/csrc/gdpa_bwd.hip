@@ -29,7 +29,12 @@ namespace gdpa {
 // tokens 0..3 go to even rows and 4..7 to odd rows.
 __device__ __forceinline__ int qpos(int t) { return (t & ~7) | ((t & 3) << 1) | ((t >> 2) & 1); }
 
-template <int D, int PHI, int NW>
+// SW: sliding-window self-attention (Kunlun paper summary, section 2.2, Sliding
+// Window Attention bullet).  The work-group's key rows are a chunk of its sample's
+// own tokens, only the query steps whose windows reach them are visited, pairs
+// outside i - window < j <= i get P = dS = 0, and dQ always goes through the fp32
+// accumulator (several chunks feed each query row).
+template <int D, int PHI, int NW, bool SW = false>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   constexpr int NJ = 32 * NW;          // context rows per work-group
   constexpr int BQ = kBwdRowsPerWave;  // query rows per step
@@ -51,19 +56,31 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   __shared__ __align__(16) uint16_t dSt[NJ * LDT];
   __shared__ float lse_s[BQ], dvec_s[BQ];
 
-  const int H = a.H, n = a.n, nch = a.n_chunks;
+  const int H = a.H, nch = a.n_chunks;
   const int item = blockIdx.x;
-  const int rank = item / (H * nch);
-  const int rem = item - rank * H * nch;
-  const int h = rem / nch, jc = rem - h * nch;
-  const int b = a.order[rank];
+  int b, h, jc;
+  if (SW) {
+    const int c = item / H;  // the grid is an upper bound on the number of chunks
+    if (c >= a.chunk_start[a.B]) return;
+    h = item - c * H;
+    b = find_sample(a.chunk_start, a.B, c);
+    jc = c - a.chunk_start[b];
+  } else {
+    const int rank = item / (H * nch);
+    const int rem = item - rank * H * nch;
+    h = rem / nch;
+    jc = rem - h * nch;
+    b = a.order[rank];
+  }
   const int seq0 = a.offsets[b], L = a.offsets[b + 1] - seq0;
+  const int n = SW ? L : a.n;  // key rows of this sample
   const int j0 = jc * NJ;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const size_t rs = (size_t)H * D;
-  const uint16_t* Kg = (const uint16_t*)a.k + ((size_t)b * n * H + h) * D;
-  const uint16_t* Vg = (const uint16_t*)a.v + ((size_t)b * n * H + h) * D;
+  const size_t kv0 = SW ? (size_t)seq0 * H : (size_t)b * n * H;
+  const uint16_t* Kg = (const uint16_t*)a.k + (kv0 + h) * D;
+  const uint16_t* Vg = (const uint16_t*)a.v + (kv0 + h) * D;
 
   // K chunk, row-major, into LDS (zero rows past n); loads first, then writes.
   {
@@ -132,9 +149,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
       dvec_next = ok ? a.dvec[r] : 0.f;
     }
   };
-  if (L > 0) load_step(0);
+  // Query steps: every token, or (SW) the tokens whose windows reach key rows
+  // j0 .. j0 + NJ - 1, i.e. j0 .. j0 + NJ + window - 2.
+  const int tq_beg = SW ? min(j0, L) : 0;
+  const int tq_end = SW ? min(L, j0 + NJ - 1 + a.window) : L;
+  if (tq_beg < tq_end) load_step(tq_beg);
 
-  for (int tq = 0; tq < L; tq += BQ) {
+  for (int tq = tq_beg; tq < tq_end; tq += BQ) {
     const int rows = min(BQ, L - tq);
     __syncthreads();  // previous step is done with Qs, dOs, dSt
 #pragma unroll
@@ -150,7 +171,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
       dvec_s[tid] = dvec_next;
     }
     __syncthreads();
-    if (tq + BQ < L) load_step(tq + BQ);
+    if (tq + BQ < tq_end) load_step(tq + BQ);
 
     // S = Q K^T and dP = dO V^T for the wave's 32 context rows.
     f32x16 S = f32x16{}, dP = f32x16{};
@@ -177,7 +198,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
         p = phi_value_grad<PHI>(S[r] * a.scale, gr);
         ds = dP[r] * gr;
       }
-      if (!jvalid) {
+      if (!jvalid || (SW && (jw > tq + t || jw <= tq + t - a.window))) {
         p = 0.f;
         ds = 0.f;
       }
@@ -231,7 +252,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
         const int t = t0 + 4 * (lane >> 4) + r;
         if (t < rows) {
           const size_t idx = (size_t)(seq0 + tq + t) * rs + (size_t)h * D + d;
-          if (nch == 1) {
+          if (!SW && nch == 1) {
             float v = acc[r];
             if (a.dq_base != nullptr) v += bf2f(((const uint16_t*)a.dq_base)[idx]);
             ((uint16_t*)a.dq)[idx] = __builtin_bit_cast(uint16_t, f2bf(v));
@@ -244,8 +265,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   }
 
   // dK, dV: lane (d + 32 g), register r holds context row 32 w + 8 (r / 4) + 4 g + r % 4.
-  uint16_t* dkp = (uint16_t*)a.dk + ((size_t)b * n * H + h) * D;
-  uint16_t* dvp = (uint16_t*)a.dv + ((size_t)b * n * H + h) * D;
+  uint16_t* dkp = (uint16_t*)a.dk + (kv0 + h) * D;
+  uint16_t* dvp = (uint16_t*)a.dv + (kv0 + h) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -396,6 +417,25 @@ static hipError_t bwd_bf16_dw(const BwdArgs& a, int phi, hipStream_t s) {
     hipLaunchKernelGGL((bwd_bf16_kernel<D, decltype(P)::value, NW>), g, blk, 0, s, a);
     return hipGetLastError();
   });
+}
+
+int swa_bwd_waves(int d) { return d == 32 ? 4 : 8; }
+
+template <int D, int NW>
+static hipError_t bwd_swa_dw(const BwdArgs& a, int max_chunks, hipStream_t s) {
+  const long items = (long)max_chunks * a.H;
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_bf16_kernel<D, kPhiSoftmax, NW, true>), dim3((unsigned)items), dim3(NW * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_swa(const BwdArgs& a, int d, int max_chunks, hipStream_t s) {
+  switch (d) {
+    case 32: return bwd_swa_dw<32, 4>(a, max_chunks, s);
+    case 64: return bwd_swa_dw<64, 8>(a, max_chunks, s);
+    case 128: return bwd_swa_dw<128, 8>(a, max_chunks, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, hipStream_t s) {

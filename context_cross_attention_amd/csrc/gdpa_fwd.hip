@@ -20,7 +20,11 @@
 
 namespace gdpa {
 
-template <int D, int PHI, bool RESID>
+// SW: sliding-window self-attention (Kunlun paper summary, section 2.2, Sliding
+// Window Attention bullet): K and V are the sample's own token rows, and token i
+// (position in its sample) attends to positions i - window < j <= i only; the
+// context-row loop covers just that band and out-of-band scores are -inf.
+template <int D, int PHI, bool RESID, bool SW = false>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   constexpr int BM = kFwdTileRows, BN = 64, KS = D / 16, DT = D / 32;
   // Row strides (elements), chosen for the 32-bank LDS: K rows are read 16 bytes
@@ -33,7 +37,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   __shared__ __align__(16) uint16_t Ks[BN * LD];
   __shared__ __align__(16) uint16_t Vs[BN * LDV];
 
-  const int H = a.H, B = a.B, n = a.n;
+  const int H = a.H, B = a.B;
   const int total = a.tile_start[B];
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
   if (wid >= total * H) return;
@@ -41,6 +45,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   const int b = find_sample(a.tile_start, B, qtile);
   const int row0 = a.offsets[b] + (qtile - a.tile_start[b]) * BM;
   const int rows = min(BM, a.offsets[b + 1] - row0);
+  const int seq0 = a.offsets[b];
+  const int n = SW ? a.offsets[b + 1] - seq0 : a.n;  // context rows of this sample
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const int trow = wave * 32 + lr;
@@ -56,8 +62,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       qf[ks] = tvalid ? as_bf16x8(gload16(qp + 16 * ks)) : bf16x8{};
   }
 
-  const uint16_t* Kg = (const uint16_t*)a.k + ((size_t)b * n * H + h) * D;
-  const uint16_t* Vg = (const uint16_t*)a.v + ((size_t)b * n * H + h) * D;
+  const size_t kv0 = SW ? (size_t)seq0 * H : (size_t)b * n * H;
+  const uint16_t* Kg = (const uint16_t*)a.k + (kv0 + h) * D;
+  const uint16_t* Vg = (const uint16_t*)a.v + (kv0 + h) * D;
+  // Context rows this tile needs: all n, or the band of its rows qlo .. qlo + rows - 1.
+  const int qlo = row0 - seq0;
+  const int jbeg = SW ? max(0, qlo - a.window + 1) : 0;
+  const int jend = SW ? min(n, qlo + rows) : n;
+  const int irow = qlo + trow;  // this lane's token position in its sample
   u32x4 kreg[SI], vreg[SI];
   auto gload_block = [&](int jb) {
 #pragma unroll
@@ -92,12 +104,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
 
-  gload_block(0);
-  for (int jb = 0; jb < n; jb += BN) {
+  gload_block(jbeg);
+  for (int jb = jbeg; jb < jend; jb += BN) {
     __syncthreads();
     store_block();
     __syncthreads();
-    if (jb + BN < n) gload_block(jb + BN);
+    if (jb + BN < jend) gload_block(jb + BN);
 
     f32x16 S[2];
 #pragma unroll
@@ -117,16 +129,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float s = S[mt][r] * sl2;
-          if (tail) {
+          if (tail || SW) {
             const int j = jb + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (j >= n) s = -INFINITY;
+            if (j >= n || (SW && (j > irow || j <= irow - a.window))) s = -INFINITY;
           }
           S[mt][r] = s;
           mx = fmaxf(mx, s);
         }
       mx = fmaxf(mx, wave_xor32(mx));
       const float m_new = fmaxf(m_run, mx);
-      const float corr = fast_exp2(m_run - m_new);
+      // A row whose window misses this whole block (SW) keeps m = -inf: shift by 0.
+      const float m_use = (SW && m_new == -INFINITY) ? 0.f : m_new;
+      const float corr = fast_exp2(m_run - m_use);
       l_run *= corr;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) O[dt] *= corr;
@@ -134,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(S[mt][r] - m_new);
+          const float p = fast_exp2(S[mt][r] - m_use);
           l_run += p;
           S[mt][r] = p;
         }
@@ -261,6 +275,22 @@ static hipError_t fwd_bf16_d(const FwdArgs& a, int phi, bool resid, int grid, hi
     else hipLaunchKernelGGL((fwd_bf16_kernel<D, PH, false>), g, blk, 0, s, a);
     return hipGetLastError();
   });
+}
+
+template <int D>
+static hipError_t fwd_swa_d(const FwdArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, kPhiSoftmax, false, true>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_swa(const FwdArgs& a, int d, int grid, hipStream_t s) {
+  if (grid == 0) return hipSuccess;
+  switch (d) {
+    case 32: return fwd_swa_d<32>(a, grid, s);
+    case 64: return fwd_swa_d<64>(a, grid, s);
+    case 128: return fwd_swa_d<128>(a, grid, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int d, int phi, bool resid, int grid, hipStream_t s) {

@@ -38,7 +38,6 @@ constexpr int NT_TILE_B = NT_M * NT_ROW_B;         // bytes of one operand tile 
 constexpr int NT_STAGE_B = 2 * NT_TILE_B;          // A tile then B tile
 constexpr int NT_RPI = 1024 / NT_ROW_B;            // rows per 1 KiB copy instruction (8)
 constexpr int NT_IPW = NT_M / 8 / NT_RPI;          // copy instructions per wave per tile (4)
-constexpr int NT_DMA = 2 * NT_IPW;                 // copies per wave per step (8)
 constexpr int NT_STORES = 16;                      // 16-byte stores per wave per tile
 constexpr int NT_CW_B = 32 * 64 * 2;               // per-wave output staging (32 x 64 bf16)
 }  // namespace

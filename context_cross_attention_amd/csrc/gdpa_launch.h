@@ -45,6 +45,7 @@ struct FwdArgs {
   float* lse;
   int B, T, n, H;
   float scale;
+  int window;                 // sliding-window self-attention: token i sees i - window < j <= i
 };
 
 struct BwdArgs {
@@ -64,6 +65,10 @@ struct BwdArgs {
   int n_chunks;       // work-groups per (sample, head)
   float scale;
   const void* dq_base;  // dq = dq_base + dQ when non-null (may alias dq or d_o)
+  // Sliding-window self-attention: K, V, dK, dV are [T,H,d] token tensors,
+  // chunk_start[B+1] the prefix sums of each sample's 32 * waves-row chunks.
+  const int32_t* chunk_start;
+  int window;
 };
 
 // Scheduling and small passes (gdpa_sched.hip).
@@ -90,6 +95,17 @@ hipError_t launch_fwd_res(const FwdArgs& a, const int32_t* order, int d, int phi
 // Backward (gdpa_bwd.hip).
 int bwd_bf16_waves(int d, int n);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, hipStream_t s);
+
+// Sliding-window self-attention on the jagged sequence (softmax, bf16): the
+// streaming kernels with K and V taken from the sample's own tokens and the
+// context rows limited to each token's window.  The forward grid is that of
+// launch_fwd_bf16 (tile_start over kFwdTileRows-row query tiles); the backward
+// runs one work-group per (chunk of 32 * swa_bwd_waves(d) key rows, head) over a
+// grid of max_chunks * H (an upper bound; surplus work-groups exit), accumulating dQ
+// in dq_acc (fp32, zeroed by the caller) for launch_dq_finalize.
+hipError_t launch_fwd_swa(const FwdArgs& a, int d, int grid, hipStream_t s);
+int swa_bwd_waves(int d);
+hipError_t launch_bwd_swa(const BwdArgs& a, int d, int max_chunks, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdArgs& a, int d, int phi, hipStream_t s);
 
 // Backward with one work-group per (sample, head) for d = 128, n <= 256 (gdpa_bwd_res.hip).

@@ -209,3 +209,34 @@ def make_stacked_inputs(cfg: GdpaConfig, seed: int = 0) -> StackedInputs:
 def small_config(base: GdpaConfig, **kw) -> GdpaConfig:
     """A copy of `base` with some fields replaced (used to shrink workloads for tests)."""
     return replace(base, **kw)
+
+
+@dataclass
+class SwaInputs:
+    """Sliding-window self-attention inputs: Q, K, V, dO all [T, H, d] from the sequence."""
+    lengths: np.ndarray
+    offsets: torch.Tensor
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    do: torch.Tensor
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.offsets[-1])
+
+
+def make_swa_inputs(length_spec: tuple, batch: int, H: int, d: int, seed: int = 0,
+                    sharp: bool = False, dtype: str = "bf16") -> SwaInputs:
+    """Draw lengths, then Q, K, V ~ N(0,1)/sqrt(d) (Q and K ~ N(0,1) when sharp), then
+    dO ~ N(0,1), all [T, H, d] and rounded to `dtype`."""
+    rng = np.random.default_rng(seed)
+    lengths = draw_lengths(rng, length_spec, batch)
+    off = offsets_from_lengths(lengths)
+    T = int(off[-1])
+    qk_div = 1.0 if sharp else math.sqrt(d)
+    q = draw_normal(rng, (T, H, d), dtype, qk_div)
+    k = draw_normal(rng, (T, H, d), dtype, qk_div)
+    v = draw_normal(rng, (T, H, d), dtype, math.sqrt(d))
+    do = draw_normal(rng, (T, H, d), dtype)
+    return SwaInputs(lengths, torch.from_numpy(off.astype(np.int32)), q, k, v, do)

@@ -137,6 +137,51 @@ gdpa_status gdpa_weightgen_fwd(int32_t batch, int32_t ctx_dim, int64_t cols, con
 gdpa_status gdpa_weightgen_bwd_w(int32_t batch, int32_t ctx_dim, int64_t cols, const void* ctx,
                                  const void* d_out, void* d_w, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Sliding-window self-attention over the same jagged batch (Kunlun paper
+ * summary, section 2.2, Sliding Window Attention bullet: the sequence's
+ * self-attention is restricted to local windows, O(T w) instead of O(T^2);
+ * Telegram review, layer step 5, and the event-level personalisation list that
+ * names w, the window size).  Q, K, V come from the sequence itself, all
+ * [T][H][d]; for token i (its position inside its sample) and head h:
+ *
+ *     s_j      = scale * < Q[i,h,:], K[j,h,:] >   for  i - window < j <= i  (same sample)
+ *     O[i,h,:] = sum_j softmax(s)_j V[j,h,:]
+ *
+ * The window is causal and holds the token and the window - 1 tokens before it
+ * (the pages' "most recent interactions"; they give no formula).  bf16 only,
+ * fp32 accumulation; head_dim in {32, 64, 128}.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;         /* B >= 1 samples */
+  int32_t total_tokens;  /* T = offsets[B] >= 0 */
+  int32_t max_seqlen;    /* >= every sample length (informational) */
+  int32_t heads;         /* H >= 1 */
+  int32_t head_dim;      /* d in {32, 64, 128} */
+  int32_t window;        /* w >= 1 */
+  float scale;           /* finite; 1/sqrt(d) is the usual value */
+  int32_t dtype;         /* GDPA_BF16 (GDPA_F32: GDPA_ERR_UNSUPPORTED) */
+  uint32_t flags;        /* must be 0 */
+} gdpa_swa_problem;
+
+/* Workspace bytes for gdpa_swa_fwd (backward = 0) or gdpa_swa_bwd (backward != 0);
+ * 0 for an invalid problem. */
+size_t gdpa_swa_workspace_bytes(const gdpa_swa_problem* p, int backward);
+
+/* Forward.  q, k, v [T,H,d] in; o [T,H,d] out (overwritten; must not alias an
+ * input); lse [T,H] float32 (natural log) written when non-NULL, required by the
+ * backward.  Errors as for gdpa_fwd. */
+gdpa_status gdpa_swa_fwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* q,
+                         const void* k, const void* v, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Backward of sum(O * dO): q, k, v, o, lse (from gdpa_swa_fwd) and d_o in; dq, dk,
+ * dv [T,H,d] out (overwritten; distinct from the inputs and from each other). */
+gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* q,
+                         const void* k, const void* v, const void* o, const float* lse,
+                         const void* d_o, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Host-side check of a HOST copy of offsets: returns GDPA_OK when offsets[0] = 0,
  * the array is non-decreasing, offsets[B] = total_tokens and every length is at
  * most max_seqlen; GDPA_ERR_INVALID_ARGUMENT otherwise. */
