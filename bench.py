@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--phi", default=None, choices=[None, "softmax", "silu", "relu", "gelu", "identity"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="gdpa", choices=["gdpa", "swa"],
+                    help="swa: sliding-window self-attention on the stacked workload's batch")
+    ap.add_argument("--window", type=int, default=512, help="window of --op swa")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
@@ -218,6 +221,114 @@ def cpu_baseline_single(inp, cfg, phi):
 
 
 # ---------------------------------------------------------------------------
+# sliding-window self-attention (--op swa)
+# ---------------------------------------------------------------------------
+
+def swa_pairs(lengths, w):
+    """Number of (token, key) pairs in the windows: sum over samples and positions of min(i + 1, w)."""
+    tot = 0
+    for L in lengths:
+        L = int(L)
+        m = min(L, w)
+        tot += m * (m + 1) // 2 + (L - m) * w
+    return tot
+
+
+def run_swa(args):
+    import numpy as np
+    import torch
+
+    import context_cross_attention_amd as cca
+    import gdpa_inputs as gi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cca.load()
+    cfg = gi.CONFIGS[5]
+    w = args.window
+    H, d, B = cfg.heads, cfg.head_dim, cfg.batch
+    inp = gi.make_swa_inputs(cfg.lengths, B, H, d, seed=args.seed)
+    T = inp.total_tokens
+    q, k, v, do = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.do))
+    off = inp.offsets.cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(cca.swa_workspace_bytes(q, off, w, True), dtype=torch.uint8, device="cuda")
+    marks = Marks(torch)
+
+    def step():
+        marks("swa_fwd", True)
+        cca.swa_fwd(q, off, k, v, w, out=o, lse=lse, workspace=ws)
+        marks("swa_fwd", False)
+        marks("swa_bwd", True)
+        cca.swa_bwd(q, off, k, v, o, lse, do, w, dq=dq, dk=dk, dv=dv, workspace=ws)
+        marks("swa_bwd", False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks.enabled = True
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    marks.enabled = False
+    pairs = swa_pairs(inp.lengths, w)
+    f_fwd, f_bwd = 4.0 * d * H * pairs, 8.0 * d * H * pairs
+    tok = T * H * d * 2
+    units = {"swa_fwd": (f_fwd, 4 * tok + 4 * T * H), "swa_bwd": (f_bwd, 8 * tok + 8 * T * H)}
+    totals, counts = marks.totals_ms(), marks.counts()
+    dom = max(totals, key=lambda x: totals[x])
+    t_dom = totals[dom] / counts[dom] * 1e-3
+    f_dom, b_dom = units[dom]
+    if b_dom / (PEAK_HBM_GBS * 1e9) >= f_dom / (PEAK_BF16_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": round(b_dom / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(f_dom / t_dom / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, kernel=dom,
+                launch_ms=round(totals[dom] / counts[dom], 4),
+                algorithmic_per_launch={"flops": f_dom, "bytes": b_dom})
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "sliding-window self-attention fwd+bwd TFLOP/s, jagged batch, 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws as in gdpa_inputs.make_swa_inputs)",
+        "config": {"workload": f"sliding-window self-attention fwd+bwd, window {w}: B={B} samples, lengths "
+                               f"log-normal (median {cfg.lengths[1]}, max {cfg.lengths[2]}), T={T}, H={H}, d={d}",
+                   "window": w, "tokens": T, "heads": H, "head_dim": d, "pairs": pairs, "seed": args.seed},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "breakdown_ms_per_step": {x: round(totals[x] / args.steps, 4) for x in totals},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import swa_oracle as swo
+        chosen, cost = [], 0.0
+        for b in range(B):
+            if inp.lengths[b] == 0:
+                continue
+            chosen.append(b)
+            cost += 12.0 * float(inp.lengths[b]) ** 2 * H * d   # the oracle forms whole L x L products
+            if cost >= 3.0e11:
+                break
+        t1 = time.perf_counter()
+        swo.swa_forward(inp.q, inp.offsets, inp.k, inp.v, w, samples=chosen)
+        swo.swa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, w, samples=chosen)
+        dt = time.perf_counter() - t1
+        p_s = swa_pairs([inp.lengths[b] for b in chosen], w)
+        fl = 12.0 * d * H * p_s
+        out["cpu_baseline"] = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"fwd+bwd on samples {chosen[0]}..{chosen[-1]} ({len(chosen)} of {B}); "
+                                         f"{fl / 1e9:.1f} GFLOP of window pairs in {dt:.1f} s (numpy float64, "
+                                         f"dense L x L per sample)", "seconds": round(dt, 2)}
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
 
@@ -232,6 +343,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.op == "swa":
+        run_swa(args)
         return
 
     import numpy as np

@@ -246,6 +246,12 @@ def _swa_problem(q: torch.Tensor, offsets: torch.Tensor, window: int, scale: Opt
                       1.0 / math.sqrt(d) if scale is None else float(scale), DTYPE[q.dtype], 0)
 
 
+def swa_workspace_bytes(q: torch.Tensor, offsets: torch.Tensor, window: int, backward: bool) -> int:
+    """Workspace bytes of swa_fwd (backward=False) or swa_bwd (backward=True)."""
+    prob = _swa_problem(q, offsets, window, None)
+    return int(load().gdpa_swa_workspace_bytes(ctypes.byref(prob), 1 if backward else 0))
+
+
 def _swa_workspace(prob: SwaProblem, backward: bool, device, workspace: Optional[torch.Tensor]):
     need = int(load().gdpa_swa_workspace_bytes(ctypes.byref(prob), 1 if backward else 0))
     if workspace is not None and workspace.numel() >= need:

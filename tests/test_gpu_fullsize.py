@@ -124,3 +124,34 @@ def test_fullsize_stacked(gdpa_lib):
     say("  errors:", {k_: f"{e:.2e}" for k_, e in errs.items()})
     for name, e in errs.items():
         assert e <= TOL["bf16"], (name, e)
+
+
+def test_fullsize_swa(gdpa_lib):
+    """Sliding-window self-attention at the size `bench.py --op swa` times (the stacked
+    workload's batch: B=1024, T=1,438,675, H=8, d=128; window 512), on sampled samples."""
+    from oracle import swa_oracle as swo
+    cca = gdpa_lib
+    cfg = gi.CONFIGS[5]
+    w = 512
+    inp = gi.make_swa_inputs(cfg.lengths, cfg.batch, cfg.heads, cfg.head_dim, seed=0)
+    samples = pick_samples(inp.lengths)
+    say(f"case: swa window {w} T={inp.total_tokens} samples={samples} "
+        f"(lengths {[int(inp.lengths[b]) for b in samples]})")
+    q, k, v, do = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.do))
+    off = inp.offsets.cuda()
+    o, lse = cca.swa_fwd(q, off, k, v, w)
+    dq, dk, dv = cca.swa_bwd(q, off, k, v, o, lse, do, w)
+    torch.cuda.synchronize()
+    rows = rows_of(inp.offsets, samples)
+    sub_len = [int(inp.lengths[b]) for b in samples]
+    sub_off = np.concatenate([[0], np.cumsum(sub_len)])
+    idx = torch.from_numpy(rows)
+    sq, sk, sv, sdo = (inp.q[idx], inp.k[idx], inp.v[idx], inp.do[idx])
+    o_ref, lse_ref = swo.swa_forward(sq, sub_off, sk, sv, w)
+    dq_ref, dk_ref, dv_ref = swo.swa_backward(sq, sub_off, sk, sv, sdo, w)
+    errs = {"o": max_abs_rel(gather(o, rows), o_ref), "lse": max_abs_rel(gather(lse, rows), lse_ref),
+            "dq": max_abs_rel(gather(dq, rows), dq_ref), "dk": max_abs_rel(gather(dk, rows), dk_ref),
+            "dv": max_abs_rel(gather(dv, rows), dv_ref)}
+    say("  errors:", {n_: f"{e:.2e}" for n_, e in errs.items()})
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (name, e)
