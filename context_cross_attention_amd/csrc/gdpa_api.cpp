@@ -46,12 +46,12 @@ gdpa_status check_problem(const gdpa_problem* p) {
 
 // Workspace layouts (each region 256-byte aligned).
 //   forward : tile_start [B+1] int32 (streaming kernel) | order [B] int32 (resident kernel)
-//   backward: order [B] int32 | dvec [T*H] fp32 (softmax) | dq_acc [T*H*d] fp32 (bf16,
-//             when the context rows span several work-groups)
+//   backward: order [B] int32 | dvec [T*H] fp32 (softmax) | tile_start [B+1] int32 (bf16,
+//             when the context rows span several work-groups: dQ per query tile)
 struct BwdPlan {
   int waves = 0, chunks = 0;
-  size_t order_off = 0, dvec_off = 0, acc_off = 0, total = 0;
-  bool need_acc = false;
+  size_t order_off = 0, dvec_off = 0, tile_off = 0, total = 0;
+  bool split_dq = false;  // several key chunks per (sample, head): dQ from the query-tile kernel
 };
 
 BwdPlan bwd_plan(const gdpa_problem* p) {
@@ -64,15 +64,15 @@ BwdPlan bwd_plan(const gdpa_problem* p) {
     pl.waves = gdpa::bwd_bf16_waves(p->head_dim, p->n_kv);
     const int nj = 32 * pl.waves;
     pl.chunks = (p->n_kv + nj - 1) / nj;
-    pl.need_acc = pl.chunks > 1;
+    pl.split_dq = pl.chunks > 1;
   }
   size_t off = 0;
   pl.order_off = off;
   off += align_up(sizeof(int32_t) * (size_t)p->batch);
   pl.dvec_off = off;
   if (p->phi == GDPA_PHI_SOFTMAX) off += align_up(sizeof(float) * TH);
-  pl.acc_off = off;
-  if (pl.need_acc) off += align_up(sizeof(float) * TH * p->head_dim);
+  pl.tile_off = off;
+  if (pl.split_dq) off += align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
   pl.total = off;
   return pl;
 }
@@ -172,7 +172,7 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dq_acc = pl.need_acc ? (float*)(ws + pl.acc_off) : nullptr;
+  a.tile_start = pl.split_dq ? (const int32_t*)(ws + pl.tile_off) : nullptr;
   a.B = p->batch;
   a.T = p->total_tokens;
   a.n = p->n_kv;
@@ -192,17 +192,19 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
 
   e = gdpa::launch_longest_first(offsets, p->batch, (int32_t*)(ws + pl.order_off), s);
   if (e != hipSuccess) return hip_status(e);
-  if (pl.need_acc) {
-    e = gdpa::launch_zero_f32(a.dq_acc, TH * p->head_dim, s);
-    if (e != hipSuccess) return hip_status(e);
-  }
   if (gdpa::bwd_res_supported(p->head_dim, p->n_kv))
     e = gdpa::launch_bwd_res(a, p->phi, s);
   else
-    e = gdpa::launch_bwd_bf16(a, p->head_dim, p->phi, pl.waves, s);
+    e = gdpa::launch_bwd_bf16(a, p->head_dim, p->phi, pl.waves, !pl.split_dq, s);
+  if (e != hipSuccess || !pl.split_dq) return hip_status(e);
+  // Several key chunks per (sample, head): dQ per 128-row query tile (no reduction
+  // across work-groups), after the key-chunk kernel, which reads every dO row - dq
+  // may be d_o itself (GDPA_BWD_RESIDUAL, GDPA_BWD_ACCUM_DQ); each dQ work-group
+  // reads the dO rows it overwrites before writing them.
+  e = gdpa::launch_tile_scan(offsets, p->batch, gdpa::kFwdTileRows, (int32_t*)(ws + pl.tile_off), s);
   if (e != hipSuccess) return hip_status(e);
-  if (pl.need_acc) e = gdpa::launch_dq_finalize(a.dq_acc, a.dq_base, dq, TH * p->head_dim, s);
-  return hip_status(e);
+  return hip_status(gdpa::launch_bwd_dq(a, p->head_dim, p->phi, false,
+                                        gdpa::fwd_bf16_grid(p->total_tokens, p->batch, p->heads), s));
 }
 
 gdpa_status gdpa_weightgen_fwd(int32_t batch, int32_t ctx_dim, int64_t cols, const void* ctx,
@@ -245,7 +247,7 @@ gdpa_status check_swa(const gdpa_swa_problem* p) {
 
 struct SwaBwdPlan {
   int waves, max_chunks;
-  size_t chunk_off, dvec_off, acc_off, total;
+  size_t chunk_off, tile_off, dvec_off, total;
 };
 
 SwaBwdPlan swa_bwd_plan(const gdpa_swa_problem* p) {
@@ -258,10 +260,10 @@ SwaBwdPlan swa_bwd_plan(const gdpa_swa_problem* p) {
   size_t off = 0;
   pl.chunk_off = off;
   off += align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
+  pl.tile_off = off;
+  off += align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
   pl.dvec_off = off;
   off += align_up(sizeof(float) * TH);
-  pl.acc_off = off;
-  off += align_up(sizeof(float) * TH * p->head_dim);
   pl.total = off;
   return pl;
 }
@@ -343,24 +345,26 @@ gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, cons
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dq_acc = (float*)(ws + pl.acc_off);
   a.B = p->batch;
   a.T = p->total_tokens;
   a.H = p->heads;
   a.n_chunks = 0;
   a.scale = p->scale;
   a.chunk_start = (const int32_t*)(ws + pl.chunk_off);
+  a.tile_start = (const int32_t*)(ws + pl.tile_off);
   a.window = p->window;
   const size_t TH = (size_t)p->total_tokens * p->heads;
   hipError_t e = gdpa::launch_softmax_dvec(o, d_o, (int)TH, p->head_dim, true, (float*)(ws + pl.dvec_off), s);
   if (e != hipSuccess) return hip_status(e);
   e = gdpa::launch_tile_scan(offsets, p->batch, 32 * pl.waves, (int32_t*)(ws + pl.chunk_off), s);
   if (e != hipSuccess) return hip_status(e);
-  e = gdpa::launch_zero_f32(a.dq_acc, TH * p->head_dim, s);
+  e = gdpa::launch_tile_scan(offsets, p->batch, gdpa::kFwdTileRows, (int32_t*)(ws + pl.tile_off), s);
   if (e != hipSuccess) return hip_status(e);
+  // dK / dV per key chunk, dQ per query tile: no cross-work-group reduction.
   e = gdpa::launch_bwd_swa(a, p->head_dim, pl.max_chunks, s);
   if (e != hipSuccess) return hip_status(e);
-  return hip_status(gdpa::launch_dq_finalize(a.dq_acc, nullptr, dq, TH * p->head_dim, s));
+  return hip_status(gdpa::launch_bwd_dq(a, p->head_dim, gdpa::kPhiSoftmax, true,
+                                        gdpa::fwd_bf16_grid(p->total_tokens, p->batch, p->heads), s));
 }
 
 gdpa_status gdpa_check_offsets(const int32_t* host_offsets, int32_t batch, int32_t total_tokens,

@@ -13,8 +13,9 @@
 //                                       B = dO / Q columns via LDS transpose reads)
 //   dQ  = scale dS K over all the work-group's context rows: dS^T goes to LDS and
 //         every wave computes 16x16 output tiles from it.
-// When the context rows need more than one work-group, dQ partial sums go to an
-// fp32 buffer with atomics and a final pass rounds them.
+// When the context rows need more than one work-group, this kernel computes dK and
+// dV only and dQ comes from the query-tile kernel of gdpa_bwd_dq.hip (S, P, dP
+// recomputed there), so nothing is reduced across work-groups.
 //
 // Work-groups are launched longest sample first (longest-processing-time list
 // scheduling by the hardware dispatcher).
@@ -32,9 +33,10 @@ __device__ __forceinline__ int qpos(int t) { return (t & ~7) | ((t & 3) << 1) | 
 // SW: sliding-window self-attention (Kunlun paper summary, section 2.2, Sliding
 // Window Attention bullet).  The work-group's key rows are a chunk of its sample's
 // own tokens, only the query steps whose windows reach them are visited, pairs
-// outside i - window < j <= i get P = dS = 0, and dQ always goes through the fp32
-// accumulator (several chunks feed each query row).
-template <int D, int PHI, int NW, bool SW = false>
+// outside i - window < j <= i get P = dS = 0.
+// DQ = false: dK and dV only (dQ comes from the query-tile kernel of gdpa_bwd_dq.hip,
+// used whenever several key chunks feed a query row).
+template <int D, int PHI, int NW, bool SW = false, bool DQ = true>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   constexpr int NJ = 32 * NW;          // context rows per work-group
   constexpr int BQ = kBwdRowsPerWave;  // query rows per step
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
 
     // dS^T rows of this wave into LDS: row jl, tokens 8 q + 4 g .. + 3.
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
+    for (int q4 = 0; q4 < (DQ ? 4 : 0); ++q4) {
       bf16x4 v;
       v[0] = f2bf(dS[4 * q4 + 0]); v[1] = f2bf(dS[4 * q4 + 1]);
       v[2] = f2bf(dS[4 * q4 + 2]); v[3] = f2bf(dS[4 * q4 + 3]);
@@ -229,6 +231,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
         dK[dt] = mfma32(sa, qb, dK[dt]);
       }
     }
+    if (!DQ) continue;
     __syncthreads();  // dS^T complete
 
     // dQ[32 x D] = dS[32 x NJ] K[NJ x D] with 16x16x32 tiles; wave w takes TPW tiles.
@@ -252,13 +255,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
         const int t = t0 + 4 * (lane >> 4) + r;
         if (t < rows) {
           const size_t idx = (size_t)(seq0 + tq + t) * rs + (size_t)h * D + d;
-          if (!SW && nch == 1) {
-            float v = acc[r];
-            if (a.dq_base != nullptr) v += bf2f(((const uint16_t*)a.dq_base)[idx]);
-            ((uint16_t*)a.dq)[idx] = __builtin_bit_cast(uint16_t, f2bf(v));
-          } else {
-            atomicAdd(a.dq_acc + idx, acc[r]);
-          }
+          float v = acc[r];
+          if (a.dq_base != nullptr) v += bf2f(((const uint16_t*)a.dq_base)[idx]);
+          ((uint16_t*)a.dq)[idx] = __builtin_bit_cast(uint16_t, f2bf(v));
         }
       }
     }
@@ -409,12 +408,13 @@ int bwd_bf16_waves(int d, int n) {
 }
 
 template <int D, int NW>
-static hipError_t bwd_bf16_dw(const BwdArgs& a, int phi, hipStream_t s) {
+static hipError_t bwd_bf16_dw(const BwdArgs& a, int phi, bool with_dq, hipStream_t s) {
   const long items = (long)a.B * a.H * a.n_chunks;
   if (items == 0) return hipSuccess;
   const dim3 g((unsigned)items), blk(NW * 64);
   return dispatch_phi(phi, [&](auto P) {
-    hipLaunchKernelGGL((bwd_bf16_kernel<D, decltype(P)::value, NW>), g, blk, 0, s, a);
+    if (with_dq) hipLaunchKernelGGL((bwd_bf16_kernel<D, decltype(P)::value, NW, false, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_bf16_kernel<D, decltype(P)::value, NW, false, false>), g, blk, 0, s, a);
     return hipGetLastError();
   });
 }
@@ -425,7 +425,8 @@ template <int D, int NW>
 static hipError_t bwd_swa_dw(const BwdArgs& a, int max_chunks, hipStream_t s) {
   const long items = (long)max_chunks * a.H;
   if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_bf16_kernel<D, kPhiSoftmax, NW, true>), dim3((unsigned)items), dim3(NW * 64), 0, s, a);
+  hipLaunchKernelGGL((bwd_bf16_kernel<D, kPhiSoftmax, NW, true, false>), dim3((unsigned)items), dim3(NW * 64), 0,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -438,12 +439,12 @@ hipError_t launch_bwd_swa(const BwdArgs& a, int d, int max_chunks, hipStream_t s
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, hipStream_t s) {
-  if (d == 32 && waves == 4) return bwd_bf16_dw<32, 4>(a, phi, s);
-  if (d == 64 && waves == 4) return bwd_bf16_dw<64, 4>(a, phi, s);
-  if (d == 64 && waves == 8) return bwd_bf16_dw<64, 8>(a, phi, s);
-  if (d == 128 && waves == 4) return bwd_bf16_dw<128, 4>(a, phi, s);
-  if (d == 128 && waves == 8) return bwd_bf16_dw<128, 8>(a, phi, s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, bool with_dq, hipStream_t s) {
+  if (d == 32 && waves == 4) return bwd_bf16_dw<32, 4>(a, phi, with_dq, s);
+  if (d == 64 && waves == 4) return bwd_bf16_dw<64, 4>(a, phi, with_dq, s);
+  if (d == 64 && waves == 8) return bwd_bf16_dw<64, 8>(a, phi, with_dq, s);
+  if (d == 128 && waves == 4) return bwd_bf16_dw<128, 4>(a, phi, with_dq, s);
+  if (d == 128 && waves == 8) return bwd_bf16_dw<128, 8>(a, phi, with_dq, s);
   return hipErrorInvalidValue;
 }
 

@@ -60,7 +60,6 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;      // [T*H*d] fp32, used when the context rows span several work-groups
   int B, T, n, H;
   int n_chunks;       // work-groups per (sample, head)
   float scale;
@@ -69,6 +68,7 @@ struct BwdArgs {
   // chunk_start[B+1] the prefix sums of each sample's 32 * waves-row chunks.
   const int32_t* chunk_start;
   int window;
+  const int32_t* tile_start;  // [B+1] query-tile prefix sums (dQ kernel)
 };
 
 // Scheduling and small passes (gdpa_sched.hip).
@@ -77,9 +77,6 @@ hipError_t launch_tile_scan(const int32_t* offsets, int B, int tile_rows, int32_
 hipError_t launch_longest_first(const int32_t* offsets, int B, int32_t* order, hipStream_t s);
 hipError_t launch_softmax_dvec(const void* o, const void* d_o, int rows, int d, bool bf16,
                                float* dvec, hipStream_t s);
-hipError_t launch_zero_f32(float* p, size_t count, hipStream_t s);
-hipError_t launch_dq_finalize(const float* acc, const void* base, void* dq, size_t count,
-                              hipStream_t s);
 
 // Forward (gdpa_fwd.hip).
 int fwd_bf16_grid(int T, int B, int H);
@@ -94,15 +91,19 @@ hipError_t launch_fwd_res(const FwdArgs& a, const int32_t* order, int d, int phi
 
 // Backward (gdpa_bwd.hip).
 int bwd_bf16_waves(int d, int n);
-hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, hipStream_t s);
+// with_dq = false: dK and dV only (dQ from launch_bwd_dq).
+hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, bool with_dq, hipStream_t s);
+// dQ over 128-row query tiles (gdpa_bwd_dq.hip), grid as launch_fwd_bf16 (a.tile_start
+// over kFwdTileRows-row tiles); sliding_window selects the window mode.
+hipError_t launch_bwd_dq(const BwdArgs& a, int d, int phi, bool sliding_window, int grid, hipStream_t s);
 
 // Sliding-window self-attention on the jagged sequence (softmax, bf16): the
 // streaming kernels with K and V taken from the sample's own tokens and the
 // context rows limited to each token's window.  The forward grid is that of
 // launch_fwd_bf16 (tile_start over kFwdTileRows-row query tiles); the backward
 // runs one work-group per (chunk of 32 * swa_bwd_waves(d) key rows, head) over a
-// grid of max_chunks * H (an upper bound; surplus work-groups exit), accumulating dQ
-// in dq_acc (fp32, zeroed by the caller) for launch_dq_finalize.
+// grid of max_chunks * H (an upper bound; surplus work-groups exit) for dK and dV;
+// dQ comes from launch_bwd_dq.
 hipError_t launch_fwd_swa(const FwdArgs& a, int d, int grid, hipStream_t s);
 int swa_bwd_waves(int d);
 hipError_t launch_bwd_swa(const BwdArgs& a, int d, int max_chunks, hipStream_t s);

@@ -120,25 +120,6 @@ __global__ __launch_bounds__(256) void softmax_dvec_kernel(const void* __restric
   if (row < rows && part == 0) dvec[row] = acc;
 }
 
-__global__ void zero_f32_kernel(float* __restrict__ p, size_t count) {
-  const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (i + 4 <= count) {
-    *(f32x4*)(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
-  } else {
-    for (size_t j = i; j < count; ++j) p[j] = 0.f;
-  }
-}
-
-// dq = bf16(acc (+ base)) elementwise; base may alias dq.
-__global__ void dq_finalize_kernel(const float* __restrict__ acc, const uint16_t* base,
-                                   uint16_t* dq, size_t count) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= count) return;
-  float v = acc[i];
-  if (base != nullptr) v += bf2f(base[i]);
-  dq[i] = __builtin_bit_cast(uint16_t, f2bf(v));
-}
-
 hipError_t launch_tile_scan(const int32_t* offsets, int B, int tile_rows, int32_t* tile_start,
                             hipStream_t s) {
   hipLaunchKernelGGL(tile_scan_kernel, dim3(1), dim3(1024), 0, s, offsets, B, tile_rows,
@@ -171,22 +152,6 @@ hipError_t launch_softmax_dvec(const void* o, const void* d_o, int rows, int d, 
   GDPA_DVEC(32) GDPA_DVEC(64) GDPA_DVEC(128)
 #undef GDPA_DVEC
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_zero_f32(float* p, size_t count, hipStream_t s) {
-  if (count == 0) return hipSuccess;
-  const size_t threads = (count + 3) / 4;
-  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p,
-                     count);
-  return hipGetLastError();
-}
-
-hipError_t launch_dq_finalize(const float* acc, const void* base, void* dq, size_t count,
-                              hipStream_t s) {
-  if (count == 0) return hipSuccess;
-  hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s,
-                     acc, (const uint16_t*)base, (uint16_t*)dq, count);
-  return hipGetLastError();
 }
 
 }  // namespace gdpa

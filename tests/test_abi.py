@@ -106,9 +106,22 @@ def test_workspace_sizes(lib):
     soft = cca.workspace_bytes(P(total_tokens=1000, phi=0), True)
     silu = cca.workspace_bytes(P(total_tokens=1000, phi=1), True)
     assert soft - silu >= 4 * 1000 * 2
-    # context rows beyond one backward work-group add an fp32 dQ buffer
+    # context rows beyond one backward work-group add the query-tile prefix sums of the
+    # dQ kernel (B + 1 int32), and no fp32 dQ buffer
     big = cca.workspace_bytes(P(total_tokens=1000, phi=1, n_kv=1024, head_dim=128), True)
-    assert big - silu >= 4 * 1000 * 2 * 128
+    assert 4 * 3 <= big - silu < 4 * 1000 * 128
+
+
+def test_swa_workspace_sizes(lib):
+    import ctypes
+    def W(backward, **kw):
+        f = dict(batch=2, total_tokens=1000, max_seqlen=1000, heads=2, head_dim=128, window=64,
+                 scale=0.1, dtype=1, flags=0)
+        f.update(kw)
+        return int(lib.gdpa_swa_workspace_bytes(ctypes.byref(cca.SwaProblem(**f)), backward))
+    assert W(0) >= 4 * 3 and W(0) % 256 == 0
+    assert W(1) >= 4 * 1000 * 2       # rowsum(dO * O) per (token, head)
+    assert W(1, window=0) == 0 and W(0, head_dim=48) == 0 and W(1, dtype=0) == 0
 
 
 def test_status_strings_and_offsets_check(lib):
