@@ -47,6 +47,14 @@ class SwaProblem(ctypes.Structure):
                 ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
+class PmaProblem(ctypes.Structure):
+    """Mirror of gdpa_pma_problem in include/gdpa.h."""
+    _fields_ = [("batch", ctypes.c_int32), ("total_tokens", ctypes.c_int32),
+                ("max_seqlen", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("seeds", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
 class GdpaError(RuntimeError):
     def __init__(self, status: int, where: str, hip_error: int = 0):
         msg = f"{where}: {STATUS.get(status, status)}"
@@ -60,6 +68,7 @@ _lib = None
 
 EXPORTS = ("gdpa_workspace_bytes", "gdpa_fwd", "gdpa_bwd", "gdpa_weightgen_fwd",
            "gdpa_weightgen_bwd_w", "gdpa_swa_workspace_bytes", "gdpa_swa_fwd", "gdpa_swa_bwd",
+           "gdpa_pma_workspace_bytes", "gdpa_pma_fwd", "gdpa_pma_bwd",
            "gdpa_check_offsets", "gdpa_status_str", "gdpa_last_hip_error")
 
 
@@ -90,6 +99,13 @@ def load(path: str = LIB_PATH):
     lib.gdpa_swa_fwd.restype = ctypes.c_int
     lib.gdpa_swa_bwd.argtypes = [SP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_swa_bwd.restype = ctypes.c_int
+    PP = ctypes.POINTER(PmaProblem)
+    lib.gdpa_pma_workspace_bytes.argtypes = [PP, ctypes.c_int]
+    lib.gdpa_pma_workspace_bytes.restype = sz
+    lib.gdpa_pma_fwd.argtypes = [PP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_pma_fwd.restype = ctypes.c_int
+    lib.gdpa_pma_bwd.argtypes = [PP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_pma_bwd.restype = ctypes.c_int
     lib.gdpa_check_offsets.argtypes = [vp, i32, i32, i32]
     lib.gdpa_check_offsets.restype = ctypes.c_int
     lib.gdpa_status_str.argtypes = [ctypes.c_int]
@@ -305,6 +321,83 @@ def swa_bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Te
                             _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
                             _stream()), "gdpa_swa_bwd")
     return dq, dk, dv
+
+
+def _pma_problem(seeds: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, scale: Optional[float]):
+    m, H, d = seeds.shape
+    if seeds.dtype not in DTYPE:
+        raise TypeError(f"unsupported dtype {seeds.dtype}")
+    return PmaProblem(offsets.shape[0] - 1, k.shape[0], k.shape[0], H, d, m,
+                      1.0 / math.sqrt(d) if scale is None else float(scale), DTYPE[seeds.dtype], 0)
+
+
+def pma_workspace_bytes(seeds: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, backward: bool) -> int:
+    """Workspace bytes of pma_fwd (backward=False) or pma_bwd (backward=True)."""
+    prob = _pma_problem(seeds, offsets, k, None)
+    return int(load().gdpa_pma_workspace_bytes(ctypes.byref(prob), 1 if backward else 0))
+
+
+def _pma_workspace(prob: PmaProblem, backward: bool, device, workspace: Optional[torch.Tensor]):
+    need = int(load().gdpa_pma_workspace_bytes(ctypes.byref(prob), 1 if backward else 0))
+    if workspace is not None and workspace.numel() >= need:
+        return workspace
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+
+def pma_fwd(seeds: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Seed pooling attention forward: seeds [m,H,d], k, v [T,H,d] bf16 over the jagged
+    batch; returns (o [B,m,H,d], lse [B,m,H] float32)."""
+    lib = load()
+    m, H, d = seeds.shape
+    T = k.shape[0]
+    B = offsets.shape[0] - 1
+    dev = seeds.device
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, (T, H, d), seeds.dtype, dev)
+    _require(seeds, "seeds", (m, H, d), seeds.dtype, dev)
+    _require(offsets, "offsets", (B + 1,), torch.int32, dev)
+    out = torch.empty((B, m, H, d), dtype=seeds.dtype, device=dev) if out is None else out
+    lse = torch.empty((B, m, H), dtype=torch.float32, device=dev) if lse is None else lse
+    _require(out, "out", (B, m, H, d), seeds.dtype, dev)
+    _require(lse, "lse", (B, m, H), torch.float32, dev)
+    prob = _pma_problem(seeds, offsets, k, scale)
+    ws = _pma_workspace(prob, False, dev, workspace)
+    _check(lib.gdpa_pma_fwd(ctypes.byref(prob), _ptr(offsets), _ptr(seeds), _ptr(k), _ptr(v), _ptr(out),
+                            _ptr(lse), _ptr(ws), ws.numel(), _stream()), "gdpa_pma_fwd")
+    return out, lse
+
+
+def pma_bwd(seeds: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            o: torch.Tensor, lse: torch.Tensor, do: torch.Tensor, scale: Optional[float] = None,
+            d_seeds: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+            dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Seed pooling attention backward of sum(O * dO).  Returns (d_seeds [m,H,d], dk, dv)."""
+    lib = load()
+    m, H, d = seeds.shape
+    T = k.shape[0]
+    B = offsets.shape[0] - 1
+    dev = seeds.device
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, (T, H, d), seeds.dtype, dev)
+    for name, t in (("o", o), ("do", do)):
+        _require(t, name, (B, m, H, d), seeds.dtype, dev)
+    _require(seeds, "seeds", (m, H, d), seeds.dtype, dev)
+    _require(lse, "lse", (B, m, H), torch.float32, dev)
+    _require(offsets, "offsets", (B + 1,), torch.int32, dev)
+    d_seeds = torch.empty_like(seeds) if d_seeds is None else d_seeds
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _require(d_seeds, "d_seeds", (m, H, d), seeds.dtype, dev)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _require(t, name, (T, H, d), seeds.dtype, dev)
+    prob = _pma_problem(seeds, offsets, k, scale)
+    ws = _pma_workspace(prob, True, dev, workspace)
+    _check(lib.gdpa_pma_bwd(ctypes.byref(prob), _ptr(offsets), _ptr(seeds), _ptr(k), _ptr(v), _ptr(o),
+                            _ptr(lse), _ptr(do), _ptr(d_seeds), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                            _stream()), "gdpa_pma_bwd")
+    return d_seeds, dk, dv
 
 
 def weightgen_fwd(ctx: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None):

@@ -30,7 +30,7 @@ CFLAGS = [
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 SOURCES = ["gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_fwd_res.hip", "gdpa_bwd.hip", "gdpa_bwd_res.hip",
-           "gdpa_bwd_dq.hip", "gdpa_gemm.hip", "gdpa_api.cpp"]
+           "gdpa_bwd_dq.hip", "gdpa_gemm.hip", "gdpa_pma.hip", "gdpa_api.cpp"]
 # Per-source extra flags.  The backward kernel keeps 256 fp32 accumulators per lane
 # in AGPRs for the whole sample; selecting the VGPR form of MFMA for everything else
 # (the per-step score tiles) keeps those accumulators resident instead of spilled.

@@ -367,6 +367,135 @@ gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, cons
                                         gdpa::fwd_bf16_grid(p->total_tokens, p->batch, p->heads), s));
 }
 
+}  // extern "C"
+
+namespace {
+
+gdpa_status check_pma(const gdpa_pma_problem* p) {
+  if (p == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->batch < 1 || p->total_tokens < 0 || p->max_seqlen < 0 || p->heads < 1 || p->head_dim < 1 ||
+      p->seeds < 1)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->dtype != GDPA_F32 && p->dtype != GDPA_BF16) return GDPA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->scale)) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)p->total_tokens * p->heads > INT32_MAX) return GDPA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)p->batch * p->seeds * p->heads > INT32_MAX) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) return GDPA_ERR_UNSUPPORTED;
+  if (p->seeds > 32 || p->dtype != GDPA_BF16 || p->flags != 0) return GDPA_ERR_UNSUPPORTED;
+  // Work-group ids: (chunks upper bound) x heads must fit a grid dimension.
+  if (((int64_t)p->total_tokens / gdpa::kPmaChunk + p->batch) * p->heads + 8 > INT32_MAX)
+    return GDPA_ERR_UNSUPPORTED;
+  return GDPA_OK;
+}
+
+// Workspace: chunk_start [B+1] int32 | part [chunks][H][32][d] fp32 | forward:
+// part_ml [chunks][H][32][2] fp32, backward: part2 [slices][H][32][d] fp32.
+struct PmaPlan {
+  size_t chunk_off, part_off, extra_off, total;
+};
+
+PmaPlan pma_plan(const gdpa_pma_problem* p, bool backward) {
+  PmaPlan pl{};
+  const size_t chunks = (size_t)p->total_tokens / gdpa::kPmaChunk + p->batch;
+  const size_t per_chunk = (size_t)p->heads * 32 * p->head_dim;
+  size_t off = 0;
+  pl.chunk_off = off;
+  off += align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
+  pl.part_off = off;
+  off += align_up(sizeof(float) * chunks * per_chunk);
+  pl.extra_off = off;
+  off += backward ? align_up(sizeof(float) * gdpa::kPmaSlices * per_chunk)
+                  : align_up(sizeof(float) * chunks * p->heads * 32 * 2);
+  pl.total = off;
+  return pl;
+}
+
+gdpa::PmaArgs pma_args(const gdpa_pma_problem* p, const int32_t* offsets, char* ws, const PmaPlan& pl) {
+  gdpa::PmaArgs a{};
+  a.offsets = offsets;
+  a.chunk_start = (const int32_t*)(ws + pl.chunk_off);
+  a.part = (float*)(ws + pl.part_off);
+  a.B = p->batch;
+  a.H = p->heads;
+  a.m = p->seeds;
+  a.scale = p->scale;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdpa_pma_workspace_bytes(const gdpa_pma_problem* p, int backward) {
+  if (check_pma(p) != GDPA_OK) return 0;
+  return pma_plan(p, backward != 0).total;
+}
+
+gdpa_status gdpa_pma_fwd(const gdpa_pma_problem* p, const int32_t* offsets, const void* seeds,
+                         const void* k, const void* v, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const gdpa_status st = check_pma(p);
+  if (st != GDPA_OK) return st;
+  if (offsets == nullptr || seeds == nullptr || o == nullptr || lse == nullptr)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->total_tokens > 0 && (k == nullptr || v == nullptr)) return GDPA_ERR_INVALID_ARGUMENT;
+  if (o == seeds || o == k || o == v) return GDPA_ERR_INVALID_ARGUMENT;
+  const PmaPlan pl = pma_plan(p, false);
+  if (workspace == nullptr || workspace_bytes < pl.total) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  gdpa::PmaArgs a = pma_args(p, offsets, ws, pl);
+  a.seeds = seeds;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.part_ml = (float*)(ws + pl.extra_off);
+  hipError_t e = gdpa::launch_tile_scan(offsets, p->batch, gdpa::kPmaChunk, (int32_t*)(ws + pl.chunk_off), s);
+  if (e != hipSuccess) return hip_status(e);
+  const int grid = p->total_tokens > 0 ? gdpa::pma_grid(p->total_tokens, p->batch, p->heads) : 0;
+  return hip_status(gdpa::launch_pma_fwd(a, p->head_dim, grid, s));
+}
+
+gdpa_status gdpa_pma_bwd(const gdpa_pma_problem* p, const int32_t* offsets, const void* seeds,
+                         const void* k, const void* v, const void* o, const float* lse,
+                         const void* d_o, void* d_seeds, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  const gdpa_status st = check_pma(p);
+  if (st != GDPA_OK) return st;
+  if (offsets == nullptr || seeds == nullptr || o == nullptr || lse == nullptr || d_o == nullptr ||
+      d_seeds == nullptr)
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->total_tokens > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  const void* outs[3] = {d_seeds, dk, dv};
+  const void* ins[6] = {seeds, k, v, o, d_o, lse};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (outs[i] != nullptr && outs[i] == ins[j]) return GDPA_ERR_INVALID_ARGUMENT;
+    for (int j = i + 1; j < 3; ++j)
+      if (outs[i] != nullptr && outs[i] == outs[j]) return GDPA_ERR_INVALID_ARGUMENT;
+  }
+  const PmaPlan pl = pma_plan(p, true);
+  if (workspace == nullptr || workspace_bytes < pl.total) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  gdpa::PmaArgs a = pma_args(p, offsets, ws, pl);
+  a.seeds = seeds;
+  a.k = k;
+  a.v = v;
+  a.o = const_cast<void*>(o);
+  a.lse = const_cast<float*>(lse);
+  a.d_o = d_o;
+  a.d_seeds = d_seeds;
+  a.dk = dk;
+  a.dv = dv;
+  hipError_t e = gdpa::launch_tile_scan(offsets, p->batch, gdpa::kPmaChunk, (int32_t*)(ws + pl.chunk_off), s);
+  if (e != hipSuccess) return hip_status(e);
+  const int grid = p->total_tokens > 0 ? gdpa::pma_grid(p->total_tokens, p->batch, p->heads) : 0;
+  return hip_status(gdpa::launch_pma_bwd(a, p->head_dim, grid, (float*)(ws + pl.extra_off), s));
+}
+
 gdpa_status gdpa_check_offsets(const int32_t* host_offsets, int32_t batch, int32_t total_tokens,
                                int32_t max_seqlen) {
   if (host_offsets == nullptr || batch < 1 || total_tokens < 0 || max_seqlen < 0)

@@ -97,6 +97,36 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, bool wit
 // over kFwdTileRows-row tiles); sliding_window selects the window mode.
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, int phi, bool sliding_window, int grid, hipStream_t s);
 
+// Seed pooling attention (gdpa_pma.hip): m <= 32 seeds [m,H,d] attend over each
+// sample's tokens K, V [T,H,d].  One work-group per (chunk of kPmaChunk tokens,
+// head) over a grid of pma_grid(T, B, H) (an upper bound; surplus work-groups
+// exit); chunk_start[B+1] holds the prefix sums of ceil(L_b / kPmaChunk).
+constexpr int kPmaChunk = 1024;
+constexpr int kPmaSlices = 32;  // first-level slices of the dSeeds reduction
+struct PmaArgs {
+  const int32_t* offsets;      // [B+1]
+  const int32_t* chunk_start;  // [B+1]
+  const void* seeds;           // [m,H,d]
+  const void* k;               // [T,H,d]
+  const void* v;
+  void* o;                     // [B,m,H,d] (backward: read)
+  float* lse;                  // [B,m,H] natural log (backward: read)
+  const void* d_o;             // [B,m,H,d]
+  void* d_seeds;               // [m,H,d]
+  void* dk;                    // [T,H,d]
+  void* dv;
+  float* part;                 // [chunks][H][32][d]: forward O partials / backward dSeeds partials
+  float* part_ml;              // [chunks][H][32][2]: forward (max in log2 units, sum)
+  int B, H, m;
+  float scale;
+};
+int pma_grid(int T, int B, int H);
+// Forward: chunk kernel, then the merge of multi-chunk and empty samples.
+hipError_t launch_pma_fwd(const PmaArgs& a, int d, int grid, hipStream_t s);
+// Backward: chunk kernel (dK, dV, dSeeds partials), then the two-level dSeeds
+// reduction through part2 [kPmaSlices][H][32][d] fp32.
+hipError_t launch_pma_bwd(const PmaArgs& a, int d, int grid, float* part2, hipStream_t s);
+
 // Sliding-window self-attention on the jagged sequence (softmax, bf16): the
 // streaming kernels with K and V taken from the sample's own tokens and the
 // context rows limited to each token's window.  The forward grid is that of

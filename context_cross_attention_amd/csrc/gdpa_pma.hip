@@ -1,0 +1,556 @@
+// Seed pooling attention over a jagged batch: the attention core of Pooling by
+// Multihead Attention, whose learnable seed queries Hierarchical Seed Pooling
+// builds on (Kunlun paper summary, section 2.2, HSP bullet; Telegram review,
+// layer step 3).  For sample b (tokens offsets[b] .. offsets[b+1]-1 of K, V
+// [T,H,d]), seed s < m and head h:
+//   O[b,s,h,:] = sum_j softmax_j(scale <Seeds[s,h,:], K[j,h,:]>) V[j,h,:]
+// and the backward gives dK, dV per token and dSeeds summed over the batch.
+// bf16 in and out, fp32 accumulation, d in {32, 64, 128}, m <= 32.
+//
+// Work: one work-group (4 waves) per (chunk of up to kPmaChunk tokens of one
+// sample, head).  The 32 (zero-padded) seeds stay in registers as MFMA operands;
+// K and V stream through a 2-stage LDS ring of 128-token blocks, filled by
+// global->LDS DMA one block ahead; wave w takes tokens 32 w .. 32 w + 31 of each
+// block.  Per byte of K/V the operation does at most m flops, far below the
+// MFMA/HBM balance point of the chip, so the kernels are organised around
+// keeping HBM busy; the MFMA work hides under the copies.
+//
+// LDS tiles are dense row-major [rows][d] bf16 with the 16-byte chunks of a row
+// permuted (chunk c of row r stored at position c ^ swz(r)), so that both the
+// 16-byte row reads (16 consecutive rows per phase) and the transpose reads
+// (4 rows x 64 bytes per 32-lane phase) hit distinct banks.
+//
+// Forward layout: S^T = K Seeds^T (lane = seed, registers = tokens), so the
+// softmax statistics are per lane; O^T += V^T P^T (A = V^T by transpose reads).
+// Backward layout: S = Seeds K^T and dP = dO V^T (lane = token, registers =
+// seeds); dV^T = dO^T P and dK^T = scale Seeds^T dS (A operands by transpose
+// reads of the seed and dO tiles); dSeeds^T += K^T dS^T with dS^T read back
+// transposed from a per-wave LDS tile.
+#include <math.h>
+
+#include "gdpa_device.h"
+#include "gdpa_launch.h"
+
+namespace gdpa {
+
+namespace {
+
+constexpr int kPmaBlock = 128;  // tokens per LDS stage
+
+// Chunk position permutation of a [rows][D] tile (see the header comment).
+template <int D>
+__device__ __forceinline__ int pma_swz(int row) {
+  if constexpr (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
+  else if constexpr (D == 64) return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+  else return (row >> 2) & 3;
+}
+// Element offset of 16-byte chunk c (elements 8 c .. 8 c + 7) of `row`.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int c) {
+  return row * D + 8 * (c ^ pma_swz<D>(row));
+}
+
+// DMA of tokens tok0 .. tok0 + 127 (rows past `last` repeat row `last`, so
+// every row holds finite data) of K and V into the tiles Kt, Vt.  Kg / Vg point
+// at token 0 of the sample, head h; rs is the token stride in elements.
+template <int D>
+__device__ __forceinline__ void pma_issue(uint16_t* Kt, uint16_t* Vt, const uint16_t* Kg,
+                                          const uint16_t* Vg, size_t rs, int tok0, int last,
+                                          int wave, int lane) {
+  constexpr int NQ = kPmaBlock * D / 512;  // 1 KiB wave copies per tensor
+#pragma unroll
+  for (int q = wave; q < NQ; q += 4) {
+    const int e = q * 512 + 8 * lane;
+    const int row = e / D, pos = (e % D) / 8;
+    const size_t src = (size_t)min(tok0 + row, last) * rs + 8 * (pos ^ pma_swz<D>(row));
+    dma16(__builtin_amdgcn_readfirstlane(lds_addr(Kt + q * 512)), Kg + src);
+    dma16(__builtin_amdgcn_readfirstlane(lds_addr(Vt + q * 512)), Vg + src);
+  }
+}
+
+// A operand of a [32][D] (or wider) tile read column-wise: lane (x + 32 g) gets
+// column 32 dt + x of rows r0 + 16 kk + 4 g + {0..3} and r0 + 16 kk + 8 + 4 g + {0..3},
+// the row order of pack_c8(C, kk) for a C tile whose rows are those rows.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_cols(const uint16_t* t, int r0, int kk, int dt, int lane) {
+  const int G = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
+  const int R = r0 + 16 * kk + 4 * (G >> 1) + rr;
+  const int c8 = 4 * dt + 2 * (G & 1) + (cc >> 1);
+  return cat8(lds_read_tr4(t + tile_off<D>(R, c8) + 4 * (cc & 1)),
+              lds_read_tr4(t + tile_off<D>(R + 8, c8) + 4 * (cc & 1)));
+}
+
+struct ChunkInfo {
+  int b, h, seq0, c0, c1, nch, chunk;
+};
+
+__device__ __forceinline__ bool decode_chunk(const PmaArgs& a, ChunkInfo& ci) {
+  const int nchunks = a.chunk_start[a.B];
+  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  if (wid >= nchunks * a.H) return false;
+  ci.chunk = wid / a.H;
+  ci.h = wid - ci.chunk * a.H;
+  ci.b = find_sample(a.chunk_start, a.B, ci.chunk);
+  ci.seq0 = a.offsets[ci.b];
+  const int len = a.offsets[ci.b + 1] - ci.seq0;
+  ci.c0 = (ci.chunk - a.chunk_start[ci.b]) * kPmaChunk;
+  ci.c1 = min(len, ci.c0 + kPmaChunk);
+  ci.nch = a.chunk_start[ci.b + 1] - a.chunk_start[ci.b];
+  return true;
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void pma_fwd_kernel(const PmaArgs a) {
+  constexpr int KS = D / 16, DT = D / 32, TILE = kPmaBlock * D, OS = D + 4;
+  __shared__ __align__(1024) uint16_t ring[4 * TILE];  // [slot][K | V][TILE]
+
+  ChunkInfo ci;
+  if (!decode_chunk(a, ci)) return;
+  const int H = a.H, h = ci.h;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const size_t rs = (size_t)H * D;
+  const uint16_t* Kg = (const uint16_t*)a.k + (size_t)ci.seq0 * rs + (size_t)h * D;
+  const uint16_t* Vg = (const uint16_t*)a.v + (size_t)ci.seq0 * rs + (size_t)h * D;
+  const int nblk = (ci.c1 - ci.c0 + kPmaBlock - 1) / kPmaBlock;
+  pma_issue<D>(ring, ring + TILE, Kg, Vg, rs, ci.c0, ci.c1 - 1, wave, lane);
+
+  // Seeds as B operands: lane (s + 32 g) holds Seeds[s][16 ks + 8 g .. + 7].
+  bf16x8 sb[KS];
+  {
+    const uint16_t* sp = (const uint16_t*)a.seeds + ((size_t)(lr < a.m ? lr : 0) * H + h) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sb[ks] = lr < a.m ? as_bf16x8(gload16(sp + 16 * ks)) : bf16x8{};
+  }
+
+  const float sl2 = a.scale * kLog2e;
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 O[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (blk + 1 < nblk)
+      pma_issue<D>(ring + ((blk + 1) & 1) * 2 * TILE, ring + ((blk + 1) & 1) * 2 * TILE + TILE, Kg, Vg,
+                   rs, ci.c0 + (blk + 1) * kPmaBlock, ci.c1 - 1, wave, lane);
+    const uint16_t* Kt = ring + (blk & 1) * 2 * TILE;
+    const uint16_t* Vt = Kt + TILE;
+    const int nvalid = min(32, ci.c1 - (ci.c0 + blk * kPmaBlock + 32 * wave));
+    if (nvalid <= 0) continue;
+    const int r0 = 32 * wave;
+
+    // S^T[t][s]: lane (s + 32 g), register r <-> token 8 (r / 4) + 4 g + r % 4.
+    f32x16 S = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) S = mfma32(lds_read8(Kt + tile_off<D>(r0 + lr, 2 * ks + g)), sb[ks], S);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 8 * (r >> 2) + 4 * g + (r & 3);
+      S[r] = t < nvalid ? S[r] * sl2 : -INFINITY;
+      mx = fmaxf(mx, S[r]);
+    }
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float m_new = fmaxf(m_run, mx);  // finite: token 0 of the block is valid
+    const float alpha = fast_exp2(m_run - m_new);
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      S[r] = fast_exp2(S[r] - m_new);
+      ls += S[r];
+    }
+    l_run = fmaf(l_run, alpha, ls);
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 pb = pack_c8(S, kk);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt] = mfma32(tile_cols<D>(Vt, r0, kk, dt, lane), pb, O[dt]);
+    }
+  }
+
+  // Merge the 4 waves' (max, sum, O) per seed through LDS (the ring is free).
+  const float l_tot = l_run + wave_xor32(l_run);
+  __syncthreads();
+  float* ob = (float*)ring;           // [4][32][OS]
+  float* ml = ob + 4 * 32 * OS;       // [4][32][2]
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 v;
+      v[0] = O[dt][4 * q]; v[1] = O[dt][4 * q + 1]; v[2] = O[dt][4 * q + 2]; v[3] = O[dt][4 * q + 3];
+      *(GDPA_LDS f32x4*)(ob + (wave * 32 + lr) * OS + 32 * dt + 8 * q + 4 * g) = v;
+    }
+  if (g == 0) {
+    ml[(wave * 32 + lr) * 2] = m_run;
+    ml[(wave * 32 + lr) * 2 + 1] = l_tot;
+  }
+  __syncthreads();
+
+  constexpr int NC = D / 8;  // columns per thread
+  const int s = tid >> 3, cb = (tid & 7) * NC;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * 32 + s) * 2]);
+  float wt[4], L = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wt[w] = fast_exp2(ml[(w * 32 + s) * 2] - M);
+    L = fmaf(ml[(w * 32 + s) * 2 + 1], wt[w], L);
+  }
+  float o[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = fmaf(ob[(w * 32 + s) * OS + cb + j], wt[w], acc);
+    o[j] = acc;
+  }
+  if (ci.nch == 1) {
+    if (s < a.m) {
+      const float inv = 1.0f / L;
+      uint16_t* op = (uint16_t*)a.o + (((size_t)ci.b * a.m + s) * H + h) * D + cb;
+#pragma unroll
+      for (int j = 0; j < NC; j += 4) {
+        bf16x4 v;
+        v[0] = f2bf(o[j] * inv); v[1] = f2bf(o[j + 1] * inv); v[2] = f2bf(o[j + 2] * inv); v[3] = f2bf(o[j + 3] * inv);
+        *(bf16x4*)(op + j) = v;
+      }
+      if ((tid & 7) == 0) a.lse[((size_t)ci.b * a.m + s) * H + h] = (M + log2f(L)) * kLn2;
+    }
+  } else {
+    float* pp = a.part + ((size_t)ci.chunk * H + h) * 32 * D + (size_t)s * D + cb;
+#pragma unroll
+    for (int j = 0; j < NC; j += 4) {
+      f32x4 v;
+      v[0] = o[j]; v[1] = o[j + 1]; v[2] = o[j + 2]; v[3] = o[j + 3];
+      *(f32x4*)(pp + j) = v;
+    }
+    if ((tid & 7) == 0) {
+      float* mp = a.part_ml + (((size_t)ci.chunk * H + h) * 32 + s) * 2;
+      mp[0] = M;
+      mp[1] = L;
+    }
+  }
+}
+
+// O and LSE of samples with no chunk (empty: zeros, -inf) or several chunks
+// (merge of the chunks' partial max / sum / O); one work-group per (sample, head).
+template <int D>
+__global__ __launch_bounds__(256) void pma_combine_kernel(const PmaArgs a) {
+  constexpr int NC = D / 8;
+  const int b = blockIdx.x / a.H, h = blockIdx.x - b * a.H;
+  const int c_beg = a.chunk_start[b], nch = a.chunk_start[b + 1] - c_beg;
+  if (nch == 1) return;
+  const int tid = threadIdx.x, s = tid >> 3, cb = (tid & 7) * NC;
+  if (s >= a.m) return;
+  uint16_t* op = (uint16_t*)a.o + (((size_t)b * a.m + s) * a.H + h) * D + cb;
+  float* lp = a.lse + ((size_t)b * a.m + s) * a.H + h;
+  if (nch == 0) {
+#pragma unroll
+    for (int j = 0; j < NC; j += 4) *(u32x2*)(op + j) = u32x2{};
+    if ((tid & 7) == 0) *lp = -INFINITY;
+    return;
+  }
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, a.part_ml[(((size_t)(c_beg + c) * a.H + h) * 32 + s) * 2]);
+  float L = 0.f, o[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) o[j] = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const size_t slot = (size_t)(c_beg + c) * a.H + h;
+    const float w = fast_exp2(a.part_ml[(slot * 32 + s) * 2] - M);
+    L = fmaf(a.part_ml[(slot * 32 + s) * 2 + 1], w, L);
+    const float* pp = a.part + slot * 32 * D + (size_t)s * D + cb;
+#pragma unroll
+    for (int j = 0; j < NC; j += 4) {
+      const f32x4 v = *(const f32x4*)(pp + j);
+      o[j] = fmaf(v[0], w, o[j]); o[j + 1] = fmaf(v[1], w, o[j + 1]);
+      o[j + 2] = fmaf(v[2], w, o[j + 2]); o[j + 3] = fmaf(v[3], w, o[j + 3]);
+    }
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int j = 0; j < NC; j += 4) {
+    bf16x4 v;
+    v[0] = f2bf(o[j] * inv); v[1] = f2bf(o[j + 1] * inv); v[2] = f2bf(o[j + 2] * inv); v[3] = f2bf(o[j + 3] * inv);
+    *(bf16x4*)(op + j) = v;
+  }
+  if ((tid & 7) == 0) *lp = (M + log2f(L)) * kLn2;
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
+  constexpr int KS = D / 16, DT = D / 32, TILE = kPmaBlock * D, OS = D + 4;
+  __shared__ __align__(1024) uint16_t ring[4 * TILE];  // [slot][K | V][TILE]
+  __shared__ __align__(16) uint16_t dst[4 * 32 * 32];  // per wave: dS as [token][seed]
+
+  ChunkInfo ci;
+  if (!decode_chunk(a, ci)) return;
+  const int H = a.H, h = ci.h, m = a.m;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const size_t rs = (size_t)H * D;
+  const uint16_t* Kg = (const uint16_t*)a.k + (size_t)ci.seq0 * rs + (size_t)h * D;
+  const uint16_t* Vg = (const uint16_t*)a.v + (size_t)ci.seq0 * rs + (size_t)h * D;
+  const int nblk = (ci.c1 - ci.c0 + kPmaBlock - 1) / kPmaBlock;
+
+  // Seeds and dO of (b, h), zero-padded to 32 rows, into slot 1 as tiles.
+  uint16_t* St = ring + 2 * TILE;
+  uint16_t* Dt = ring + 3 * TILE;
+  for (int i = tid; i < 32 * (D / 8); i += 256) {
+    const int s = i / (D / 8), c = i % (D / 8);
+    u32x4 sv = u32x4{}, dv = u32x4{};
+    if (s < m) {
+      sv = gload16((const uint16_t*)a.seeds + ((size_t)s * H + h) * D + 8 * c);
+      dv = gload16((const uint16_t*)a.d_o + (((size_t)ci.b * m + s) * H + h) * D + 8 * c);
+    }
+    lds_write16(St + tile_off<D>(s, c), sv);
+    lds_write16(Dt + tile_off<D>(s, c), dv);
+  }
+  pma_issue<D>(ring, ring + TILE, Kg, Vg, rs, ci.c0, ci.c1 - 1, wave, lane);
+  __syncthreads();
+
+  // Row operands, lane (s + 32 g): Seeds / dO [s][16 ks + 8 g .. + 7].
+  bf16x8 seA[KS], doA[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    seA[ks] = lds_read8(St + tile_off<D>(lr, 2 * ks + g));
+    doA[ks] = lds_read8(Dt + tile_off<D>(lr, 2 * ks + g));
+  }
+  // Column operands, lane (x + 32 g): Seeds / dO [seeds of pack_c8(., kk)][32 dt + x].
+  bf16x8 seT[2][DT], doT[2][DT];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      seT[kk][dt] = tile_cols<D>(St, 0, kk, dt, lane);
+      doT[kk][dt] = tile_cols<D>(Dt, 0, kk, dt, lane);
+    }
+  // rowsum(dO * O) and the log2-scaled LSE of seed lr; padded seeds get P = 0.
+  float dv_s = 0.f;
+  if (lr < m) {
+    const uint16_t* op = (const uint16_t*)a.o + (((size_t)ci.b * m + lr) * H + h) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 ov = gload16(op + 16 * ks);
+      const u32x4 dw = __builtin_bit_cast(u32x4, doA[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dv_s = fmaf(__uint_as_float(ov[e] << 16), __uint_as_float(dw[e] << 16), dv_s);
+        dv_s = fmaf(__uint_as_float(ov[e] & 0xffff0000u), __uint_as_float(dw[e] & 0xffff0000u), dv_s);
+      }
+    }
+  }
+  dv_s += wave_xor32(dv_s);
+  const float lse2_s = lr < m ? a.lse[((size_t)ci.b * m + lr) * H + h] * kLog2e : INFINITY;
+  // Per register of the lane = token layout: register r <-> seed 8 (r / 4) + 4 g + r % 4.
+  float lse2r[16], dvr[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int src = 8 * (r >> 2) + 4 * g + (r & 3);
+    lse2r[r] = __shfl(lse2_s, src, 64);
+    dvr[r] = __shfl(dv_s, src, 64);
+  }
+
+  const float sl2 = a.scale * kLog2e;
+  uint16_t* myds = dst + wave * 32 * 32;
+  f32x16 dSd[DT];  // dSeeds^T: lane (s + 32 g), register r <-> d = 32 dt + 8 (r / 4) + 4 g + r % 4
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dSd[dt] = f32x16{};
+  const int G = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (blk + 1 < nblk)
+      pma_issue<D>(ring + ((blk + 1) & 1) * 2 * TILE, ring + ((blk + 1) & 1) * 2 * TILE + TILE, Kg, Vg,
+                   rs, ci.c0 + (blk + 1) * kPmaBlock, ci.c1 - 1, wave, lane);
+    const uint16_t* Kt = ring + (blk & 1) * 2 * TILE;
+    const uint16_t* Vt = Kt + TILE;
+    const int tok0 = ci.c0 + blk * kPmaBlock + 32 * wave;  // sample-local
+    const int nvalid = min(32, ci.c1 - tok0);
+    if (nvalid <= 0) continue;
+    const int r0 = 32 * wave;
+
+    // S = Seeds K^T, dP = dO V^T: lane (t + 32 g), register r <-> seed 8 (r / 4) + 4 g + r % 4.
+    f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = tile_off<D>(r0 + lr, 2 * ks + g);
+      S = mfma32(seA[ks], lds_read8(Kt + off), S);
+      dP = mfma32(doA[ks], lds_read8(Vt + off), dP);
+    }
+    const bool tv = lr < nvalid;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = tv ? fast_exp2(fmaf(S[r], sl2, -lse2r[r])) : 0.f;
+      S[r] = p;
+      dP[r] = p * (dP[r] - dvr[r]);
+    }
+    const size_t grow = (size_t)(ci.seq0 + tok0 + (tv ? lr : 0)) * rs + (size_t)h * D + 4 * g;
+    // dV^T = dO^T P, dK^T = scale Seeds^T dS: lane (t + 32 g), register r <-> d = 32 dt + 8 (r / 4) + 4 g + r % 4.
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc = mfma32(doT[kk][dt], pack_c8(S, kk), acc);
+      if (tv) {
+        uint16_t* p = (uint16_t*)a.dv + grow + 32 * dt;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 v;
+          v[0] = f2bf(acc[4 * q]); v[1] = f2bf(acc[4 * q + 1]); v[2] = f2bf(acc[4 * q + 2]); v[3] = f2bf(acc[4 * q + 3]);
+          *(bf16x4*)(p + 8 * q) = v;
+        }
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc = mfma32(seT[kk][dt], pack_c8(dP, kk), acc);
+      if (tv) {
+        uint16_t* p = (uint16_t*)a.dk + grow + 32 * dt;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 v;
+          v[0] = f2bf(acc[4 * q] * a.scale); v[1] = f2bf(acc[4 * q + 1] * a.scale);
+          v[2] = f2bf(acc[4 * q + 2] * a.scale); v[3] = f2bf(acc[4 * q + 3] * a.scale);
+          *(bf16x4*)(p + 8 * q) = v;
+        }
+      }
+    }
+    // dS into the wave's tile as [token][seed]: 4-seed (8-byte) unit u of row t at u ^ ((t >> 2) & 7).
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x4 v;
+      v[0] = f2bf(dP[4 * q]); v[1] = f2bf(dP[4 * q + 1]); v[2] = f2bf(dP[4 * q + 2]); v[3] = f2bf(dP[4 * q + 3]);
+      *(GDPA_LDS bf16x4*)(myds + 32 * lr + 4 * ((2 * q + g) ^ ((lr >> 2) & 7))) = v;
+    }
+    // dSeeds^T += K^T dS^T: B = dS^T read back transposed, lane (s + 32 g) gets the
+    // tokens 16 kk + 4 g + {0..3}, 16 kk + 8 + 4 g + {0..3} of seed s.
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int R = 16 * kk + 4 * (G >> 1) + rr, u = 4 * (G & 1) + cc;
+      const bf16x8 bs = cat8(lds_read_tr4(myds + 32 * R + 4 * (u ^ ((R >> 2) & 7))),
+                             lds_read_tr4(myds + 32 * (R + 8) + 4 * (u ^ (((R + 8) >> 2) & 7))));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) dSd[dt] = mfma32(tile_cols<D>(Kt, r0, kk, dt, lane), bs, dSd[dt]);
+    }
+  }
+
+  // Sum the 4 waves' dSeeds^T and store this chunk's partial [32][D] (unscaled).
+  __syncthreads();
+  float* ob = (float*)ring;  // [4][32][OS]
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 v;
+      v[0] = dSd[dt][4 * q]; v[1] = dSd[dt][4 * q + 1]; v[2] = dSd[dt][4 * q + 2]; v[3] = dSd[dt][4 * q + 3];
+      *(GDPA_LDS f32x4*)(ob + (wave * 32 + lr) * OS + 32 * dt + 8 * q + 4 * g) = v;
+    }
+  __syncthreads();
+  constexpr int NC = D / 8;
+  const int s = tid >> 3, cb = (tid & 7) * NC;
+  float* pp = a.part + ((size_t)ci.chunk * H + h) * 32 * D + (size_t)s * D + cb;
+#pragma unroll
+  for (int j = 0; j < NC; j += 4) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = ob[s * OS + cb + j + e] + ob[(32 + s) * OS + cb + j + e] + ob[(64 + s) * OS + cb + j + e] +
+             ob[(96 + s) * OS + cb + j + e];
+    *(f32x4*)(pp + j) = v;
+  }
+}
+
+// dSeeds, first level: slice sl sums the partials of chunks sl, sl + kPmaSlices, ...
+// (4 consecutive elements of one (head, seed, d) row per thread).
+__global__ __launch_bounds__(256) void pma_reduce1_kernel(const float* __restrict__ part, const int32_t* chunk_start,
+                                                          int B, int per_chunk, float* __restrict__ part2) {
+  const int sl = blockIdx.y;
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= per_chunk) return;
+  const int nchunks = chunk_start[B];
+  f32x4 acc = f32x4{};
+  for (int c = sl; c < nchunks; c += kPmaSlices) acc += *(const f32x4*)(part + (size_t)c * per_chunk + e);
+  *(f32x4*)(part2 + (size_t)sl * per_chunk + e) = acc;
+}
+
+// dSeeds, second level: sum of the slices, times scale, into d_seeds [m][H][D] bf16.
+template <int D>
+__global__ __launch_bounds__(256) void pma_reduce2_kernel(const float* __restrict__ part2, int H, int m,
+                                                          float scale, uint16_t* __restrict__ d_seeds) {
+  const int per_chunk = H * 32 * D;
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= per_chunk) return;
+  const int hs = e / D, d = e % D, h = hs / 32, s = hs % 32;
+  if (s >= m) return;
+  f32x4 acc = f32x4{};
+  for (int sl = 0; sl < kPmaSlices; ++sl) acc += *(const f32x4*)(part2 + (size_t)sl * per_chunk + e);
+  bf16x4 v;
+  v[0] = f2bf(acc[0] * scale); v[1] = f2bf(acc[1] * scale); v[2] = f2bf(acc[2] * scale); v[3] = f2bf(acc[3] * scale);
+  *(bf16x4*)(d_seeds + ((size_t)s * H + h) * D + d) = v;
+}
+
+}  // namespace
+
+int pma_grid(int T, int B, int H) {
+  const long chunks = (long)T / kPmaChunk + B;  // >= sum_b ceil(L_b / kPmaChunk)
+  const long g = (chunks * H + 7) / 8 * 8;
+  return (int)g;
+}
+
+hipError_t launch_pma_fwd(const PmaArgs& a, int d, int grid, hipStream_t s) {
+  if (grid > 0) {
+    switch (d) {
+      case 32: hipLaunchKernelGGL(pma_fwd_kernel<32>, dim3(grid), dim3(256), 0, s, a); break;
+      case 64: hipLaunchKernelGGL(pma_fwd_kernel<64>, dim3(grid), dim3(256), 0, s, a); break;
+      case 128: hipLaunchKernelGGL(pma_fwd_kernel<128>, dim3(grid), dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const dim3 cg((unsigned)(a.B * a.H));
+  switch (d) {
+    case 32: hipLaunchKernelGGL(pma_combine_kernel<32>, cg, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(pma_combine_kernel<64>, cg, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(pma_combine_kernel<128>, cg, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pma_bwd(const PmaArgs& a, int d, int grid, float* part2, hipStream_t s) {
+  if (grid > 0) {
+    switch (d) {
+      case 32: hipLaunchKernelGGL(pma_bwd_kernel<32>, dim3(grid), dim3(256), 0, s, a); break;
+      case 64: hipLaunchKernelGGL(pma_bwd_kernel<64>, dim3(grid), dim3(256), 0, s, a); break;
+      case 128: hipLaunchKernelGGL(pma_bwd_kernel<128>, dim3(grid), dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int per_chunk = a.H * 32 * d;
+  const unsigned nb = (unsigned)((per_chunk / 4 + 255) / 256);
+  hipLaunchKernelGGL(pma_reduce1_kernel, dim3(nb, kPmaSlices), dim3(256), 0, s, a.part, a.chunk_start, a.B,
+                     per_chunk, part2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (d) {
+    case 32: hipLaunchKernelGGL(pma_reduce2_kernel<32>, dim3(nb), dim3(256), 0, s, part2, a.H, a.m, a.scale, (uint16_t*)a.d_seeds); break;
+    case 64: hipLaunchKernelGGL(pma_reduce2_kernel<64>, dim3(nb), dim3(256), 0, s, part2, a.H, a.m, a.scale, (uint16_t*)a.d_seeds); break;
+    case 128: hipLaunchKernelGGL(pma_reduce2_kernel<128>, dim3(nb), dim3(256), 0, s, part2, a.H, a.m, a.scale, (uint16_t*)a.d_seeds); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gdpa

@@ -240,3 +240,34 @@ def make_swa_inputs(length_spec: tuple, batch: int, H: int, d: int, seed: int = 
     v = draw_normal(rng, (T, H, d), dtype, math.sqrt(d))
     do = draw_normal(rng, (T, H, d), dtype)
     return SwaInputs(lengths, torch.from_numpy(off.astype(np.int32)), q, k, v, do)
+
+
+@dataclass
+class PmaInputs:
+    """Seed pooling inputs: seeds [m,H,d]; K, V [T,H,d] from the sequence; dO [B,m,H,d]."""
+    lengths: np.ndarray
+    offsets: torch.Tensor
+    seeds: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    do: torch.Tensor
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.offsets[-1])
+
+
+def make_pma_inputs(length_spec: tuple, batch: int, H: int, d: int, m: int, seed: int = 0,
+                    sharp: bool = False, dtype: str = "bf16") -> PmaInputs:
+    """Draw lengths, then seeds [m,H,d] and K [T,H,d] ~ N(0,1)/sqrt(d) (N(0,1) when sharp),
+    then V ~ N(0,1)/sqrt(d), then dO [B,m,H,d] ~ N(0,1), all rounded to `dtype`."""
+    rng = np.random.default_rng(seed)
+    lengths = draw_lengths(rng, length_spec, batch)
+    off = offsets_from_lengths(lengths)
+    T = int(off[-1])
+    qk_div = 1.0 if sharp else math.sqrt(d)
+    seeds = draw_normal(rng, (m, H, d), dtype, qk_div)
+    k = draw_normal(rng, (T, H, d), dtype, qk_div)
+    v = draw_normal(rng, (T, H, d), dtype, math.sqrt(d))
+    do = draw_normal(rng, (batch, m, H, d), dtype)
+    return PmaInputs(lengths, torch.from_numpy(off.astype(np.int32)), seeds, k, v, do)

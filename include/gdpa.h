@@ -182,6 +182,55 @@ gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, cons
                          const void* d_o, void* dq, void* dk, void* dv, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Seed pooling attention over the same jagged batch: the attention core of
+ * Pooling by Multihead Attention, whose learnable seed queries Hierarchical
+ * Seed Pooling builds on to summarise long sequences (Kunlun paper summary,
+ * section 2.2, HSP bullet; Telegram review, layer step 3).  m learned seeds
+ * [m][H][d], shared by all samples, attend over each sample's tokens K, V
+ * [T][H][d]; for sample b, seed s and head h:
+ *
+ *     s_j        = scale * < Seeds[s,h,:], K[j,h,:] >    j over the tokens of sample b
+ *     O[b,s,h,:] = sum_j softmax(s)_j V[j,h,:]
+ *
+ * O is [B][m][H][d] and lse [B][m][H] float32 (natural log).  An empty sample
+ * pools nothing: its O rows are 0 and its lse -inf.  The compression that HSP
+ * applies to the pooled seeds (SumKronLinear) has no formula on the pages and is
+ * not part of this call.  bf16 only, fp32 accumulation; head_dim in {32, 64,
+ * 128}; 1 <= m <= 32.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;         /* B >= 1 samples */
+  int32_t total_tokens;  /* T = offsets[B] >= 0 */
+  int32_t max_seqlen;    /* >= every sample length (informational) */
+  int32_t heads;         /* H >= 1 */
+  int32_t head_dim;      /* d in {32, 64, 128} */
+  int32_t seeds;         /* m, 1 .. 32 */
+  float scale;           /* finite; 1/sqrt(d) is the usual value */
+  int32_t dtype;         /* GDPA_BF16 (GDPA_F32: GDPA_ERR_UNSUPPORTED) */
+  uint32_t flags;        /* must be 0 */
+} gdpa_pma_problem;
+
+/* Workspace bytes for gdpa_pma_fwd (backward = 0) or gdpa_pma_bwd (backward != 0);
+ * 0 for an invalid problem.  About (T / 1024 + B) * H * 16 * d bytes (chunk
+ * partials in fp32). */
+size_t gdpa_pma_workspace_bytes(const gdpa_pma_problem* p, int backward);
+
+/* Forward.  seeds [m,H,d], k, v [T,H,d] in; o [B,m,H,d] and lse [B,m,H] out
+ * (overwritten; o must not alias an input; both required).  Errors as for
+ * gdpa_fwd. */
+gdpa_status gdpa_pma_fwd(const gdpa_pma_problem* p, const int32_t* offsets, const void* seeds,
+                         const void* k, const void* v, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Backward of sum(O * dO): seeds, k, v, o and lse (from gdpa_pma_fwd) and d_o
+ * [B,m,H,d] in; d_seeds [m,H,d] (summed over every sample), dk and dv [T,H,d]
+ * out (overwritten; distinct from the inputs and from each other). */
+gdpa_status gdpa_pma_bwd(const gdpa_pma_problem* p, const int32_t* offsets, const void* seeds,
+                         const void* k, const void* v, const void* o, const float* lse,
+                         const void* d_o, void* d_seeds, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Host-side check of a HOST copy of offsets: returns GDPA_OK when offsets[0] = 0,
  * the array is non-decreasing, offsets[B] = total_tokens and every length is at
  * most max_seqlen; GDPA_ERR_INVALID_ARGUMENT otherwise. */

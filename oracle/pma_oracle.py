@@ -28,7 +28,7 @@ step.
 from __future__ import annotations
 
 import math
-from typing import Optional, Tuple
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -47,8 +47,10 @@ def _check(seeds, offsets, k, v):
     return m, H, d, len(offsets) - 1
 
 
-def pma_forward(seeds, offsets, k, v, scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """(O [B,m,H,d], LSE [B,m,H]) in float64; zeros and -inf for an empty sample."""
+def pma_forward(seeds, offsets, k, v, scale: Optional[float] = None,
+                samples: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """(O [B,m,H,d], LSE [B,m,H]) in float64; zeros and -inf for an empty sample.  With
+    `samples`, only those samples are computed (the others stay NaN)."""
     seeds, k, v = as_f64(seeds), as_f64(k), as_f64(v)
     offsets = np.asarray(as_f64(offsets), dtype=np.int64)
     m, H, d, B = _check(seeds, offsets, k, v)
@@ -56,9 +58,14 @@ def pma_forward(seeds, offsets, k, v, scale: Optional[float] = None) -> Tuple[np
         scale = 1.0 / math.sqrt(d)
     o = np.zeros((B, m, H, d))
     lse = np.full((B, m, H), -np.inf)
-    for b in range(B):
+    if samples is not None:
+        o[:] = np.nan
+        lse[:] = np.nan
+    for b in (range(B) if samples is None else samples):
         r = slice(int(offsets[b]), int(offsets[b + 1]))
         if r.stop == r.start:
+            o[b] = 0.0
+            lse[b] = -np.inf
             continue
         for h in range(H):
             p, l = row_softmax(scale * (seeds[:, h, :] @ k[r, h, :].T))    # [m, L]
@@ -67,8 +74,11 @@ def pma_forward(seeds, offsets, k, v, scale: Optional[float] = None) -> Tuple[np
     return o, lse
 
 
-def pma_backward(seeds, offsets, k, v, do, scale: Optional[float] = None):
+def pma_backward(seeds, offsets, k, v, do, scale: Optional[float] = None,
+                 samples: Optional[Sequence[int]] = None):
     """Gradients of sum(O * dO): (dSeeds [m,H,d] summed over samples, dK, dV [T,H,d]).
+    With `samples`, only those samples contribute (dSeeds is their sum; the other
+    samples' dK, dV rows stay NaN).
 
     Per sample and head: dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
     dSeeds += scale dS K, dK = scale dS^T Seeds."""
@@ -78,9 +88,9 @@ def pma_backward(seeds, offsets, k, v, do, scale: Optional[float] = None):
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dseeds = np.zeros((m, H, d))
-    dk = np.zeros(k.shape)
-    dv = np.zeros(v.shape)
-    for b in range(B):
+    dk = np.zeros(k.shape) if samples is None else np.full(k.shape, np.nan)
+    dv = np.zeros(v.shape) if samples is None else np.full(v.shape, np.nan)
+    for b in (range(B) if samples is None else samples):
         r = slice(int(offsets[b]), int(offsets[b + 1]))
         if r.stop == r.start:
             continue

@@ -124,6 +124,32 @@ def test_swa_workspace_sizes(lib):
     assert W(1, window=0) == 0 and W(0, head_dim=48) == 0 and W(1, dtype=0) == 0
 
 
+def test_pma_workspace_sizes_and_checks(lib):
+    def prob(**kw):
+        f = dict(batch=3, total_tokens=3000, max_seqlen=3000, heads=2, head_dim=128, seeds=32,
+                 scale=0.1, dtype=1, flags=0)
+        f.update(kw)
+        return cca.PmaProblem(**f)
+
+    def W(backward, **kw):
+        return int(lib.gdpa_pma_workspace_bytes(ctypes.byref(prob(**kw)), backward))
+    chunks = 3000 // 1024 + 3                      # upper bound on sum_b ceil(L_b / 1024)
+    part = chunks * 2 * 32 * 128 * 4               # fp32 partials per (chunk, head)
+    assert W(0) >= part + chunks * 2 * 32 * 2 * 4 and W(0) % 256 == 0
+    assert W(1) >= part + 32 * 2 * 32 * 128 * 4     # second-level dSeeds slices
+    assert W(0, seeds=0) == 0 and W(0, seeds=33) == 0 and W(0, head_dim=48) == 0
+    assert W(1, dtype=0) == 0 and W(1, flags=1) == 0 and W(0, scale=float("inf")) == 0
+    # Invalid arguments are reported before any HIP call.
+    st = lib.gdpa_pma_fwd(ctypes.byref(prob(seeds=40)), V, V, V, V, V, V, V, 1 << 30, None)
+    assert st == 2
+    st = lib.gdpa_pma_fwd(ctypes.byref(prob()), V, V, V, V, None, V, V, 1 << 30, None)
+    assert st == 1                                  # no output
+    st = lib.gdpa_pma_fwd(ctypes.byref(prob()), V, V, V, V, ctypes.c_void_p(512), V, V, 16, None)
+    assert st == 3                                  # workspace too small
+    st = lib.gdpa_pma_bwd(ctypes.byref(prob()), V, V, V, V, V, V, V, V, V, V, V, 1 << 30, None)
+    assert st == 1                                  # outputs alias inputs
+
+
 def test_status_strings_and_offsets_check(lib):
     assert lib.gdpa_status_str(0) == b"GDPA_OK"
     assert lib.gdpa_status_str(3) == b"GDPA_ERR_WORKSPACE_TOO_SMALL"

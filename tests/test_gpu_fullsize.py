@@ -155,3 +155,41 @@ def test_fullsize_swa(gdpa_lib):
     say("  errors:", {n_: f"{e:.2e}" for n_, e in errs.items()})
     for name, e in errs.items():
         assert e <= TOL["bf16"], (name, e)
+
+
+def test_fullsize_pma(gdpa_lib):
+    """Seed pooling attention at the size `bench.py --op pma` times (the stacked
+    workload's batch: B=1024, lengths log-normal median 1024 max 8192, H=8, d=128;
+    32 seeds).  O, LSE, dK, dV on sampled samples; dSeeds from a second backward
+    whose dO is zero outside the sampled samples (samples contribute independently)."""
+    from oracle import pma_oracle as pmo
+    cca = gdpa_lib
+    cfg = gi.CONFIGS[5]
+    m = 32
+    inp = gi.make_pma_inputs(cfg.lengths, cfg.batch, cfg.heads, cfg.head_dim, m, seed=0)
+    samples = pick_samples(inp.lengths)
+    say(f"case: pma m={m} T={inp.total_tokens} samples={samples} "
+        f"(lengths {[int(inp.lengths[b]) for b in samples]})")
+    seeds, k, v, do = (t.cuda() for t in (inp.seeds, inp.k, inp.v, inp.do))
+    off = inp.offsets.cuda()
+    o, lse = cca.pma_fwd(seeds, off, k, v)
+    ds, dk, dv = cca.pma_bwd(seeds, off, k, v, o, lse, do)
+    sel = torch.zeros(cfg.batch, dtype=torch.bool)
+    sel[samples] = True
+    do_sel = torch.where(sel.view(-1, 1, 1, 1), inp.do, torch.zeros_like(inp.do))
+    ds_sel, _, _ = cca.pma_bwd(seeds, off, k, v, o, lse, do_sel.cuda())
+    torch.cuda.synchronize()
+    rows = rows_of(inp.offsets, samples)
+    sub_len = [int(inp.lengths[b]) for b in samples]
+    sub_off = np.concatenate([[0], np.cumsum(sub_len)])
+    idx = torch.from_numpy(rows)
+    sidx = torch.tensor(samples)
+    o_ref, lse_ref = pmo.pma_forward(inp.seeds, sub_off, inp.k[idx], inp.v[idx])
+    ds_ref, dk_ref, dv_ref = pmo.pma_backward(inp.seeds, sub_off, inp.k[idx], inp.v[idx], inp.do[sidx])
+    errs = {"o": max_abs_rel(o[sidx.cuda()].cpu(), o_ref), "lse": max_abs_rel(lse[sidx.cuda()].cpu(), lse_ref),
+            "dseeds": max_abs_rel(ds_sel, ds_ref), "dk": max_abs_rel(gather(dk, rows), dk_ref),
+            "dv": max_abs_rel(gather(dv, rows), dv_ref)}
+    say("  errors:", {n_: f"{e:.2e}" for n_, e in errs.items()})
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (name, e)
+    assert torch.isfinite(ds.float()).all()
