@@ -54,9 +54,11 @@ def parse():
     ap.add_argument("--phi", default=None, choices=[None, "softmax", "silu", "relu", "gelu", "identity"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="gdpa", choices=["gdpa", "swa"],
-                    help="swa: sliding-window self-attention on the stacked workload's batch")
+    ap.add_argument("--op", default="gdpa", choices=["gdpa", "swa", "pma"],
+                    help="swa: sliding-window self-attention on the stacked workload's batch; "
+                         "pma: seed pooling attention over that batch")
     ap.add_argument("--window", type=int, default=512, help="window of --op swa")
+    ap.add_argument("--seeds", type=int, default=32, help="seeds of --op pma (1..32)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
@@ -329,6 +331,107 @@ def run_swa(args):
 
 
 # ---------------------------------------------------------------------------
+# seed pooling attention (--op pma)
+# ---------------------------------------------------------------------------
+
+def pma_units(T, B, H, d, m):
+    """(flops, algorithmic HBM bytes) of the forward and the backward calls."""
+    tok = T * H * d * 2                       # one bf16 [T,H,d] tensor
+    pooled = B * m * H * d * 2                # one bf16 [B,m,H,d] tensor
+    small = m * H * d * 2 + B * m * H * 4     # seeds, LSE
+    fwd = (4.0 * m * d * H * T, 2 * tok + pooled + small)
+    bwd = (10.0 * m * d * H * T, 4 * tok + 2 * pooled + small + m * H * d * 2)
+    return fwd, bwd
+
+
+def run_pma(args):
+    import torch
+
+    import context_cross_attention_amd as cca
+    import gdpa_inputs as gi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cca.load()
+    cfg = gi.CONFIGS[5]
+    m = args.seeds
+    H, d, B = cfg.heads, cfg.head_dim, cfg.batch
+    inp = gi.make_pma_inputs(cfg.lengths, B, H, d, m, seed=args.seed)
+    T = inp.total_tokens
+    seeds, k, v, do = (t.cuda() for t in (inp.seeds, inp.k, inp.v, inp.do))
+    off = inp.offsets.cuda()
+    o = torch.empty((B, m, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, m, H), dtype=torch.float32, device="cuda")
+    dseeds, dk, dv = torch.empty_like(seeds), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(cca.pma_workspace_bytes(seeds, off, k, True), dtype=torch.uint8, device="cuda")
+    marks = Marks(torch)
+
+    def step():
+        marks("pma_fwd", True)
+        cca.pma_fwd(seeds, off, k, v, out=o, lse=lse, workspace=ws)
+        marks("pma_fwd", False)
+        marks("pma_bwd", True)
+        cca.pma_bwd(seeds, off, k, v, o, lse, do, d_seeds=dseeds, dk=dk, dv=dv, workspace=ws)
+        marks("pma_bwd", False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks.enabled = True
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    marks.enabled = False
+    (f_fwd, b_fwd), (f_bwd, b_bwd) = pma_units(T, B, H, d, m)
+    units = {"pma_fwd": (f_fwd, b_fwd), "pma_bwd": (f_bwd, b_bwd)}
+    totals, counts = marks.totals_ms(), marks.counts()
+    dom = max(totals, key=lambda x: totals[x])
+    t_dom = totals[dom] / counts[dom] * 1e-3
+    f_dom, b_dom = units[dom]
+    roof = {"bound": "hbm", "achieved": round(b_dom / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, kernel=dom,
+                launch_ms=round(totals[dom] / counts[dom], 4),
+                algorithmic_per_launch={"flops": f_dom, "bytes": b_dom},
+                other_bound_frac=round(f_dom / t_dom / 1e12 / PEAK_BF16_TFLOPS, 4))
+    value = (b_fwd + b_bwd) / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": "seed pooling attention fwd+bwd, algorithmic HBM GB/s, jagged batch, 1 MI355X",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws as in gdpa_inputs.make_pma_inputs)",
+        "config": {"workload": f"seed pooling attention fwd+bwd, {m} seeds: B={B} samples, lengths "
+                               f"log-normal (median {cfg.lengths[1]}, max {cfg.lengths[2]}), T={T}, H={H}, d={d}",
+                   "seeds": m, "tokens": T, "heads": H, "head_dim": d, "seed": args.seed},
+        "tflops": round((f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12, 2),
+        "breakdown_ms_per_step": {x: round(totals[x] / args.steps, 4) for x in totals},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import pma_oracle as pmo
+        chosen, toks = [], 0
+        for b in range(B):
+            if inp.lengths[b] == 0:
+                continue
+            chosen.append(b)
+            toks += int(inp.lengths[b])
+            if toks >= 600000:
+                break
+        t1 = time.perf_counter()
+        pmo.pma_forward(inp.seeds, inp.offsets, inp.k, inp.v, samples=chosen)
+        pmo.pma_backward(inp.seeds, inp.offsets, inp.k, inp.v, inp.do, samples=chosen)
+        dt = time.perf_counter() - t1
+        (_, bf), (_, bb) = pma_units(toks, len(chosen), H, d, m)
+        out["cpu_baseline"] = {"value": round((bf + bb) / dt / 1e9, 3), "unit": "GB/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"fwd+bwd on samples {chosen[0]}..{chosen[-1]} ({len(chosen)} of {B}, "
+                                         f"{toks} tokens); {(bf + bb) / 1e9:.2f} GB algorithmic in {dt:.1f} s "
+                                         f"(numpy float64)", "seconds": round(dt, 2)}
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
 
@@ -346,6 +449,9 @@ def main():
         return
     if args.op == "swa":
         run_swa(args)
+        return
+    if args.op == "pma":
+        run_pma(args)
         return
 
     import numpy as np
