@@ -31,10 +31,10 @@ CFLAGS = [
 ]
 SOURCES = ["gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_fwd_res.hip", "gdpa_bwd.hip", "gdpa_bwd_res.hip",
            "gdpa_bwd_dq.hip", "gdpa_gemm.hip", "gdpa_pma.hip", "gdpa_api.cpp"]
-# Per-source extra flags.  The backward kernel keeps 256 fp32 accumulators per lane
-# in AGPRs for the whole sample; selecting the VGPR form of MFMA for everything else
-# (the per-step score tiles) keeps those accumulators resident instead of spilled.
-EXTRA_FLAGS = {}
+# Per-source extra flags.  The seed pooling kernels touch their MFMA results with
+# VALU code every block (softmax, bf16 packing, rescale); with the VGPR form of
+# MFMA the compiler keeps them in VGPRs instead of copying them out of AGPRs.
+EXTRA_FLAGS = {"gdpa_pma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -8,12 +8,13 @@
 // bf16 in and out, fp32 accumulation, d in {32, 64, 128}, m <= 32.
 //
 // Work: one work-group (4 waves) per (chunk of up to kPmaChunk tokens of one
-// sample, head).  The 32 (zero-padded) seeds stay in registers as MFMA operands;
-// K and V stream through a 2-stage LDS ring of 128-token blocks, filled by
-// global->LDS DMA one block ahead; wave w takes tokens 32 w .. 32 w + 31 of each
-// block.  Per byte of K/V the operation does at most m flops, far below the
-// MFMA/HBM balance point of the chip, so the kernels are organised around
-// keeping HBM busy; the MFMA work hides under the copies.
+// sample, head).  The 32 (zero-padded) seeds stay in registers as MFMA operands.
+// Wave w takes the chunk's 32-token blocks w, w + 4, w + 8, ... and streams them
+// through two LDS slots of its own, filled by global->LDS DMA two blocks ahead;
+// the waves never wait for each other inside the loop, so each slot is in flight
+// except while its wave computes on it.  Per byte of K/V the operation does at
+// most m flops, far below the MFMA/HBM balance point of the chip, so the kernels
+// are organised around keeping HBM busy; the MFMA work hides under the copies.
 //
 // LDS tiles are dense row-major [rows][d] bf16 with the 16-byte chunks of a row
 // permuted (chunk c of row r stored at position c ^ swz(r)), so that both the
@@ -35,7 +36,7 @@ namespace gdpa {
 
 namespace {
 
-constexpr int kPmaBlock = 128;  // tokens per LDS stage
+constexpr int kPmaBlock = 32;  // tokens per LDS slot (one wave's MFMA tile)
 
 // Chunk position permutation of a [rows][D] tile (see the header comment).
 template <int D>
@@ -50,22 +51,31 @@ __device__ __forceinline__ int tile_off(int row, int c) {
   return row * D + 8 * (c ^ pma_swz<D>(row));
 }
 
-// DMA of tokens tok0 .. tok0 + 127 (rows past `last` repeat row `last`, so
-// every row holds finite data) of K and V into the tiles Kt, Vt.  Kg / Vg point
-// at token 0 of the sample, head h; rs is the token stride in elements.
+// DMA of tokens tok0 .. tok0 + 31 (rows past `last` repeat row `last`, so every
+// row holds finite data) of K and V into the [32][D] tiles Kt, Vt, by one wave.
+// Kg / Vg point at token 0 of the sample, head h; rs is the token stride in
+// elements.  D / 8 copies of 1 KiB, tracked by the wave's vmcnt.
 template <int D>
 __device__ __forceinline__ void pma_issue(uint16_t* Kt, uint16_t* Vt, const uint16_t* Kg,
-                                          const uint16_t* Vg, size_t rs, int tok0, int last,
-                                          int wave, int lane) {
+                                          const uint16_t* Vg, size_t rs, int tok0, int last, int lane) {
   constexpr int NQ = kPmaBlock * D / 512;  // 1 KiB wave copies per tensor
 #pragma unroll
-  for (int q = wave; q < NQ; q += 4) {
+  for (int q = 0; q < NQ; ++q) {
     const int e = q * 512 + 8 * lane;
     const int row = e / D, pos = (e % D) / 8;
     const size_t src = (size_t)min(tok0 + row, last) * rs + 8 * (pos ^ pma_swz<D>(row));
     dma16(__builtin_amdgcn_readfirstlane(lds_addr(Kt + q * 512)), Kg + src);
     dma16(__builtin_amdgcn_readfirstlane(lds_addr(Vt + q * 512)), Vg + src);
   }
+}
+
+// Waits until the wave's older slot has landed: at most N copies outstanding
+// (N = those of the newer slot, or 0), then keeps the compiler from moving LDS
+// reads of the slot above the wait.
+template <int N>
+__device__ __forceinline__ void slot_wait() {
+  wait_vmcnt<N>();
+  asm volatile("" ::: "memory");
 }
 
 // A operand of a [32][D] (or wider) tile read column-wise: lane (x + 32 g) gets
@@ -101,8 +111,8 @@ __device__ __forceinline__ bool decode_chunk(const PmaArgs& a, ChunkInfo& ci) {
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void pma_fwd_kernel(const PmaArgs a) {
-  constexpr int KS = D / 16, DT = D / 32, TILE = kPmaBlock * D, OS = D + 4;
-  __shared__ __align__(1024) uint16_t ring[4 * TILE];  // [slot][K | V][TILE]
+  constexpr int KS = D / 16, DT = D / 32, TS = kPmaBlock * D, OS = D + 4, NPB = D / 8;
+  __shared__ __align__(1024) uint16_t ring[16 * TS];  // [wave][slot][K | V][TS]
 
   ChunkInfo ci;
   if (!decode_chunk(a, ci)) return;
@@ -111,16 +121,23 @@ __global__ __launch_bounds__(256, 1) void pma_fwd_kernel(const PmaArgs a) {
   const size_t rs = (size_t)H * D;
   const uint16_t* Kg = (const uint16_t*)a.k + (size_t)ci.seq0 * rs + (size_t)h * D;
   const uint16_t* Vg = (const uint16_t*)a.v + (size_t)ci.seq0 * rs + (size_t)h * D;
-  const int nblk = (ci.c1 - ci.c0 + kPmaBlock - 1) / kPmaBlock;
-  pma_issue<D>(ring, ring + TILE, Kg, Vg, rs, ci.c0, ci.c1 - 1, wave, lane);
+  const int len = ci.c1 - ci.c0, last = ci.c1 - 1;
+  const int nb = (len + kPmaBlock - 1) / kPmaBlock;  // 32-token blocks; this wave takes wave, wave + 4, ...
+  uint16_t* my = ring + wave * 4 * TS;
+  if (wave < nb) pma_issue<D>(my, my + TS, Kg, Vg, rs, ci.c0 + kPmaBlock * wave, last, lane);
 
-  // Seeds as B operands: lane (s + 32 g) holds Seeds[s][16 ks + 8 g .. + 7].
+  // Seeds as B operands: lane (s + 32 g) holds Seeds[s][16 ks + 8 g .. + 7].  They
+  // are waited for here, before the second slot's copies are issued, so that no
+  // wait for them is left inside the loop (it would also wait for every copy).
   bf16x8 sb[KS];
   {
     const uint16_t* sp = (const uint16_t*)a.seeds + ((size_t)(lr < a.m ? lr : 0) * H + h) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) sb[ks] = lr < a.m ? as_bf16x8(gload16(sp + 16 * ks)) : bf16x8{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(sb[ks]));
   }
+  if (wave + 4 < nb) pma_issue<D>(my + 2 * TS, my + 3 * TS, Kg, Vg, rs, ci.c0 + kPmaBlock * (wave + 4), last, lane);
 
   const float sl2 = a.scale * kLog2e;
   float m_run = -INFINITY, l_run = 0.f;
@@ -128,22 +145,16 @@ __global__ __launch_bounds__(256, 1) void pma_fwd_kernel(const PmaArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
 
-  for (int blk = 0; blk < nblk; ++blk) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (blk + 1 < nblk)
-      pma_issue<D>(ring + ((blk + 1) & 1) * 2 * TILE, ring + ((blk + 1) & 1) * 2 * TILE + TILE, Kg, Vg,
-                   rs, ci.c0 + (blk + 1) * kPmaBlock, ci.c1 - 1, wave, lane);
-    const uint16_t* Kt = ring + (blk & 1) * 2 * TILE;
-    const uint16_t* Vt = Kt + TILE;
-    const int nvalid = min(32, ci.c1 - (ci.c0 + blk * kPmaBlock + 32 * wave));
-    if (nvalid <= 0) continue;
-    const int r0 = 32 * wave;
+  for (int i = 0, j = wave; j < nb; ++i, j += 4) {
+    if (j + 4 < nb) slot_wait<NPB>(); else slot_wait<0>();
+    uint16_t* Kt = my + (i & 1) * 2 * TS;
+    const uint16_t* Vt = Kt + TS;
+    const int nvalid = min(kPmaBlock, len - kPmaBlock * j);
 
     // S^T[t][s]: lane (s + 32 g), register r <-> token 8 (r / 4) + 4 g + r % 4.
     f32x16 S = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) S = mfma32(lds_read8(Kt + tile_off<D>(r0 + lr, 2 * ks + g)), sb[ks], S);
+    for (int ks = 0; ks < KS; ++ks) S = mfma32(lds_read8(Kt + tile_off<D>(lr, 2 * ks + g)), sb[ks], S);
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -151,25 +162,32 @@ __global__ __launch_bounds__(256, 1) void pma_fwd_kernel(const PmaArgs a) {
       S[r] = t < nvalid ? S[r] * sl2 : -INFINITY;
       mx = fmaxf(mx, S[r]);
     }
-    mx = fmaxf(mx, wave_xor32(mx));
-    const float m_new = fmaxf(m_run, mx);  // finite: token 0 of the block is valid
-    const float alpha = fast_exp2(m_run - m_new);
+    mx = fmaxf(mx, wave_xor32(mx));  // finite: token 0 of the block is valid
+    // Lazy rescale: the reference maximum moves only when a score exceeds it by
+    // more than 2^8, so P <= 256 and the O / l rescale is rare (first block).
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+      m_run = m_new;
+    }
     float ls = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      S[r] = fast_exp2(S[r] - m_new);
+      S[r] = fast_exp2(S[r] - m_run);
       ls += S[r];
     }
-    l_run = fmaf(l_run, alpha, ls);
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[dt] *= alpha;
+    l_run += ls;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const bf16x8 pb = pack_c8(S, kk);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[dt] = mfma32(tile_cols<D>(Vt, r0, kk, dt, lane), pb, O[dt]);
+      for (int dt = 0; dt < DT; ++dt) O[dt] = mfma32(tile_cols<D>(Vt, 0, kk, dt, lane), pb, O[dt]);
     }
+    // The slot's LDS reads have completed (their data fed the MFMAs): refill it.
+    if (j + 8 < nb) pma_issue<D>(Kt, Kt + TS, Kg, Vg, rs, ci.c0 + kPmaBlock * (j + 8), last, lane);
   }
 
   // Merge the 4 waves' (max, sum, O) per seed through LDS (the ring is free).
@@ -285,9 +303,10 @@ __global__ __launch_bounds__(256) void pma_combine_kernel(const PmaArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
-  constexpr int KS = D / 16, DT = D / 32, TILE = kPmaBlock * D, OS = D + 4;
-  __shared__ __align__(1024) uint16_t ring[4 * TILE];  // [slot][K | V][TILE]
-  __shared__ __align__(16) uint16_t dst[4 * 32 * 32];  // per wave: dS as [token][seed]
+  constexpr int KS = D / 16, DT = D / 32, TS = kPmaBlock * D, OS = D + 4, NPB = D / 8;
+  __shared__ __align__(1024) uint16_t ring[16 * TS];      // [wave][slot][K | V][TS]
+  __shared__ __align__(16) uint16_t sdt[2 * TS];          // Seeds and dO of (b, h) as [32][D] tiles
+  __shared__ __align__(16) uint16_t dst[4 * 32 * 32];     // per wave: dS as [token][seed]
 
   ChunkInfo ci;
   if (!decode_chunk(a, ci)) return;
@@ -296,11 +315,16 @@ __global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
   const size_t rs = (size_t)H * D;
   const uint16_t* Kg = (const uint16_t*)a.k + (size_t)ci.seq0 * rs + (size_t)h * D;
   const uint16_t* Vg = (const uint16_t*)a.v + (size_t)ci.seq0 * rs + (size_t)h * D;
-  const int nblk = (ci.c1 - ci.c0 + kPmaBlock - 1) / kPmaBlock;
+  const int len = ci.c1 - ci.c0, last = ci.c1 - 1;
+  const int nb = (len + kPmaBlock - 1) / kPmaBlock;  // 32-token blocks; this wave takes wave, wave + 4, ...
+  uint16_t* my = ring + wave * 4 * TS;
+  if (wave < nb) pma_issue<D>(my, my + TS, Kg, Vg, rs, ci.c0 + kPmaBlock * wave, last, lane);
 
-  // Seeds and dO of (b, h), zero-padded to 32 rows, into slot 1 as tiles.
-  uint16_t* St = ring + 2 * TILE;
-  uint16_t* Dt = ring + 3 * TILE;
+  // Seeds and dO of (b, h), zero-padded to 32 rows.  The set-up's loads wait for
+  // the first slot's copies too (they were issued earlier); the second slot's
+  // copies are issued after the set-up so that no wait inside the loop covers them.
+  uint16_t* St = sdt;
+  uint16_t* Dt = sdt + TS;
   for (int i = tid; i < 32 * (D / 8); i += 256) {
     const int s = i / (D / 8), c = i % (D / 8);
     u32x4 sv = u32x4{}, dv = u32x4{};
@@ -311,7 +335,6 @@ __global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
     lds_write16(St + tile_off<D>(s, c), sv);
     lds_write16(Dt + tile_off<D>(s, c), dv);
   }
-  pma_issue<D>(ring, ring + TILE, Kg, Vg, rs, ci.c0, ci.c1 - 1, wave, lane);
   __syncthreads();
 
   // Row operands, lane (s + 32 g): Seeds / dO [s][16 ks + 8 g .. + 7].
@@ -356,6 +379,9 @@ __global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
     dvr[r] = __shfl(dv_s, src, 64);
   }
 
+  asm volatile("" :: "v"(dv_s), "v"(lse2_s));
+  if (wave + 4 < nb) pma_issue<D>(my + 2 * TS, my + 3 * TS, Kg, Vg, rs, ci.c0 + kPmaBlock * (wave + 4), last, lane);
+
   const float sl2 = a.scale * kLog2e;
   uint16_t* myds = dst + wave * 32 * 32;
   f32x16 dSd[DT];  // dSeeds^T: lane (s + 32 g), register r <-> d = 32 dt + 8 (r / 4) + 4 g + r % 4
@@ -363,18 +389,15 @@ __global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
   for (int dt = 0; dt < DT; ++dt) dSd[dt] = f32x16{};
   const int G = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
 
-  for (int blk = 0; blk < nblk; ++blk) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (blk + 1 < nblk)
-      pma_issue<D>(ring + ((blk + 1) & 1) * 2 * TILE, ring + ((blk + 1) & 1) * 2 * TILE + TILE, Kg, Vg,
-                   rs, ci.c0 + (blk + 1) * kPmaBlock, ci.c1 - 1, wave, lane);
-    const uint16_t* Kt = ring + (blk & 1) * 2 * TILE;
-    const uint16_t* Vt = Kt + TILE;
-    const int tok0 = ci.c0 + blk * kPmaBlock + 32 * wave;  // sample-local
-    const int nvalid = min(32, ci.c1 - tok0);
-    if (nvalid <= 0) continue;
-    const int r0 = 32 * wave;
+  for (int i = 0, j = wave; j < nb; ++i, j += 4) {
+    // Outstanding after the older slot's copies: the newer slot's and this wave's
+    // earlier dK / dV stores; waiting for those too is the conservative choice.
+    if (j + 4 < nb) slot_wait<NPB>(); else slot_wait<0>();
+    uint16_t* Kt = my + (i & 1) * 2 * TS;
+    const uint16_t* Vt = Kt + TS;
+    const int tok0 = ci.c0 + kPmaBlock * j;  // sample-local
+    const int nvalid = min(kPmaBlock, ci.c1 - tok0);
+    const int r0 = 0;
 
     // S = Seeds K^T, dP = dO V^T: lane (t + 32 g), register r <-> seed 8 (r / 4) + 4 g + r % 4.
     f32x16 S = f32x16{}, dP = f32x16{};
@@ -391,37 +414,20 @@ __global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
       S[r] = p;
       dP[r] = p * (dP[r] - dvr[r]);
     }
-    const size_t grow = (size_t)(ci.seq0 + tok0 + (tv ? lr : 0)) * rs + (size_t)h * D + 4 * g;
     // dV^T = dO^T P, dK^T = scale Seeds^T dS: lane (t + 32 g), register r <-> d = 32 dt + 8 (r / 4) + 4 g + r % 4.
+    // Both go out through the slot's own tiles (V is no longer needed once dP is
+    // formed, K once the dSeeds products have read it), as whole rows.
+    uint16_t* Vw = Kt + TS;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) acc = mfma32(doT[kk][dt], pack_c8(S, kk), acc);
-      if (tv) {
-        uint16_t* p = (uint16_t*)a.dv + grow + 32 * dt;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bf16x4 v;
-          v[0] = f2bf(acc[4 * q]); v[1] = f2bf(acc[4 * q + 1]); v[2] = f2bf(acc[4 * q + 2]); v[3] = f2bf(acc[4 * q + 3]);
-          *(bf16x4*)(p + 8 * q) = v;
-        }
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) acc = mfma32(seT[kk][dt], pack_c8(dP, kk), acc);
-      if (tv) {
-        uint16_t* p = (uint16_t*)a.dk + grow + 32 * dt;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bf16x4 v;
-          v[0] = f2bf(acc[4 * q] * a.scale); v[1] = f2bf(acc[4 * q + 1] * a.scale);
-          v[2] = f2bf(acc[4 * q + 2] * a.scale); v[3] = f2bf(acc[4 * q + 3] * a.scale);
-          *(bf16x4*)(p + 8 * q) = v;
-        }
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+        v[0] = f2bf(acc[4 * q]); v[1] = f2bf(acc[4 * q + 1]); v[2] = f2bf(acc[4 * q + 2]); v[3] = f2bf(acc[4 * q + 3]);
+        *(GDPA_LDS bf16x4*)(Vw + tile_off<D>(lr, 4 * dt + q) + 4 * g) = v;
       }
     }
     // dS into the wave's tile as [token][seed]: 4-seed (8-byte) unit u of row t at u ^ ((t >> 2) & 7).
@@ -441,6 +447,38 @@ __global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) dSd[dt] = mfma32(tile_cols<D>(Kt, r0, kk, dt, lane), bs, dSd[dt]);
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc = mfma32(seT[kk][dt], pack_c8(dP, kk), acc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x4 v;
+        v[0] = f2bf(acc[4 * q] * a.scale); v[1] = f2bf(acc[4 * q + 1] * a.scale);
+        v[2] = f2bf(acc[4 * q + 2] * a.scale); v[3] = f2bf(acc[4 * q + 3] * a.scale);
+        *(GDPA_LDS bf16x4*)(Kt + tile_off<D>(lr, 4 * dt + q) + 4 * g) = v;
+      }
+    }
+    // Rows out: lane l takes 16-byte chunk l % (D / 8) of row RPI i + l / (D / 8).
+    {
+      constexpr int CH = D / 8, RPI = 64 / CH;
+      const int c = lane % CH;
+      uint16_t* dvg = (uint16_t*)a.dv + (size_t)(ci.seq0 + tok0) * rs + (size_t)h * D + 8 * c;
+      uint16_t* dkg = (uint16_t*)a.dk + (size_t)(ci.seq0 + tok0) * rs + (size_t)h * D + 8 * c;
+#pragma unroll
+      for (int i2 = 0; i2 < 32 / RPI; ++i2) {
+        const int row = RPI * i2 + lane / CH;
+        const u32x4 vv = __builtin_bit_cast(u32x4, lds_read8(Vw + tile_off<D>(row, c)));
+        const u32x4 kv = __builtin_bit_cast(u32x4, lds_read8(Kt + tile_off<D>(row, c)));
+        if (row < nvalid) {
+          *(u32x4*)(dvg + (size_t)row * rs) = vv;
+          *(u32x4*)(dkg + (size_t)row * rs) = kv;
+        }
+      }
+    }
+    // The slot's LDS reads have completed (their data fed the MFMAs): refill it.
+    if (j + 8 < nb) pma_issue<D>(Kt, Kt + TS, Kg, Vg, rs, ci.c0 + kPmaBlock * (j + 8), last, lane);
   }
 
   // Sum the 4 waves' dSeeds^T and store this chunk's partial [32][D] (unscaled).
