@@ -383,22 +383,24 @@ gdpa_status check_pma(const gdpa_pma_problem* p) {
   if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) return GDPA_ERR_UNSUPPORTED;
   if (p->seeds > 32 || p->dtype != GDPA_BF16 || p->flags != 0) return GDPA_ERR_UNSUPPORTED;
   // Work-group ids: (chunks upper bound) x heads must fit a grid dimension.
-  if (((int64_t)p->total_tokens / gdpa::kPmaChunk + p->batch) * p->heads + 8 > INT32_MAX)
+  if (((int64_t)p->total_tokens / 1024 + p->batch) * p->heads + 8 > INT32_MAX)
     return GDPA_ERR_UNSUPPORTED;
   return GDPA_OK;
 }
 
-// Workspace: chunk_start [B+1] int32 | part [chunks][H][32][d] fp32 | forward:
-// part_ml [chunks][H][32][2] fp32, backward: part2 [slices][H][32][d] fp32.
+// Workspace: order [B] int32 | chunk_start [B+1] int32 | part [chunks][H][32][d]
+// fp32 | forward: part_ml [chunks][H][32][2] fp32, backward: part2 [slices][H][32][d] fp32.
 struct PmaPlan {
-  size_t chunk_off, part_off, extra_off, total;
+  size_t order_off, chunk_off, part_off, extra_off, total;
 };
 
 PmaPlan pma_plan(const gdpa_pma_problem* p, bool backward) {
   PmaPlan pl{};
-  const size_t chunks = (size_t)p->total_tokens / gdpa::kPmaChunk + p->batch;
+  const size_t chunks = (size_t)p->total_tokens / gdpa::pma_chunk(p->total_tokens, p->heads) + p->batch;
   const size_t per_chunk = (size_t)p->heads * 32 * p->head_dim;
   size_t off = 0;
+  pl.order_off = off;
+  off += align_up(sizeof(int32_t) * (size_t)p->batch);
   pl.chunk_off = off;
   off += align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
   pl.part_off = off;
@@ -413,13 +415,25 @@ PmaPlan pma_plan(const gdpa_pma_problem* p, bool backward) {
 gdpa::PmaArgs pma_args(const gdpa_pma_problem* p, const int32_t* offsets, char* ws, const PmaPlan& pl) {
   gdpa::PmaArgs a{};
   a.offsets = offsets;
+  a.order = (const int32_t*)(ws + pl.order_off);
   a.chunk_start = (const int32_t*)(ws + pl.chunk_off);
   a.part = (float*)(ws + pl.part_off);
   a.B = p->batch;
   a.H = p->heads;
   a.m = p->seeds;
   a.scale = p->scale;
+  a.chunk = gdpa::pma_chunk(p->total_tokens, p->heads);
   return a;
+}
+
+// Longest-first sample order and the chunk prefix sums over it.
+hipError_t pma_schedule(const gdpa_pma_problem* p, const int32_t* offsets, char* ws, const PmaPlan& pl,
+                        hipStream_t s) {
+  int32_t* order = (int32_t*)(ws + pl.order_off);
+  const hipError_t e = gdpa::launch_longest_first(offsets, p->batch, order, s);
+  if (e != hipSuccess) return e;
+  return gdpa::launch_tile_scan(offsets, p->batch, gdpa::pma_chunk(p->total_tokens, p->heads),
+                                (int32_t*)(ws + pl.chunk_off), s, order);
 }
 
 }  // namespace
@@ -451,9 +465,9 @@ gdpa_status gdpa_pma_fwd(const gdpa_pma_problem* p, const int32_t* offsets, cons
   a.o = o;
   a.lse = lse;
   a.part_ml = (float*)(ws + pl.extra_off);
-  hipError_t e = gdpa::launch_tile_scan(offsets, p->batch, gdpa::kPmaChunk, (int32_t*)(ws + pl.chunk_off), s);
+  hipError_t e = pma_schedule(p, offsets, ws, pl, s);
   if (e != hipSuccess) return hip_status(e);
-  const int grid = p->total_tokens > 0 ? gdpa::pma_grid(p->total_tokens, p->batch, p->heads) : 0;
+  const int grid = p->total_tokens > 0 ? gdpa::pma_grid(p->total_tokens, p->batch, p->heads, a.chunk) : 0;
   return hip_status(gdpa::launch_pma_fwd(a, p->head_dim, grid, s));
 }
 
@@ -490,9 +504,9 @@ gdpa_status gdpa_pma_bwd(const gdpa_pma_problem* p, const int32_t* offsets, cons
   a.d_seeds = d_seeds;
   a.dk = dk;
   a.dv = dv;
-  hipError_t e = gdpa::launch_tile_scan(offsets, p->batch, gdpa::kPmaChunk, (int32_t*)(ws + pl.chunk_off), s);
+  hipError_t e = pma_schedule(p, offsets, ws, pl, s);
   if (e != hipSuccess) return hip_status(e);
-  const int grid = p->total_tokens > 0 ? gdpa::pma_grid(p->total_tokens, p->batch, p->heads) : 0;
+  const int grid = p->total_tokens > 0 ? gdpa::pma_grid(p->total_tokens, p->batch, p->heads, a.chunk) : 0;
   return hip_status(gdpa::launch_pma_bwd(a, p->head_dim, grid, (float*)(ws + pl.extra_off), s));
 }
 

@@ -72,8 +72,10 @@ struct BwdArgs {
 };
 
 // Scheduling and small passes (gdpa_sched.hip).
+// Prefix sums of ceil(len / tile_rows) over the samples in index order, or in the
+// order order[0..B-1] when `order` is given.
 hipError_t launch_tile_scan(const int32_t* offsets, int B, int tile_rows, int32_t* tile_start,
-                            hipStream_t s);
+                            hipStream_t s, const int32_t* order = nullptr);
 hipError_t launch_longest_first(const int32_t* offsets, int B, int32_t* order, hipStream_t s);
 hipError_t launch_softmax_dvec(const void* o, const void* d_o, int rows, int d, bool bf16,
                                float* dvec, hipStream_t s);
@@ -98,14 +100,22 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, int d, int phi, int waves, bool wit
 hipError_t launch_bwd_dq(const BwdArgs& a, int d, int phi, bool sliding_window, int grid, hipStream_t s);
 
 // Seed pooling attention (gdpa_pma.hip): m <= 32 seeds [m,H,d] attend over each
-// sample's tokens K, V [T,H,d].  One work-group per (chunk of kPmaChunk tokens,
-// head) over a grid of pma_grid(T, B, H) (an upper bound; surplus work-groups
-// exit); chunk_start[B+1] holds the prefix sums of ceil(L_b / kPmaChunk).
-constexpr int kPmaChunk = 1024;
+// sample's tokens K, V [T,H,d].  One single-wave work-group per (chunk of
+// a.chunk tokens, head) over a grid of pma_grid(T, B, H, chunk) (an upper bound;
+// surplus work-groups exit).  Samples are visited longest first: order[B]
+// (launch_longest_first) and chunk_start[B+1], the prefix sums of
+// ceil(L / chunk) over that order.
 constexpr int kPmaSlices = 32;  // first-level slices of the dSeeds reduction
+// Chunk length for T tokens and H heads: the longest power of two in
+// [1024, 8192] that still leaves about 2 work-groups per resident slot of the
+// chip (T H / chunk >= 2560).  Longer chunks mean fewer partial results to
+// merge; the longest-first order keeps the long ones from forming the tail.
+int pma_chunk(int T, int H);
 struct PmaArgs {
   const int32_t* offsets;      // [B+1]
-  const int32_t* chunk_start;  // [B+1]
+  const int32_t* order;        // [B] samples, longest first
+  const int32_t* chunk_start;  // [B+1] over the order
+  int chunk;                   // tokens per chunk
   const void* seeds;           // [m,H,d]
   const void* k;               // [T,H,d]
   const void* v;
@@ -120,7 +130,7 @@ struct PmaArgs {
   int B, H, m;
   float scale;
 };
-int pma_grid(int T, int B, int H);
+int pma_grid(int T, int B, int H, int chunk);
 // Forward: chunk kernel, then the merge of multi-chunk and empty samples.
 hipError_t launch_pma_fwd(const PmaArgs& a, int d, int grid, hipStream_t s);
 // Backward: chunk kernel (dK, dV, dSeeds partials), then the two-level dSeeds

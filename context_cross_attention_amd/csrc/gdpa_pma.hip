@@ -7,14 +7,14 @@
 // and the backward gives dK, dV per token and dSeeds summed over the batch.
 // bf16 in and out, fp32 accumulation, d in {32, 64, 128}, m <= 32.
 //
-// Work: one work-group (4 waves) per (chunk of up to kPmaChunk tokens of one
-// sample, head).  The 32 (zero-padded) seeds stay in registers as MFMA operands.
-// Wave w takes the chunk's 32-token blocks w, w + 4, w + 8, ... and streams them
-// through two LDS slots of its own, filled by global->LDS DMA two blocks ahead;
-// the waves never wait for each other inside the loop, so each slot is in flight
-// except while its wave computes on it.  Per byte of K/V the operation does at
-// most m flops, far below the MFMA/HBM balance point of the chip, so the kernels
-// are organised around keeping HBM busy; the MFMA work hides under the copies.
+// Work: one single-wave work-group per (chunk of up to a.chunk tokens of one
+// sample, head), several per CU, so that one work-group's start and epilogue
+// overlap the others' streaming.  The 32 (zero-padded) seeds stay in registers
+// as MFMA operands; the chunk's 32-token blocks stream through two LDS slots
+// filled by global->LDS DMA two blocks ahead, so each slot is in flight except
+// while the wave computes on it.  Per byte of K/V the operation does at most m
+// flops, far below the MFMA/HBM balance point of the chip, so the kernels are
+// organised around keeping HBM busy; the MFMA work hides under the copies.
 //
 // LDS tiles are dense row-major [rows][d] bf16 with the 16-byte chunks of a row
 // permuted (chunk c of row r stored at position c ^ swz(r)), so that both the
@@ -90,45 +90,96 @@ __device__ __forceinline__ bf16x8 tile_cols(const uint16_t* t, int r0, int kk, i
               lds_read_tr4(t + tile_off<D>(R + 8, c8) + 4 * (cc & 1)));
 }
 
+// Epilogue staging of a 32 x D fp32 C tile held as lane (s + 32 g), register r of
+// C[dt] <-> row s, column 32 dt + 8 (r / 4) + 4 g + r % 4: rows of D + 4 floats
+// in LDS (16-byte writes of 16 consecutive rows fall in distinct banks), each
+// value times `mul`.  Waits for the wave's LDS traffic on both sides.
+template <int D>
+__device__ __forceinline__ void stage_rows(float* st, const f32x16* C, float mul, int lane) {
+  const int lr = lane & 31, g = lane >> 5;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 v;
+      v[0] = C[dt][4 * q] * mul; v[1] = C[dt][4 * q + 1] * mul;
+      v[2] = C[dt][4 * q + 2] * mul; v[3] = C[dt][4 * q + 3] * mul;
+      *(GDPA_LDS f32x4*)(st + lr * (D + 4) + 32 * dt + 8 * q + 4 * g) = v;
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+// Rows 0 .. nrows-1 of the staged tile to dst + row * stride as bf16: each lane
+// converts 8 consecutive columns, so a wave store covers whole 2 D-byte rows.
+template <int D>
+__device__ __forceinline__ void store_rows_bf16(const float* st, uint16_t* dst, size_t stride, int nrows, int lane) {
+  constexpr int CH = D / 8, RPI = 64 / CH;
+  const int c = lane % CH;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = RPI * i + lane / CH;
+    const f32x4 x = *(const GDPA_LDS f32x4*)(st + row * (D + 4) + 8 * c);
+    const f32x4 y = *(const GDPA_LDS f32x4*)(st + row * (D + 4) + 8 * c + 4);
+    if (row < nrows) {
+      bf16x8 v;
+      v[0] = f2bf(x[0]); v[1] = f2bf(x[1]); v[2] = f2bf(x[2]); v[3] = f2bf(x[3]);
+      v[4] = f2bf(y[0]); v[5] = f2bf(y[1]); v[6] = f2bf(y[2]); v[7] = f2bf(y[3]);
+      *(bf16x8*)(dst + (size_t)row * stride + 8 * c) = v;
+    }
+  }
+}
+// All 32 rows of the staged tile to the dense [32][D] fp32 array dst.
+template <int D>
+__device__ __forceinline__ void store_rows_f32(const float* st, float* dst, int lane) {
+  constexpr int CH = D / 4, RPI = 64 / CH;
+  const int c = lane % CH;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = RPI * i + lane / CH;
+    *(f32x4*)(dst + (size_t)row * D + 4 * c) = *(const GDPA_LDS f32x4*)(st + row * (D + 4) + 4 * c);
+  }
+}
+
 struct ChunkInfo {
   int b, h, seq0, c0, c1, nch, chunk;
 };
 
 __device__ __forceinline__ bool decode_chunk(const PmaArgs& a, ChunkInfo& ci) {
   const int nchunks = a.chunk_start[a.B];
-  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  // Work items in launch order: the dispatcher deals consecutive work-groups to
+  // the 8 XCDs in turn, so the longest-first order stays balanced across them.
+  const int wid = blockIdx.x;
   if (wid >= nchunks * a.H) return false;
   ci.chunk = wid / a.H;
   ci.h = wid - ci.chunk * a.H;
-  ci.b = find_sample(a.chunk_start, a.B, ci.chunk);
+  const int r = find_sample(a.chunk_start, a.B, ci.chunk);  // rank in the longest-first order
+  ci.b = a.order[r];
   ci.seq0 = a.offsets[ci.b];
   const int len = a.offsets[ci.b + 1] - ci.seq0;
-  ci.c0 = (ci.chunk - a.chunk_start[ci.b]) * kPmaChunk;
-  ci.c1 = min(len, ci.c0 + kPmaChunk);
-  ci.nch = a.chunk_start[ci.b + 1] - a.chunk_start[ci.b];
+  ci.c0 = (ci.chunk - a.chunk_start[r]) * a.chunk;
+  ci.c1 = min(len, ci.c0 + a.chunk);
+  ci.nch = a.chunk_start[r + 1] - a.chunk_start[r];
   return true;
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void pma_fwd_kernel(const PmaArgs a) {
-  constexpr int KS = D / 16, DT = D / 32, TS = kPmaBlock * D, OS = D + 4, NPB = D / 8;
-  __shared__ __align__(1024) uint16_t ring[16 * TS];  // [wave][slot][K | V][TS]
+__global__ __launch_bounds__(64) void pma_fwd_kernel(const PmaArgs a) {
+  constexpr int KS = D / 16, DT = D / 32, TS = kPmaBlock * D, NPB = D / 8;
+  __shared__ __align__(1024) uint16_t ring[4 * TS];  // [slot][K | V][TS]
 
   ChunkInfo ci;
   if (!decode_chunk(a, ci)) return;
   const int H = a.H, h = ci.h;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x, lr = lane & 31, g = lane >> 5;
   const size_t rs = (size_t)H * D;
   const uint16_t* Kg = (const uint16_t*)a.k + (size_t)ci.seq0 * rs + (size_t)h * D;
   const uint16_t* Vg = (const uint16_t*)a.v + (size_t)ci.seq0 * rs + (size_t)h * D;
   const int len = ci.c1 - ci.c0, last = ci.c1 - 1;
-  const int nb = (len + kPmaBlock - 1) / kPmaBlock;  // 32-token blocks; this wave takes wave, wave + 4, ...
-  uint16_t* my = ring + wave * 4 * TS;
-  if (wave < nb) pma_issue<D>(my, my + TS, Kg, Vg, rs, ci.c0 + kPmaBlock * wave, last, lane);
+  const int nb = (len + kPmaBlock - 1) / kPmaBlock;  // >= 1
 
   // Seeds as B operands: lane (s + 32 g) holds Seeds[s][16 ks + 8 g .. + 7].  They
-  // are waited for here, before the second slot's copies are issued, so that no
-  // wait for them is left inside the loop (it would also wait for every copy).
+  // are waited for before the first copy is issued, so that no wait for them is
+  // left inside the loop (it would also wait for every copy in flight).
   bf16x8 sb[KS];
   {
     const uint16_t* sp = (const uint16_t*)a.seeds + ((size_t)(lr < a.m ? lr : 0) * H + h) * D + 8 * g;
@@ -137,17 +188,18 @@ __global__ __launch_bounds__(256, 1) void pma_fwd_kernel(const PmaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" :: "v"(sb[ks]));
   }
-  if (wave + 4 < nb) pma_issue<D>(my + 2 * TS, my + 3 * TS, Kg, Vg, rs, ci.c0 + kPmaBlock * (wave + 4), last, lane);
+  pma_issue<D>(ring, ring + TS, Kg, Vg, rs, ci.c0, last, lane);
+  if (nb > 1) pma_issue<D>(ring + 2 * TS, ring + 3 * TS, Kg, Vg, rs, ci.c0 + kPmaBlock, last, lane);
 
   const float sl2 = a.scale * kLog2e;
   float m_run = -INFINITY, l_run = 0.f;
-  f32x16 O[DT];
+  f32x16 O[DT];  // O^T: lane (s + 32 g), register r <-> d = 32 dt + 8 (r / 4) + 4 g + r % 4
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
 
-  for (int i = 0, j = wave; j < nb; ++i, j += 4) {
-    if (j + 4 < nb) slot_wait<NPB>(); else slot_wait<0>();
-    uint16_t* Kt = my + (i & 1) * 2 * TS;
+  for (int j = 0; j < nb; ++j) {
+    if (j + 1 < nb) slot_wait<NPB>(); else slot_wait<0>();
+    uint16_t* Kt = ring + (j & 1) * 2 * TS;
     const uint16_t* Vt = Kt + TS;
     const int nvalid = min(kPmaBlock, len - kPmaBlock * j);
 
@@ -187,82 +239,37 @@ __global__ __launch_bounds__(256, 1) void pma_fwd_kernel(const PmaArgs a) {
       for (int dt = 0; dt < DT; ++dt) O[dt] = mfma32(tile_cols<D>(Vt, 0, kk, dt, lane), pb, O[dt]);
     }
     // The slot's LDS reads have completed (their data fed the MFMAs): refill it.
-    if (j + 8 < nb) pma_issue<D>(Kt, Kt + TS, Kg, Vg, rs, ci.c0 + kPmaBlock * (j + 8), last, lane);
+    if (j + 2 < nb) pma_issue<D>(Kt, Kt + TS, Kg, Vg, rs, ci.c0 + kPmaBlock * (j + 2), last, lane);
   }
 
-  // Merge the 4 waves' (max, sum, O) per seed through LDS (the ring is free).
-  const float l_tot = l_run + wave_xor32(l_run);
-  __syncthreads();
-  float* ob = (float*)ring;           // [4][32][OS]
-  float* ml = ob + 4 * 32 * OS;       // [4][32][2]
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 v;
-      v[0] = O[dt][4 * q]; v[1] = O[dt][4 * q + 1]; v[2] = O[dt][4 * q + 2]; v[3] = O[dt][4 * q + 3];
-      *(GDPA_LDS f32x4*)(ob + (wave * 32 + lr) * OS + 32 * dt + 8 * q + 4 * g) = v;
-    }
-  if (g == 0) {
-    ml[(wave * 32 + lr) * 2] = m_run;
-    ml[(wave * 32 + lr) * 2 + 1] = l_tot;
-  }
-  __syncthreads();
-
-  constexpr int NC = D / 8;  // columns per thread
-  const int s = tid >> 3, cb = (tid & 7) * NC;
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * 32 + s) * 2]);
-  float wt[4], L = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    wt[w] = fast_exp2(ml[(w * 32 + s) * 2] - M);
-    L = fmaf(ml[(w * 32 + s) * 2 + 1], wt[w], L);
-  }
-  float o[NC];
-#pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) acc = fmaf(ob[(w * 32 + s) * OS + cb + j], wt[w], acc);
-    o[j] = acc;
-  }
-  if (ci.nch == 1) {
-    if (s < a.m) {
-      const float inv = 1.0f / L;
-      uint16_t* op = (uint16_t*)a.o + (((size_t)ci.b * a.m + s) * H + h) * D + cb;
-#pragma unroll
-      for (int j = 0; j < NC; j += 4) {
-        bf16x4 v;
-        v[0] = f2bf(o[j] * inv); v[1] = f2bf(o[j + 1] * inv); v[2] = f2bf(o[j + 2] * inv); v[3] = f2bf(o[j + 3] * inv);
-        *(bf16x4*)(op + j) = v;
-      }
-      if ((tid & 7) == 0) a.lse[((size_t)ci.b * a.m + s) * H + h] = (M + log2f(L)) * kLn2;
-    }
+  // Epilogue: O^T goes through LDS (the ring is idle now) so that it leaves as
+  // whole rows; scattered 8- or 16-byte pieces of 32 rows cost HBM transactions
+  // far beyond their bytes.
+  const float L = l_run + wave_xor32(l_run);
+  const bool single = ci.nch == 1;
+  stage_rows<D>((float*)ring, O, single ? 1.0f / L : 1.0f, lane);
+  if (single) {
+    store_rows_bf16<D>((const float*)ring, (uint16_t*)a.o + ((size_t)ci.b * a.m * H + h) * D, rs, a.m, lane);
+    if (lane < a.m) a.lse[((size_t)ci.b * a.m + lane) * H + h] = (m_run + log2f(L)) * kLn2;
   } else {
-    float* pp = a.part + ((size_t)ci.chunk * H + h) * 32 * D + (size_t)s * D + cb;
-#pragma unroll
-    for (int j = 0; j < NC; j += 4) {
-      f32x4 v;
-      v[0] = o[j]; v[1] = o[j + 1]; v[2] = o[j + 2]; v[3] = o[j + 3];
-      *(f32x4*)(pp + j) = v;
-    }
-    if ((tid & 7) == 0) {
-      float* mp = a.part_ml + (((size_t)ci.chunk * H + h) * 32 + s) * 2;
-      mp[0] = M;
+    store_rows_f32<D>((const float*)ring, a.part + ((size_t)ci.chunk * H + h) * 32 * D, lane);
+    if (g == 0) {
+      float* mp = a.part_ml + (((size_t)ci.chunk * H + h) * 32 + lr) * 2;
+      mp[0] = m_run;
       mp[1] = L;
     }
   }
 }
 
 // O and LSE of samples with no chunk (empty: zeros, -inf) or several chunks
-// (merge of the chunks' partial max / sum / O); one work-group per (sample, head).
+// (merge of the chunks' partial max / sum / O); one work-group per (sample, head),
+// samples taken by their rank in the longest-first order.
 template <int D>
 __global__ __launch_bounds__(256) void pma_combine_kernel(const PmaArgs a) {
   constexpr int NC = D / 8;
-  const int b = blockIdx.x / a.H, h = blockIdx.x - b * a.H;
-  const int c_beg = a.chunk_start[b], nch = a.chunk_start[b + 1] - c_beg;
+  const int r = blockIdx.x / a.H, h = blockIdx.x - r * a.H;
+  const int b = a.order[r];
+  const int c_beg = a.chunk_start[r], nch = a.chunk_start[r + 1] - c_beg;
   if (nch == 1) return;
   const int tid = threadIdx.x, s = tid >> 3, cb = (tid & 7) * NC;
   if (s >= a.m) return;
@@ -302,30 +309,29 @@ __global__ __launch_bounds__(256) void pma_combine_kernel(const PmaArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
-  constexpr int KS = D / 16, DT = D / 32, TS = kPmaBlock * D, OS = D + 4, NPB = D / 8;
-  __shared__ __align__(1024) uint16_t ring[16 * TS];      // [wave][slot][K | V][TS]
-  __shared__ __align__(16) uint16_t sdt[2 * TS];          // Seeds and dO of (b, h) as [32][D] tiles
-  __shared__ __align__(16) uint16_t dst[4 * 32 * 32];     // per wave: dS as [token][seed]
+__global__ __launch_bounds__(64) void pma_bwd_kernel(const PmaArgs a) {
+  constexpr int KS = D / 16, DT = D / 32, TS = kPmaBlock * D, NPB = D / 8;
+  __shared__ __align__(1024) uint16_t ring[4 * TS];  // [slot][K | V][TS]
+  __shared__ __align__(16) uint16_t dst[32 * 32];    // dS as [token][seed]
 
   ChunkInfo ci;
   if (!decode_chunk(a, ci)) return;
   const int H = a.H, h = ci.h, m = a.m;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x, lr = lane & 31, g = lane >> 5;
   const size_t rs = (size_t)H * D;
   const uint16_t* Kg = (const uint16_t*)a.k + (size_t)ci.seq0 * rs + (size_t)h * D;
   const uint16_t* Vg = (const uint16_t*)a.v + (size_t)ci.seq0 * rs + (size_t)h * D;
   const int len = ci.c1 - ci.c0, last = ci.c1 - 1;
-  const int nb = (len + kPmaBlock - 1) / kPmaBlock;  // 32-token blocks; this wave takes wave, wave + 4, ...
-  uint16_t* my = ring + wave * 4 * TS;
-  if (wave < nb) pma_issue<D>(my, my + TS, Kg, Vg, rs, ci.c0 + kPmaBlock * wave, last, lane);
+  const int nb = (len + kPmaBlock - 1) / kPmaBlock;  // >= 1
+  pma_issue<D>(ring, ring + TS, Kg, Vg, rs, ci.c0, last, lane);
 
-  // Seeds and dO of (b, h), zero-padded to 32 rows.  The set-up's loads wait for
-  // the first slot's copies too (they were issued earlier); the second slot's
-  // copies are issued after the set-up so that no wait inside the loop covers them.
-  uint16_t* St = sdt;
-  uint16_t* Dt = sdt + TS;
-  for (int i = tid; i < 32 * (D / 8); i += 256) {
+  // Seeds and dO of (b, h), zero-padded to 32 rows, as [32][D] tiles in the
+  // second slot (filled only after the set-up).  The set-up's loads wait for the
+  // first slot's copies too (they were issued earlier); the second slot's copies
+  // are issued after the set-up so that no wait inside the loop covers them.
+  uint16_t* St = ring + 2 * TS;
+  uint16_t* Dt = ring + 3 * TS;
+  for (int i = lane; i < 32 * (D / 8); i += 64) {
     const int s = i / (D / 8), c = i % (D / 8);
     u32x4 sv = u32x4{}, dv = u32x4{};
     if (s < m) {
@@ -380,20 +386,21 @@ __global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
   }
 
   asm volatile("" :: "v"(dv_s), "v"(lse2_s));
-  if (wave + 4 < nb) pma_issue<D>(my + 2 * TS, my + 3 * TS, Kg, Vg, rs, ci.c0 + kPmaBlock * (wave + 4), last, lane);
+  __syncthreads();  // the tile reads have completed: the second slot may be filled
+  if (nb > 1) pma_issue<D>(ring + 2 * TS, ring + 3 * TS, Kg, Vg, rs, ci.c0 + kPmaBlock, last, lane);
 
   const float sl2 = a.scale * kLog2e;
-  uint16_t* myds = dst + wave * 32 * 32;
+  uint16_t* myds = dst;
   f32x16 dSd[DT];  // dSeeds^T: lane (s + 32 g), register r <-> d = 32 dt + 8 (r / 4) + 4 g + r % 4
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dSd[dt] = f32x16{};
   const int G = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
 
-  for (int i = 0, j = wave; j < nb; ++i, j += 4) {
+  for (int j = 0; j < nb; ++j) {
     // Outstanding after the older slot's copies: the newer slot's and this wave's
     // earlier dK / dV stores; waiting for those too is the conservative choice.
-    if (j + 4 < nb) slot_wait<NPB>(); else slot_wait<0>();
-    uint16_t* Kt = my + (i & 1) * 2 * TS;
+    if (j + 1 < nb) slot_wait<NPB>(); else slot_wait<0>();
+    uint16_t* Kt = ring + (j & 1) * 2 * TS;
     const uint16_t* Vt = Kt + TS;
     const int tok0 = ci.c0 + kPmaBlock * j;  // sample-local
     const int nvalid = min(kPmaBlock, ci.c1 - tok0);
@@ -478,33 +485,12 @@ __global__ __launch_bounds__(256, 1) void pma_bwd_kernel(const PmaArgs a) {
       }
     }
     // The slot's LDS reads have completed (their data fed the MFMAs): refill it.
-    if (j + 8 < nb) pma_issue<D>(Kt, Kt + TS, Kg, Vg, rs, ci.c0 + kPmaBlock * (j + 8), last, lane);
+    if (j + 2 < nb) pma_issue<D>(Kt, Kt + TS, Kg, Vg, rs, ci.c0 + kPmaBlock * (j + 2), last, lane);
   }
 
-  // Sum the 4 waves' dSeeds^T and store this chunk's partial [32][D] (unscaled).
-  __syncthreads();
-  float* ob = (float*)ring;  // [4][32][OS]
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 v;
-      v[0] = dSd[dt][4 * q]; v[1] = dSd[dt][4 * q + 1]; v[2] = dSd[dt][4 * q + 2]; v[3] = dSd[dt][4 * q + 3];
-      *(GDPA_LDS f32x4*)(ob + (wave * 32 + lr) * OS + 32 * dt + 8 * q + 4 * g) = v;
-    }
-  __syncthreads();
-  constexpr int NC = D / 8;
-  const int s = tid >> 3, cb = (tid & 7) * NC;
-  float* pp = a.part + ((size_t)ci.chunk * H + h) * 32 * D + (size_t)s * D + cb;
-#pragma unroll
-  for (int j = 0; j < NC; j += 4) {
-    f32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = ob[s * OS + cb + j + e] + ob[(32 + s) * OS + cb + j + e] + ob[(64 + s) * OS + cb + j + e] +
-             ob[(96 + s) * OS + cb + j + e];
-    *(f32x4*)(pp + j) = v;
-  }
+  // This chunk's dSeeds^T partial [32][D] (unscaled), as whole rows through LDS.
+  stage_rows<D>((float*)ring, dSd, 1.0f, lane);
+  store_rows_f32<D>((const float*)ring, a.part + ((size_t)ci.chunk * H + h) * 32 * D, lane);
 }
 
 // dSeeds, first level: slice sl sums the partials of chunks sl, sl + kPmaSlices, ...
@@ -538,8 +524,14 @@ __global__ __launch_bounds__(256) void pma_reduce2_kernel(const float* __restric
 
 }  // namespace
 
-int pma_grid(int T, int B, int H) {
-  const long chunks = (long)T / kPmaChunk + B;  // >= sum_b ceil(L_b / kPmaChunk)
+int pma_chunk(int T, int H) {
+  int c = 1024;
+  while (c < 8192 && (int64_t)T * H / (2 * c) >= 2560) c *= 2;
+  return c;
+}
+
+int pma_grid(int T, int B, int H, int chunk) {
+  const long chunks = (long)T / chunk + B;  // >= sum_b ceil(L_b / chunk)
   const long g = (chunks * H + 7) / 8 * 8;
   return (int)g;
 }
@@ -547,9 +539,9 @@ int pma_grid(int T, int B, int H) {
 hipError_t launch_pma_fwd(const PmaArgs& a, int d, int grid, hipStream_t s) {
   if (grid > 0) {
     switch (d) {
-      case 32: hipLaunchKernelGGL(pma_fwd_kernel<32>, dim3(grid), dim3(256), 0, s, a); break;
-      case 64: hipLaunchKernelGGL(pma_fwd_kernel<64>, dim3(grid), dim3(256), 0, s, a); break;
-      case 128: hipLaunchKernelGGL(pma_fwd_kernel<128>, dim3(grid), dim3(256), 0, s, a); break;
+      case 32: hipLaunchKernelGGL(pma_fwd_kernel<32>, dim3(grid), dim3(64), 0, s, a); break;
+      case 64: hipLaunchKernelGGL(pma_fwd_kernel<64>, dim3(grid), dim3(64), 0, s, a); break;
+      case 128: hipLaunchKernelGGL(pma_fwd_kernel<128>, dim3(grid), dim3(64), 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
     const hipError_t e = hipGetLastError();
@@ -568,9 +560,9 @@ hipError_t launch_pma_fwd(const PmaArgs& a, int d, int grid, hipStream_t s) {
 hipError_t launch_pma_bwd(const PmaArgs& a, int d, int grid, float* part2, hipStream_t s) {
   if (grid > 0) {
     switch (d) {
-      case 32: hipLaunchKernelGGL(pma_bwd_kernel<32>, dim3(grid), dim3(256), 0, s, a); break;
-      case 64: hipLaunchKernelGGL(pma_bwd_kernel<64>, dim3(grid), dim3(256), 0, s, a); break;
-      case 128: hipLaunchKernelGGL(pma_bwd_kernel<128>, dim3(grid), dim3(256), 0, s, a); break;
+      case 32: hipLaunchKernelGGL(pma_bwd_kernel<32>, dim3(grid), dim3(64), 0, s, a); break;
+      case 64: hipLaunchKernelGGL(pma_bwd_kernel<64>, dim3(grid), dim3(64), 0, s, a); break;
+      case 128: hipLaunchKernelGGL(pma_bwd_kernel<128>, dim3(grid), dim3(64), 0, s, a); break;
       default: return hipErrorInvalidValue;
     }
     const hipError_t e = hipGetLastError();

@@ -9,11 +9,13 @@
 
 namespace gdpa {
 
-// tile_start[b] = sum_{b' < b} ceil(len(b') / tile_rows), tile_start[B] = total.
+// tile_start[b] = sum_{b' < b} ceil(len(b') / tile_rows), tile_start[B] = total;
+// with `order`, the scan runs over the samples order[0], order[1], ... instead.
 // One work-group of 1024 threads scans the batch in chunks of 1024 samples.
 __global__ __launch_bounds__(1024) void tile_scan_kernel(const int32_t* __restrict__ off, int B,
                                                          int tile_rows,
-                                                         int32_t* __restrict__ tile_start) {
+                                                         int32_t* __restrict__ tile_start,
+                                                         const int32_t* __restrict__ order) {
   __shared__ int32_t wave_sums[16];
   __shared__ int32_t carry;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -23,7 +25,8 @@ __global__ __launch_bounds__(1024) void tile_scan_kernel(const int32_t* __restri
     const int b = base + tid;
     int c = 0;
     if (b < B) {
-      const int len = off[b + 1] - off[b];
+      const int sb = order != nullptr ? order[b] : b;
+      const int len = off[sb + 1] - off[sb];
       c = (len + tile_rows - 1) / tile_rows;
     }
     // inclusive scan inside the wave
@@ -121,9 +124,9 @@ __global__ __launch_bounds__(256) void softmax_dvec_kernel(const void* __restric
 }
 
 hipError_t launch_tile_scan(const int32_t* offsets, int B, int tile_rows, int32_t* tile_start,
-                            hipStream_t s) {
+                            hipStream_t s, const int32_t* order) {
   hipLaunchKernelGGL(tile_scan_kernel, dim3(1), dim3(1024), 0, s, offsets, B, tile_rows,
-                     tile_start);
+                     tile_start, order);
   return hipGetLastError();
 }
 

@@ -212,8 +212,8 @@ typedef struct {
 } gdpa_pma_problem;
 
 /* Workspace bytes for gdpa_pma_fwd (backward = 0) or gdpa_pma_bwd (backward != 0);
- * 0 for an invalid problem.  About (T / 1024 + B) * H * 16 * d bytes (chunk
- * partials in fp32). */
+ * 0 for an invalid problem.  At most about (T / 1024 + B) * H * 128 * d bytes
+ * (per-chunk partial results in fp32). */
 size_t gdpa_pma_workspace_bytes(const gdpa_pma_problem* p, int backward);
 
 /* Forward.  seeds [m,H,d], k, v [T,H,d] in; o [B,m,H,d] and lse [B,m,H] out
