@@ -396,10 +396,18 @@ __global__ __launch_bounds__(64) void pma_bwd_kernel(const PmaArgs a) {
   for (int dt = 0; dt < DT; ++dt) dSd[dt] = f32x16{};
   const int G = lane >> 4, rr = (lane >> 2) & 3, cc = lane & 3;
 
+  // vmcnt counts this wave's copies and stores together, in issue order.  Issued
+  // after block j's copies: the previous block's NST row stores, then block
+  // j + 1's NPB copies; waiting for exactly block j keeps both in flight (the
+  // stores of a full block are NST instructions; only the last block can be
+  // partial, and nothing waits past it).
+  constexpr int NST = 2 * (D / 16);
   for (int j = 0; j < nb; ++j) {
-    // Outstanding after the older slot's copies: the newer slot's and this wave's
-    // earlier dK / dV stores; waiting for those too is the conservative choice.
-    if (j + 1 < nb) slot_wait<NPB>(); else slot_wait<0>();
+    if (j == 0) {
+      if (nb > 1) slot_wait<NPB>(); else slot_wait<0>();
+    } else {
+      if (j + 1 < nb) slot_wait<NPB + NST>(); else slot_wait<NST>();
+    }
     uint16_t* Kt = ring + (j & 1) * 2 * TS;
     const uint16_t* Vt = Kt + TS;
     const int tok0 = ci.c0 + kPmaBlock * j;  // sample-local
