@@ -66,6 +66,7 @@ def parse():
 
 CSRC = os.path.join(ROOT, "context_cross_attention_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stacked_b1024_h8_d128_n256.json")
+PMA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pma_b1024_h8_d128_m32.json")
 
 
 def kernel_source_hash():
@@ -78,10 +79,10 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
+def measured_traffic(kernel, path=TRAFFIC_FILE):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -390,7 +391,8 @@ def run_pma(args):
     t_dom = totals[dom] / counts[dom] * 1e-3
     f_dom, b_dom = units[dom]
     roof = {"bound": "hbm", "achieved": round(b_dom / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, kernel=dom,
+    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=measured_traffic(dom, PMA_TRAFFIC_FILE),
+                kernel=dom,
                 launch_ms=round(totals[dom] / counts[dom], 4),
                 algorithmic_per_launch={"flops": f_dom, "bytes": b_dom},
                 other_bound_frac=round(f_dom / t_dom / 1e12 / PEAK_BF16_TFLOPS, 4))

@@ -25,8 +25,6 @@ CFLAGS = [
     # Packed fp32 VALU forms stay off: the compiler would otherwise emit them from
     # plain float code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # Hardware fp32 atomic add for the dQ partial sums.
-    "-munsafe-fp-atomics",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 SOURCES = ["gdpa_sched.hip", "gdpa_fwd.hip", "gdpa_fwd_res.hip", "gdpa_bwd.hip", "gdpa_bwd_res.hip",
