@@ -271,3 +271,39 @@ def make_pma_inputs(length_spec: tuple, batch: int, H: int, d: int, m: int, seed
     v = draw_normal(rng, (T, H, d), dtype, math.sqrt(d))
     do = draw_normal(rng, (batch, m, H, d), dtype)
     return PmaInputs(lengths, torch.from_numpy(off.astype(np.int32)), seeds, k, v, do)
+
+
+@dataclass
+class JaggedKvInputs:
+    """GDPA inputs with a jagged context: K, V [rows,H,d], sample b owning rows kv_offsets[b]:kv_offsets[b+1]."""
+    lengths: np.ndarray
+    kv_counts: np.ndarray
+    offsets: torch.Tensor
+    kv_offsets: torch.Tensor
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    do: torch.Tensor
+
+    @property
+    def n_kv(self) -> int:
+        return int(self.kv_counts.max())
+
+
+def make_jagged_kv_inputs(length_spec: tuple, count_spec: tuple, batch: int, H: int, d: int,
+                          seed: int = 0, sharp: bool = False, dtype: str = "bf16") -> JaggedKvInputs:
+    """Draw token lengths, then context row counts (each >= 1), then Q, K, V ~ N(0,1)/sqrt(d)
+    (Q and K ~ N(0,1) when sharp), then dO ~ N(0,1), rounded to `dtype`."""
+    rng = np.random.default_rng(seed)
+    lengths = draw_lengths(rng, length_spec, batch)
+    counts = np.maximum(draw_lengths(rng, count_spec, batch), 1)
+    off = offsets_from_lengths(lengths)
+    kv_off = offsets_from_lengths(counts)
+    T, N = int(off[-1]), int(kv_off[-1])
+    qk_div = 1.0 if sharp else math.sqrt(d)
+    q = draw_normal(rng, (T, H, d), dtype, qk_div)
+    k = draw_normal(rng, (N, H, d), dtype, qk_div)
+    v = draw_normal(rng, (N, H, d), dtype, math.sqrt(d))
+    do = draw_normal(rng, (T, H, d), dtype)
+    return JaggedKvInputs(lengths, counts, torch.from_numpy(off.astype(np.int32)),
+                          torch.from_numpy(kv_off.astype(np.int32)), q, k, v, do)

@@ -190,17 +190,45 @@ def _check(q, offsets, k, v):
     return T, H, d, B, n
 
 
+def _check_jagged(q, offsets, kv_offsets, k, v):
+    """Jagged context: k, v [rows,H,d], sample b owns rows kv_offsets[b]:kv_offsets[b+1], at least one."""
+    T, H, d = q.shape
+    B = len(offsets) - 1
+    if k.ndim != 3 or v.shape != k.shape or k.shape[1:] != (H, d):
+        raise ValueError("jagged K/V must be [rows,H,d] with the heads and width of Q")
+    if len(kv_offsets) != B + 1 or kv_offsets[0] != 0 or kv_offsets[-1] != k.shape[0]:
+        raise ValueError("kv_offsets must have B+1 entries from 0 to the number of rows")
+    if np.any(np.diff(kv_offsets) < 1):
+        raise ValueError("every sample needs at least one context row")
+    if offsets[0] != 0 or offsets[-1] != T or np.any(np.diff(offsets) < 0):
+        raise ValueError("offsets must be non-decreasing from 0 to T")
+    return T, H, d, B
+
+
+def _context(k, v, b, h, kv_offsets):
+    """K and V rows of sample b, head h: the dense [B,n,H,d] slice or the jagged rows."""
+    if kv_offsets is None:
+        return k[b, :, h, :], v[b, :, h, :]
+    r = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
+    return k[r, h, :], v[r, h, :]
+
+
 def gdpa_forward(q, offsets, k, v, phi: str = "softmax", scale: Optional[float] = None,
-                 samples: Optional[Sequence[int]] = None):
+                 samples: Optional[Sequence[int]] = None, kv_offsets=None):
     """Forward over a jagged batch.
 
-    q: [T,H,d]; offsets: [B+1]; k, v: [B,n,H,d].  Returns (O [T,H,d],
-    lse [T,H] for softmax else None), float64.  With `samples`, only those
-    samples' rows are computed (the rest stay NaN): samples are independent.
+    q: [T,H,d]; offsets: [B+1]; k, v: [B,n,H,d], or with kv_offsets [B+1] a jagged
+    context [rows,H,d] (sample b owns rows kv_offsets[b]:kv_offsets[b+1]).  Returns
+    (O [T,H,d], lse [T,H] for softmax else None), float64.  With `samples`, only
+    those samples' rows are computed (the rest stay NaN): samples are independent.
     """
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     offsets = np.asarray(as_f64(offsets), dtype=np.int64)
-    T, H, d, B, n = _check(q, offsets, k, v)
+    if kv_offsets is None:
+        T, H, d, B, n = _check(q, offsets, k, v)
+    else:
+        kv_offsets = np.asarray(as_f64(kv_offsets), dtype=np.int64)
+        T, H, d, B = _check_jagged(q, offsets, kv_offsets, k, v)
     if scale is None:
         scale = default_scale(phi, d)
     o = np.full((T, H, d), np.nan)
@@ -208,7 +236,8 @@ def gdpa_forward(q, offsets, k, v, phi: str = "softmax", scale: Optional[float] 
     for b in (range(B) if samples is None else samples):
         r0, r1 = int(offsets[b]), int(offsets[b + 1])
         for h in range(H):
-            ob, lb = gdpa_forward_bh(q[r0:r1, h, :], k[b, :, h, :], v[b, :, h, :], phi, scale)
+            kb, vb = _context(k, v, b, h, kv_offsets)
+            ob, lb = gdpa_forward_bh(q[r0:r1, h, :], kb, vb, phi, scale)
             o[r0:r1, h, :] = ob
             if lse is not None:
                 lse[r0:r1, h] = lb
@@ -216,28 +245,37 @@ def gdpa_forward(q, offsets, k, v, phi: str = "softmax", scale: Optional[float] 
 
 
 def gdpa_backward(q, offsets, k, v, do, phi: str = "softmax", scale: Optional[float] = None,
-                  samples: Optional[Sequence[int]] = None):
-    """Backward over a jagged batch: (dQ [T,H,d], dK [B,n,H,d], dV [B,n,H,d]).
+                  samples: Optional[Sequence[int]] = None, kv_offsets=None):
+    """Backward over a jagged batch: (dQ [T,H,d], dK, dV shaped like K, V).
 
     dK and dV are sums over each sample's own tokens; an empty sample gets zeros.
     With `samples`, rows and K/V slots of other samples stay NaN.
     """
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     offsets = np.asarray(as_f64(offsets), dtype=np.int64)
-    T, H, d, B, n = _check(q, offsets, k, v)
+    if kv_offsets is None:
+        T, H, d, B, n = _check(q, offsets, k, v)
+    else:
+        kv_offsets = np.asarray(as_f64(kv_offsets), dtype=np.int64)
+        T, H, d, B = _check_jagged(q, offsets, kv_offsets, k, v)
     if scale is None:
         scale = default_scale(phi, d)
     dq = np.full((T, H, d), np.nan)
-    dk = np.full((B, n, H, d), np.nan)
-    dv = np.full((B, n, H, d), np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
     for b in (range(B) if samples is None else samples):
         r0, r1 = int(offsets[b]), int(offsets[b + 1])
         for h in range(H):
-            gx, gk, gv = gdpa_backward_bh(q[r0:r1, h, :], k[b, :, h, :], v[b, :, h, :],
-                                          do[r0:r1, h, :], phi, scale)
+            kb, vb = _context(k, v, b, h, kv_offsets)
+            gx, gk, gv = gdpa_backward_bh(q[r0:r1, h, :], kb, vb, do[r0:r1, h, :], phi, scale)
             dq[r0:r1, h, :] = gx
-            dk[b, :, h, :] = gk
-            dv[b, :, h, :] = gv
+            if kv_offsets is None:
+                dk[b, :, h, :] = gk
+                dv[b, :, h, :] = gv
+            else:
+                c = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
+                dk[c, h, :] = gk
+                dv[c, h, :] = gv
     return dq, dk, dv
 
 
