@@ -69,6 +69,7 @@ _lib = None
 EXPORTS = ("gdpa_workspace_bytes", "gdpa_fwd", "gdpa_bwd", "gdpa_weightgen_fwd",
            "gdpa_weightgen_bwd_w", "gdpa_swa_workspace_bytes", "gdpa_swa_fwd", "gdpa_swa_bwd",
            "gdpa_pma_workspace_bytes", "gdpa_pma_fwd", "gdpa_pma_bwd",
+           "gdpa_fwd_jagged_kv", "gdpa_bwd_jagged_kv", "gdpa_check_kv_offsets",
            "gdpa_check_offsets", "gdpa_status_str", "gdpa_last_hip_error")
 
 
@@ -106,6 +107,12 @@ def load(path: str = LIB_PATH):
     lib.gdpa_pma_fwd.restype = ctypes.c_int
     lib.gdpa_pma_bwd.argtypes = [PP, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_pma_bwd.restype = ctypes.c_int
+    lib.gdpa_fwd_jagged_kv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_fwd_jagged_kv.restype = ctypes.c_int
+    lib.gdpa_bwd_jagged_kv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_bwd_jagged_kv.restype = ctypes.c_int
+    lib.gdpa_check_kv_offsets.argtypes = [vp, i32, i32]
+    lib.gdpa_check_kv_offsets.restype = ctypes.c_int
     lib.gdpa_check_offsets.argtypes = [vp, i32, i32, i32]
     lib.gdpa_check_offsets.restype = ctypes.c_int
     lib.gdpa_status_str.argtypes = [ctypes.c_int]
@@ -252,6 +259,86 @@ def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                       _stream())
     _check(st, "gdpa_bwd")
     return dq, dk, dv
+
+
+def _jagged_problem(q, offsets, k, n_kv: int, phi: str, scale: Optional[float], flags: int) -> GdpaProblem:
+    T, H, d = q.shape
+    if phi not in PHI:
+        raise ValueError(f"phi must be one of {tuple(PHI)}")
+    if q.dtype not in DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return GdpaProblem(offsets.shape[0] - 1, T, T, int(n_kv), H, d, PHI[phi],
+                       default_scale(phi, d) if scale is None else float(scale), DTYPE[q.dtype], flags)
+
+
+def fwd_jagged_kv(q: torch.Tensor, offsets: torch.Tensor, kv_offsets: torch.Tensor, k: torch.Tensor,
+                  v: torch.Tensor, n_kv: int, phi: str = "softmax", scale: Optional[float] = None,
+                  residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """GDPA forward with a jagged context: sample b owns rows kv_offsets[b] .. kv_offsets[b+1]-1
+    of k, v [rows,H,d]; n_kv is the largest per-sample count (1 <= count <= n_kv).
+    Returns (o [T,H,d], lse [T,H] for softmax else None)."""
+    lib = load()
+    T, H, d = q.shape
+    B = offsets.shape[0] - 1
+    dev = q.device
+    _require(offsets, "offsets", (B + 1,), torch.int32, dev)
+    _require(kv_offsets, "kv_offsets", (B + 1,), torch.int32, dev)
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, (k.shape[0], H, d), q.dtype, dev)
+    flags = 0
+    if residual is not None:
+        _require(residual, "residual", (T, H, d), q.dtype, dev)
+        flags |= FWD_RESIDUAL
+    out = torch.empty_like(q) if out is None else out
+    _require(out, "out", (T, H, d), q.dtype, dev)
+    if phi == "softmax":
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev) if lse is None else lse
+    else:
+        lse = None
+    prob = _jagged_problem(q, offsets, k, n_kv, phi, scale, flags)
+    ws = _workspace(prob, False, dev, workspace)
+    _check(lib.gdpa_fwd_jagged_kv(ctypes.byref(prob), _ptr(offsets), _ptr(kv_offsets), _ptr(q), _ptr(k),
+                                  _ptr(v), _ptr(residual), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                  _stream()), "gdpa_fwd_jagged_kv")
+    return out, lse
+
+
+def bwd_jagged_kv(q: torch.Tensor, offsets: torch.Tensor, kv_offsets: torch.Tensor, k: torch.Tensor,
+                  v: torch.Tensor, n_kv: int, o: Optional[torch.Tensor], lse: Optional[torch.Tensor],
+                  do: torch.Tensor, phi: str = "softmax", scale: Optional[float] = None,
+                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                  dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Backward of fwd_jagged_kv: returns (dq [T,H,d], dk, dv [rows,H,d])."""
+    lib = load()
+    T, H, d = q.shape
+    B = offsets.shape[0] - 1
+    dev = q.device
+    _require(offsets, "offsets", (B + 1,), torch.int32, dev)
+    _require(kv_offsets, "kv_offsets", (B + 1,), torch.int32, dev)
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, (k.shape[0], H, d), q.dtype, dev)
+    _require(do, "do", (T, H, d), q.dtype, dev)
+    if phi == "softmax":
+        _require(o, "o", (T, H, d), q.dtype, dev)
+        _require(lse, "lse", (T, H), torch.float32, dev)
+    else:
+        o, lse = None, None
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    prob = _jagged_problem(q, offsets, k, n_kv, phi, scale, 0)
+    ws = _workspace(prob, True, dev, workspace)
+    _check(lib.gdpa_bwd_jagged_kv(ctypes.byref(prob), _ptr(offsets), _ptr(kv_offsets), _ptr(q), _ptr(k),
+                                  _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _ptr(ws), ws.numel(), _stream()), "gdpa_bwd_jagged_kv")
+    return dq, dk, dv
+
+
+def check_kv_offsets(kv_offsets, n_kv: int) -> bool:
+    """Host-side check of a kv_offsets array (list / numpy / CPU tensor)."""
+    t = torch.as_tensor(kv_offsets, dtype=torch.int32).contiguous().cpu()
+    return load().gdpa_check_kv_offsets(ctypes.c_void_p(t.data_ptr()), t.numel() - 1, int(n_kv)) == 0
 
 
 def _swa_problem(q: torch.Tensor, offsets: torch.Tensor, window: int, scale: Optional[float]):

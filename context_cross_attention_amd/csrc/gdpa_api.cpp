@@ -90,9 +90,15 @@ size_t gdpa_workspace_bytes(const gdpa_problem* p, int backward) {
   return backward ? bwd_plan(p).total : fwd_workspace(p);
 }
 
-gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
-                     const void* v, const void* residual, void* o, float* lse, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Forward and backward of the dense ([B, n_kv, H, d]) and jagged ([rows, H, d]
+// with kv_offsets) context forms; kv_offsets == nullptr selects the dense one.
+gdpa_status fwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
+                     const void* q, const void* k, const void* v, const void* residual, void* o,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   const gdpa_status st = check_problem(p);
   if (st != GDPA_OK) return st;
   if (offsets == nullptr || k == nullptr || v == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
@@ -116,6 +122,7 @@ gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* 
   a.residual = residual;
   a.o = o;
   a.lse = (p->phi == GDPA_PHI_SOFTMAX) ? lse : nullptr;
+  a.kv_offsets = kv_offsets;
   a.B = p->batch;
   a.T = p->total_tokens;
   a.n = p->n_kv;
@@ -137,9 +144,10 @@ gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* 
   return hip_status(gdpa::launch_fwd_bf16(a, p->head_dim, p->phi, resid, grid, s));
 }
 
-gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
-                     const void* v, const void* o, const float* lse, const void* d_o, void* dq,
-                     void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+gdpa_status bwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
+                     const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* d_o, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   const gdpa_status st = check_problem(p);
   if (st != GDPA_OK) return st;
   if (offsets == nullptr || k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)
@@ -173,6 +181,7 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
   a.dk = dk;
   a.dv = dv;
   a.tile_start = pl.split_dq ? (const int32_t*)(ws + pl.tile_off) : nullptr;
+  a.kv_offsets = kv_offsets;
   a.B = p->batch;
   a.T = p->total_tokens;
   a.n = p->n_kv;
@@ -205,6 +214,50 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
   if (e != hipSuccess) return hip_status(e);
   return hip_status(gdpa::launch_bwd_dq(a, p->head_dim, p->phi, false,
                                         gdpa::fwd_bf16_grid(p->total_tokens, p->batch, p->heads), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
+                     const void* v, const void* residual, void* o, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  return fwd_impl(p, offsets, nullptr, q, k, v, residual, o, lse, workspace, workspace_bytes, stream);
+}
+
+gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
+                     const void* v, const void* o, const float* lse, const void* d_o, void* dq,
+                     void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, offsets, nullptr, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes,
+                  stream);
+}
+
+gdpa_status gdpa_fwd_jagged_kv(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
+                               const void* q, const void* k, const void* v, const void* residual,
+                               void* o, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (kv_offsets == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  return fwd_impl(p, offsets, kv_offsets, q, k, v, residual, o, lse, workspace, workspace_bytes, stream);
+}
+
+gdpa_status gdpa_bwd_jagged_kv(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
+                               const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (kv_offsets == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  return bwd_impl(p, offsets, kv_offsets, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes,
+                  stream);
+}
+
+gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv) {
+  if (host_kv_offsets == nullptr || batch < 1 || n_kv < 1) return GDPA_ERR_INVALID_ARGUMENT;
+  if (host_kv_offsets[0] != 0) return GDPA_ERR_INVALID_ARGUMENT;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t rows = (int64_t)host_kv_offsets[b + 1] - host_kv_offsets[b];
+    if (rows < 1 || rows > n_kv) return GDPA_ERR_INVALID_ARGUMENT;
+  }
+  return GDPA_OK;
 }
 
 gdpa_status gdpa_weightgen_fwd(int32_t batch, int32_t ctx_dim, int64_t cols, const void* ctx,

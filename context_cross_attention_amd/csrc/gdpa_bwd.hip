@@ -75,12 +75,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
     b = a.order[rank];
   }
   const int seq0 = a.offsets[b], L = a.offsets[b + 1] - seq0;
-  const int n = SW ? L : a.n;  // key rows of this sample
+  size_t crow0 = 0;  // first context row of this sample
+  const int n = SW ? L : kv_rows(a.kv_offsets, b, a.n, crow0);  // key rows of this sample
   const int j0 = jc * NJ;
+  if (j0 >= n) return;  // a jagged context with fewer rows than the largest
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const size_t rs = (size_t)H * D;
-  const size_t kv0 = SW ? (size_t)seq0 * H : (size_t)b * n * H;
+  const size_t kv0 = SW ? (size_t)seq0 * H : crow0 * H;
   const uint16_t* Kg = (const uint16_t*)a.k + (kv0 + h) * D;
   const uint16_t* Vg = (const uint16_t*)a.v + (kv0 + h) * D;
 
@@ -322,9 +324,11 @@ __global__ __launch_bounds__(128) void bwd_f32_dq_kernel(const BwdArgs a) {
   float acc[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) acc[e] = 0.f;
-  const float* Kb = (const float*)a.k + ((size_t)b * a.n * a.H + h) * D;
-  const float* Vb = (const float*)a.v + ((size_t)b * a.n * a.H + h) * D;
-  for (int j = 0; j < a.n; ++j) {
+  size_t crow0;
+  const int n = kv_rows(a.kv_offsets, b, a.n, crow0);
+  const float* Kb = (const float*)a.k + (crow0 * a.H + h) * D;
+  const float* Vb = (const float*)a.v + (crow0 * a.H + h) * D;
+  for (int j = 0; j < n; ++j) {
     const float* kj = Kb + (size_t)j * rs;
     const float* vj = Vb + (size_t)j * rs;
     float s = 0.f, dp = 0.f;
@@ -358,9 +362,11 @@ __global__ __launch_bounds__(128) void bwd_f32_dkdv_kernel(const BwdArgs a) {
   const long bj = bjh / a.H;
   const int j = bj % a.n;
   const int b = (int)(bj / a.n);
+  size_t crow0;
+  if (j >= kv_rows(a.kv_offsets, b, a.n, crow0)) return;  // past a jagged sample's rows
   const size_t rs = (size_t)a.H * D;
-  const float* kj = (const float*)a.k + ((size_t)b * a.n + j) * rs + (size_t)h * D;
-  const float* vj = (const float*)a.v + ((size_t)b * a.n + j) * rs + (size_t)h * D;
+  const float* kj = (const float*)a.k + (crow0 + j) * rs + (size_t)h * D;
+  const float* vj = (const float*)a.v + (crow0 + j) * rs + (size_t)h * D;
   float gk[32], gv[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
@@ -387,8 +393,8 @@ __global__ __launch_bounds__(128) void bwd_f32_dkdv_kernel(const BwdArgs a) {
       gk[e] = fmaf(ds, qp[32 * sl + e], gk[e]);
     }
   }
-  float* dkp = (float*)a.dk + ((size_t)b * a.n + j) * rs + (size_t)h * D + 32 * sl;
-  float* dvp = (float*)a.dv + ((size_t)b * a.n + j) * rs + (size_t)h * D + 32 * sl;
+  float* dkp = (float*)a.dk + (crow0 + j) * rs + (size_t)h * D + 32 * sl;
+  float* dvp = (float*)a.dv + (crow0 + j) * rs + (size_t)h * D + 32 * sl;
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
     dkp[e] = gk[e];

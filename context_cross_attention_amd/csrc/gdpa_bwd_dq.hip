@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   const int seq0 = a.offsets[b];
   const int row0 = seq0 + (qtile - a.tile_start[b]) * BM;
   const int rows = min(BM, a.offsets[b + 1] - row0);
-  const int n = SW ? a.offsets[b + 1] - seq0 : a.n;
+  size_t crow0 = 0;  // first context row of this sample
+  const int n = SW ? a.offsets[b + 1] - seq0 : kv_rows(a.kv_offsets, b, a.n, crow0);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const int trow = wave * 32 + lr;
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   const float lse2 = (PHI == kPhiSoftmax) ? a.lse[th] * kLog2e : 0.f;
   const float dvec = (PHI == kPhiSoftmax) ? a.dvec[th] : 0.f;
 
-  const size_t kv0 = SW ? (size_t)seq0 * H : (size_t)b * n * H;
+  const size_t kv0 = SW ? (size_t)seq0 * H : crow0 * H;
   const uint16_t* Kg = (const uint16_t*)a.k + (kv0 + h) * D;
   const uint16_t* Vg = (const uint16_t*)a.v + (kv0 + h) * D;
   const int qlo = row0 - seq0;

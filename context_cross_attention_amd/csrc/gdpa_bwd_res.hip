@@ -80,10 +80,12 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   __shared__ __align__(16) uint16_t dSs[BQ * LDJ];
   static_assert(8 * 32 * LDE <= D * LDJ, "epilogue tiles must fit in Kt");
 
-  const int H = a.H, n = a.n;
+  const int H = a.H;
   const int item = blockIdx.x;
   const int rank = item / H, h = item - rank * H;
   const int b = a.order[rank];
+  size_t crow0;
+  const int n = kv_rows(a.kv_offsets, b, a.n, crow0);  // 1 <= n <= a.n
   const int seq0 = a.offsets[b], L = a.offsets[b + 1] - seq0;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const size_t rs = (size_t)H * D;
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   // half-wave: each 2-byte write instruction covers two contiguous 64-byte runs).
   bf16x8 kf[KS], vf[KS];
   {
-    const size_t row = ((size_t)b * n + min(j, n - 1)) * rs + (size_t)h * D + 8 * g;
+    const size_t row = (crow0 + min(j, n - 1)) * rs + (size_t)h * D + 8 * g;
     u32x4 kr[KS], vr[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       for (int r = 0; r < 16; ++r)
         Ew[(8 * (r >> 2) + 4 * g + (r & 3)) * LDE + 32 * dt + lr] =
             __builtin_bit_cast(uint16_t, f2bf(which == 0 ? dK[dt][r] * scale : dV[dt][r]));
-    uint16_t* dst = (uint16_t*)(which == 0 ? a.dk : a.dv) + ((size_t)b * n * H + h) * D;
+    uint16_t* dst = (uint16_t*)(which == 0 ? a.dk : a.dv) + (crow0 * H + h) * D;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int row = 4 * u + (lane >> 4), c = lane & 15;

@@ -183,6 +183,20 @@ __device__ __forceinline__ int xcd_remap(int bid, int grid) {  // grid % 8 == 0
   return (bid & 7) * per + (bid >> 3);
 }
 
+// Context rows of sample b: rows row0 .. row0 + n - 1 of the K / V tensors, with
+// n returned.  kv_off == nullptr: every sample owns n_fixed rows, stored sample
+// after sample ([B, n_fixed, H, d]); otherwise kv_off[B+1] are the row offsets of
+// a jagged [total, H, d] context.
+__device__ __forceinline__ int kv_rows(const int32_t* kv_off, int b, int n_fixed, size_t& row0) {
+  if (kv_off != nullptr) {
+    const int r0 = kv_off[b];
+    row0 = (size_t)r0;
+    return kv_off[b + 1] - r0;
+  }
+  row0 = (size_t)b * n_fixed;
+  return n_fixed;
+}
+
 // Largest b in [0, B-1] with tile_start[b] <= tile (tile_start non-decreasing,
 // tile_start[0] = 0).
 __device__ __forceinline__ int find_sample(const int32_t* __restrict__ tile_start, int B, int tile) {

@@ -46,7 +46,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   const int row0 = a.offsets[b] + (qtile - a.tile_start[b]) * BM;
   const int rows = min(BM, a.offsets[b + 1] - row0);
   const int seq0 = a.offsets[b];
-  const int n = SW ? a.offsets[b + 1] - seq0 : a.n;  // context rows of this sample
+  size_t crow0 = 0;  // first context row of this sample
+  const int n = SW ? a.offsets[b + 1] - seq0 : kv_rows(a.kv_offsets, b, a.n, crow0);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const int trow = wave * 32 + lr;
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       qf[ks] = tvalid ? as_bf16x8(gload16(qp + 16 * ks)) : bf16x8{};
   }
 
-  const size_t kv0 = SW ? (size_t)seq0 * H : (size_t)b * n * H;
+  const size_t kv0 = SW ? (size_t)seq0 * H : crow0 * H;
   const uint16_t* Kg = (const uint16_t*)a.k + (kv0 + h) * D;
   const uint16_t* Vg = (const uint16_t*)a.v + (kv0 + h) * D;
   // Context rows this tile needs: all n, or the band of its rows qlo .. qlo + rows - 1.
@@ -226,9 +227,11 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const FwdArgs a) {
     acc[e] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const float* Kb = (const float*)a.k + ((size_t)b * a.n * a.H + h) * D;
-  const float* Vb = (const float*)a.v + ((size_t)b * a.n * a.H + h) * D;
-  for (int j = 0; j < a.n; ++j) {
+  size_t crow0;
+  const int n = kv_rows(a.kv_offsets, b, a.n, crow0);
+  const float* Kb = (const float*)a.k + (crow0 * a.H + h) * D;
+  const float* Vb = (const float*)a.v + (crow0 * a.H + h) * D;
+  for (int j = 0; j < n; ++j) {
     const float* kj = Kb + (size_t)j * rs;
     const float* vj = Vb + (size_t)j * rs;
     float s = 0.f;

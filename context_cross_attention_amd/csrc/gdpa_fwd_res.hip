@@ -44,17 +44,19 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
   __shared__ __align__(16) uint16_t Kc[NMAX * LDK];
   __shared__ __align__(16) uint16_t Vt[D * LDV];
 
-  const int H = a.H, n = a.n;
-  const int npad = (n + 63) & ~63;
+  const int H = a.H;
   const int item = blockIdx.x;
   const int rank = item / H, h = item - rank * H;
   const int b = order[rank];
   const int seq0 = a.offsets[b], L = a.offsets[b + 1] - seq0;
   if (L == 0) return;
+  size_t crow0;
+  const int n = kv_rows(a.kv_offsets, b, a.n, crow0);  // 1 <= n <= a.n <= NMAX
+  const int npad = (n + 63) & ~63;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, g = lane >> 5;
   const size_t rs = (size_t)H * D;
-  const uint16_t* Kg = (const uint16_t*)a.k + ((size_t)b * n * H + h) * D;
-  const uint16_t* Vg = (const uint16_t*)a.v + ((size_t)b * n * H + h) * D;
+  const uint16_t* Kg = (const uint16_t*)a.k + (crow0 * H + h) * D;
+  const uint16_t* Vg = (const uint16_t*)a.v + (crow0 * H + h) * D;
 
   // Stage K row-major and V^T.  Every load is unconditional (row index clamped
   // into the sample) so the compiler keeps them in flight together; padding rows

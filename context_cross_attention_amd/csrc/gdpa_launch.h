@@ -46,6 +46,7 @@ struct FwdArgs {
   int B, T, n, H;
   float scale;
   int window;                 // sliding-window self-attention: token i sees i - window < j <= i
+  const int32_t* kv_offsets;  // [B+1] jagged context rows (n = the largest count), or nullptr
 };
 
 struct BwdArgs {
@@ -69,6 +70,7 @@ struct BwdArgs {
   const int32_t* chunk_start;
   int window;
   const int32_t* tile_start;  // [B+1] query-tile prefix sums (dQ kernel)
+  const int32_t* kv_offsets;  // [B+1] jagged context rows (n = the largest count), or nullptr
 };
 
 // Scheduling and small passes (gdpa_sched.hip).

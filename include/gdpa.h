@@ -123,6 +123,30 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
                      const void* v, const void* o, const float* lse, const void* d_o, void* dq,
                      void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Jagged context (a variant of the same op: event-level personalisation gives
+ * each event type its own number of context tokens, Kunlun paper summary,
+ * section 2.3, Event-Level Personalization bullet; Telegram review, the list of
+ * per-event hyper-parameters, n_tokens among them).  Sample b owns context rows kv_offsets[b] ..
+ * kv_offsets[b+1]-1 of k, v [rows][H][d] (dk, dv likewise); p->n_kv is the
+ * largest per-sample count (it selects the kernels and sizes the workspace,
+ * gdpa_workspace_bytes as for the dense form).  Every sample must own at least
+ * one and at most n_kv context rows (a softmax over no rows is undefined); like
+ * `offsets`, the device array is the caller's contract and gdpa_check_kv_offsets
+ * checks a host copy.  Otherwise as gdpa_fwd / gdpa_bwd; a NULL kv_offsets is
+ * GDPA_ERR_INVALID_ARGUMENT. */
+gdpa_status gdpa_fwd_jagged_kv(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
+                               const void* q, const void* k, const void* v, const void* residual,
+                               void* o, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream);
+gdpa_status gdpa_bwd_jagged_kv(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
+                               const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host-side check of a HOST copy of kv_offsets: kv_offsets[0] = 0 and every
+ * sample owns 1 .. n_kv rows; GDPA_OK or GDPA_ERR_INVALID_ARGUMENT. */
+gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv);
+
 /* Weight generation (paper summary section 2.1, interaction block; Telegram
  * review, layer step 1: K and V are obtained from the context features), read
  * as one linear map per layer with an output-major weight (the usual linear-layer
