@@ -54,9 +54,10 @@ def parse():
     ap.add_argument("--phi", default=None, choices=[None, "softmax", "silu", "relu", "gelu", "identity"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="gdpa", choices=["gdpa", "swa", "pma"],
+    ap.add_argument("--op", default="gdpa", choices=["gdpa", "swa", "pma", "jagged_kv"],
                     help="swa: sliding-window self-attention on the stacked workload's batch; "
-                         "pma: seed pooling attention over that batch")
+                         "pma: seed pooling attention over that batch; jagged_kv: GDPA fwd+bwd with "
+                         "per-sample context row counts (the fwd+bwd workload's batch)")
     ap.add_argument("--window", type=int, default=512, help="window of --op swa")
     ap.add_argument("--seeds", type=int, default=32, help="seeds of --op pma (1..32)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -332,6 +333,108 @@ def run_swa(args):
 
 
 # ---------------------------------------------------------------------------
+# GDPA with a jagged context (--op jagged_kv)
+# ---------------------------------------------------------------------------
+
+JAGGED_KV_COUNTS = ("uniform", 64, 1024)
+
+
+def run_jagged_kv(args):
+    import numpy as np
+    import torch
+
+    import context_cross_attention_amd as cca
+    import gdpa_inputs as gi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cca.load()
+    cfg = gi.CONFIGS[4]
+    phi = args.phi or "softmax"
+    H, d, B = cfg.heads, cfg.head_dim, cfg.batch
+    inp = gi.make_jagged_kv_inputs(cfg.lengths, JAGGED_KV_COUNTS, B, H, d, seed=args.seed)
+    T, n_max = int(inp.offsets[-1]), inp.n_kv
+    q, k, v, do = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.do))
+    off, ko = inp.offsets.cuda(), inp.kv_offsets.cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(cca.jagged_kv_workspace_bytes(q, off, k, n_max, phi, True), 1),
+                     dtype=torch.uint8, device="cuda")
+    marks = Marks(torch)
+
+    def step():
+        marks("gdpa_fwd", True)
+        cca.fwd_jagged_kv(q, off, ko, k, v, n_max, phi=phi, out=o, lse=lse, workspace=ws)
+        marks("gdpa_fwd", False)
+        marks("gdpa_bwd", True)
+        cca.bwd_jagged_kv(q, off, ko, k, v, n_max, o, lse, do, phi=phi, dq=dq, dk=dk, dv=dv, workspace=ws)
+        marks("gdpa_bwd", False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks.enabled = True
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    marks.enabled = False
+    pairs = float(np.dot(inp.lengths, inp.kv_counts))  # (token, context row) pairs
+    rows = int(inp.kv_counts.sum())
+    tok, kvb = T * H * d * 2, rows * H * d * 2
+    f_fwd, f_bwd = 4.0 * d * H * pairs, 8.0 * d * H * pairs
+    b_fwd = 2 * tok + 2 * kvb + (T * H * 4 if phi == "softmax" else 0)
+    b_bwd = 3 * tok + 4 * kvb + ((tok + 2 * T * H * 4) if phi == "softmax" else 0)
+    units = {"gdpa_fwd": (f_fwd, b_fwd), "gdpa_bwd": (f_bwd, b_bwd)}
+    totals, counts = marks.totals_ms(), marks.counts()
+    dom = max(totals, key=lambda x: totals[x])
+    t_dom = totals[dom] / counts[dom] * 1e-3
+    f_dom, b_dom = units[dom]
+    if b_dom / (PEAK_HBM_GBS * 1e9) >= f_dom / (PEAK_BF16_TFLOPS * 1e12):
+        roof = {"bound": "hbm", "achieved": round(b_dom / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(f_dom / t_dom / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, kernel=dom,
+                launch_ms=round(totals[dom] / counts[dom], 4),
+                algorithmic_per_launch={"flops": f_dom, "bytes": b_dom})
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "GDPA fwd+bwd TFLOP/s with a jagged context, jagged batch, 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws as in gdpa_inputs.make_jagged_kv_inputs)",
+        "config": {"workload": f"GDPA fwd+bwd, phi={phi}, jagged context: B={B}, L~U[256,2048], context rows "
+                               f"~U[{JAGGED_KV_COUNTS[1]},{JAGGED_KV_COUNTS[2]}] per sample (max {n_max}), "
+                               f"T={T}, H={H}, d={d}",
+                   "tokens": T, "context_rows": rows, "heads": H, "head_dim": d, "phi": phi, "seed": args.seed},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "breakdown_ms_per_step": {x: round(totals[x] / args.steps, 4) for x in totals},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import gdpa_oracle as orc
+        chosen, cost = [], 0.0
+        for b in range(B):
+            chosen.append(b)
+            cost += 12.0 * float(inp.lengths[b]) * float(inp.kv_counts[b]) * H * d
+            if cost >= 1.5e11:
+                break
+        t1 = time.perf_counter()
+        orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=chosen, kv_offsets=inp.kv_offsets)
+        orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi, samples=chosen, kv_offsets=inp.kv_offsets)
+        dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": cost / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"fwd+bwd on samples 0..{chosen[-1]} ({len(chosen)} of {B}); "
+                                         f"{cost / 1e9:.1f} GFLOP in {dt:.1f} s (numpy float64)",
+                               "seconds": round(dt, 2)}
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------------------
 # seed pooling attention (--op pma)
 # ---------------------------------------------------------------------------
 
@@ -454,6 +557,9 @@ def main():
         return
     if args.op == "pma":
         run_pma(args)
+        return
+    if args.op == "jagged_kv":
+        run_jagged_kv(args)
         return
 
     import numpy as np

@@ -271,6 +271,13 @@ def _jagged_problem(q, offsets, k, n_kv: int, phi: str, scale: Optional[float], 
                        default_scale(phi, d) if scale is None else float(scale), DTYPE[q.dtype], flags)
 
 
+def jagged_kv_workspace_bytes(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, n_kv: int,
+                              phi: str, backward: bool) -> int:
+    """Workspace bytes of fwd_jagged_kv (backward=False) or bwd_jagged_kv (backward=True)."""
+    prob = _jagged_problem(q, offsets, k, n_kv, phi, None, 0)
+    return int(load().gdpa_workspace_bytes(ctypes.byref(prob), 1 if backward else 0))
+
+
 def fwd_jagged_kv(q: torch.Tensor, offsets: torch.Tensor, kv_offsets: torch.Tensor, k: torch.Tensor,
                   v: torch.Tensor, n_kv: int, phi: str = "softmax", scale: Optional[float] = None,
                   residual: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,

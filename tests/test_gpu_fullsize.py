@@ -193,3 +193,34 @@ def test_fullsize_pma(gdpa_lib):
     for name, e in errs.items():
         assert e <= TOL["bf16"], (name, e)
     assert torch.isfinite(ds.float()).all()
+
+
+@pytest.mark.parametrize("phi", ["softmax", "silu"])
+def test_fullsize_jagged_kv(gdpa_lib, phi):
+    """GDPA with a jagged context at the size `bench.py --op jagged_kv` times (the
+    fwd+bwd workload's batch: B=256, L~U[256,2048], H=4, d=128; context rows
+    ~U[64,1024] per sample), on sampled samples."""
+    import bench
+    cca = gdpa_lib
+    cfg = gi.CONFIGS[4]
+    inp = gi.make_jagged_kv_inputs(cfg.lengths, bench.JAGGED_KV_COUNTS, cfg.batch, cfg.heads, cfg.head_dim, seed=0)
+    samples = pick_samples(inp.lengths)
+    say(f"case: jagged kv phi={phi} T={int(inp.offsets[-1])} rows={int(inp.kv_counts.sum())} samples={samples}")
+    q, k, v, do = (t.cuda() for t in (inp.q, inp.k, inp.v, inp.do))
+    off, ko = inp.offsets.cuda(), inp.kv_offsets.cuda()
+    o, lse = cca.fwd_jagged_kv(q, off, ko, k, v, inp.n_kv, phi=phi)
+    dq, dk, dv = cca.bwd_jagged_kv(q, off, ko, k, v, inp.n_kv, o, lse, do, phi=phi)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=samples,
+                                      kv_offsets=inp.kv_offsets)
+    dq_ref, dk_ref, dv_ref = orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi, samples=samples,
+                                               kv_offsets=inp.kv_offsets)
+    rows = rows_of(inp.offsets, samples)
+    krows = rows_of(inp.kv_offsets, samples)
+    errs = {"o": max_abs_rel(gather(o, rows), o_ref[rows]), "dq": max_abs_rel(gather(dq, rows), dq_ref[rows]),
+            "dk": max_abs_rel(gather(dk, krows), dk_ref[krows]), "dv": max_abs_rel(gather(dv, krows), dv_ref[krows])}
+    if lse is not None:
+        errs["lse"] = max_abs_rel(gather(lse, rows), lse_ref[rows])
+    say("  errors:", {n_: f"{e:.2e}" for n_, e in errs.items()})
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (name, e)
