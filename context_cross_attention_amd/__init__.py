@@ -69,7 +69,7 @@ _lib = None
 EXPORTS = ("gdpa_workspace_bytes", "gdpa_fwd", "gdpa_bwd", "gdpa_weightgen_fwd",
            "gdpa_weightgen_bwd_w", "gdpa_swa_workspace_bytes", "gdpa_swa_fwd", "gdpa_swa_bwd",
            "gdpa_pma_workspace_bytes", "gdpa_pma_fwd", "gdpa_pma_bwd",
-           "gdpa_fwd_jagged_kv", "gdpa_bwd_jagged_kv", "gdpa_check_kv_offsets",
+           "gdpa_fwd_jagged_kv", "gdpa_bwd_jagged_kv", "gdpa_check_kv_offsets", "gdpa_add_bf16",
            "gdpa_check_offsets", "gdpa_status_str", "gdpa_last_hip_error")
 
 
@@ -111,6 +111,8 @@ def load(path: str = LIB_PATH):
     lib.gdpa_fwd_jagged_kv.restype = ctypes.c_int
     lib.gdpa_bwd_jagged_kv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_bwd_jagged_kv.restype = ctypes.c_int
+    lib.gdpa_add_bf16.argtypes = [i64, vp, vp, vp, vp, vp, vp]
+    lib.gdpa_add_bf16.restype = ctypes.c_int
     lib.gdpa_check_kv_offsets.argtypes = [vp, i32, i32]
     lib.gdpa_check_kv_offsets.restype = ctypes.c_int
     lib.gdpa_check_offsets.argtypes = [vp, i32, i32, i32]
@@ -340,6 +342,18 @@ def bwd_jagged_kv(q: torch.Tensor, offsets: torch.Tensor, kv_offsets: torch.Tens
                                   _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
                                   _ptr(ws), ws.numel(), _stream()), "gdpa_bwd_jagged_kv")
     return dq, dk, dv
+
+
+def add_bf16(out: torch.Tensor, x0: torch.Tensor, x1: torch.Tensor, x2: Optional[torch.Tensor] = None,
+             x3: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out = x0 + x1 (+ x2) (+ x3), bf16 tensors of one size (out may alias an input)."""
+    for name, t in (("x0", x0), ("x1", x1), ("x2", x2), ("x3", x3)):
+        if t is not None:
+            _require(t, name, out.shape, torch.bfloat16, out.device)
+    _require(out, "out", out.shape, torch.bfloat16, out.device)
+    _check(load().gdpa_add_bf16(out.numel(), _ptr(out), _ptr(x0), _ptr(x1), _ptr(x2), _ptr(x3), _stream()),
+           "gdpa_add_bf16")
+    return out
 
 
 def check_kv_offsets(kv_offsets, n_kv: int) -> bool:

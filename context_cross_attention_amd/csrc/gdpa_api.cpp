@@ -250,6 +250,14 @@ gdpa_status gdpa_bwd_jagged_kv(const gdpa_problem* p, const int32_t* offsets, co
                   stream);
 }
 
+gdpa_status gdpa_add_bf16(int64_t count, void* out, const void* x0, const void* x1, const void* x2,
+                          const void* x3, void* stream) {
+  if (count < 0 || (count > 0 && (out == nullptr || x0 == nullptr || x1 == nullptr)))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (count % 8 != 0 || count / 8 >= (int64_t)INT32_MAX * 256) return GDPA_ERR_UNSUPPORTED;
+  return hip_status(gdpa::launch_add_bf16((long)count, out, x0, x1, x2, x3, (hipStream_t)stream));
+}
+
 gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv) {
   if (host_kv_offsets == nullptr || batch < 1 || n_kv < 1) return GDPA_ERR_INVALID_ARGUMENT;
   if (host_kv_offsets[0] != 0) return GDPA_ERR_INVALID_ARGUMENT;

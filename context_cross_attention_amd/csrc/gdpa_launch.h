@@ -79,6 +79,9 @@ struct BwdArgs {
 hipError_t launch_tile_scan(const int32_t* offsets, int B, int tile_rows, int32_t* tile_start,
                             hipStream_t s, const int32_t* order = nullptr);
 hipError_t launch_longest_first(const int32_t* offsets, int B, int32_t* order, hipStream_t s);
+// out = x0 + x1 (+ x2) (+ x3), bf16, n % 8 == 0; null x2 / x3 are skipped.
+hipError_t launch_add_bf16(long n, void* out, const void* x0, const void* x1, const void* x2,
+                           const void* x3, hipStream_t s);
 hipError_t launch_softmax_dvec(const void* o, const void* d_o, int rows, int d, bool bf16,
                                float* dvec, hipStream_t s);
 

@@ -123,6 +123,38 @@ __global__ __launch_bounds__(256) void softmax_dvec_kernel(const void* __restric
   if (row < rows && part == 0) dvec[row] = acc;
 }
 
+// out = x0 + x1 (+ x2) (+ x3) over n bf16 values (n % 8 == 0), fp32 sums rounded
+// once; out may alias any input (each thread reads its 8 values before writing).
+__global__ __launch_bounds__(256) void add_bf16_kernel(uint16_t* out, const uint16_t* x0, const uint16_t* x1,
+                                                       const uint16_t* x2, const uint16_t* x3, long n8) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const uint16_t* src[4] = {x0, x1, x2, x3};
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (src[k] == nullptr) continue;
+    const u32x4 v = *(const u32x4*)(src[k] + 8 * i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += __uint_as_float(v[e] << 16);
+      acc[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+    }
+  }
+  *(bf16x8*)(out + 8 * i) = pack8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7]);
+}
+
+hipError_t launch_add_bf16(long n, void* out, const void* x0, const void* x1, const void* x2,
+                           const void* x3, hipStream_t s) {
+  const long n8 = n / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(add_bf16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, (uint16_t*)out,
+                     (const uint16_t*)x0, (const uint16_t*)x1, (const uint16_t*)x2, (const uint16_t*)x3, n8);
+  return hipGetLastError();
+}
+
 hipError_t launch_tile_scan(const int32_t* offsets, int B, int tile_rows, int32_t* tile_start,
                             hipStream_t s, const int32_t* order) {
   hipLaunchKernelGGL(tile_scan_kernel, dim3(1), dim3(1024), 0, s, offsets, B, tile_rows,

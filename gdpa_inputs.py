@@ -307,3 +307,39 @@ def make_jagged_kv_inputs(length_spec: tuple, count_spec: tuple, batch: int, H: 
     do = draw_normal(rng, (T, H, d), dtype)
     return JaggedKvInputs(lengths, counts, torch.from_numpy(off.astype(np.int32)),
                           torch.from_numpy(kv_off.astype(np.int32)), q, k, v, do)
+
+
+@dataclass
+class LayerStackInputs:
+    """Inputs of the Kunlun layer stack: token states X0 [T,H,d], context C [B,c], per-layer
+    weight-generation matrices W_K, W_V [n*H*d, c], pooling seeds [m,H,d], upstream gradients."""
+    lengths: np.ndarray
+    offsets: torch.Tensor
+    x0: torch.Tensor
+    ctx: torch.Tensor
+    w_k: list
+    w_v: list
+    seeds: list
+    dx: torch.Tensor
+    dz: list
+
+
+def make_layer_stack_inputs(length_spec: tuple, batch: int, H: int, d: int, n: int, ctx_dim: int,
+                            layers: int, m: int, seed: int = 0) -> LayerStackInputs:
+    """Draw lengths, X0 ~ N(0,1)/sqrt(d), C ~ N(0,1), then per layer W_K, W_V ~ U(+-xavier) and
+    seeds ~ N(0,1)/sqrt(d), then dX ~ N(0,1) [T,H,d] and per layer dZ ~ N(0,1) [B,m,H,d]; bf16."""
+    rng = np.random.default_rng(seed)
+    lengths = draw_lengths(rng, length_spec, batch)
+    off = offsets_from_lengths(lengths)
+    T = int(off[-1])
+    x0 = draw_normal(rng, (T, H, d), "bf16", math.sqrt(d))
+    ctx = draw_normal(rng, (batch, ctx_dim), "bf16")
+    bound = xavier_uniform_bound(ctx_dim, n * H * d)
+    w_k, w_v, seeds = [], [], []
+    for _ in range(layers):
+        w_k.append(draw_uniform(rng, (n * H * d, ctx_dim), "bf16", bound))
+        w_v.append(draw_uniform(rng, (n * H * d, ctx_dim), "bf16", bound))
+        seeds.append(draw_normal(rng, (m, H, d), "bf16", math.sqrt(d)))
+    dx = draw_normal(rng, (T, H, d), "bf16")
+    dz = [draw_normal(rng, (batch, m, H, d), "bf16") for _ in range(layers)]
+    return LayerStackInputs(lengths, torch.from_numpy(off.astype(np.int32)), x0, ctx, w_k, w_v, seeds, dx, dz)

@@ -143,6 +143,14 @@ gdpa_status gdpa_bwd_jagged_kv(const gdpa_problem* p, const int32_t* offsets, co
                                const float* lse, const void* d_o, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Residual sums of a layer stack: out = x0 + x1 (+ x2) (+ x3) over `count` bf16
+ * values (count % 8 == 0, else GDPA_ERR_UNSUPPORTED), summed in fp32 and rounded
+ * once; x2 and x3 may be NULL; out may alias any input.  Used by layer drivers
+ * for the residual of a self-attention layer and for gradients that reach one
+ * tensor through several uses (Q = K = V = X). */
+gdpa_status gdpa_add_bf16(int64_t count, void* out, const void* x0, const void* x1, const void* x2,
+                          const void* x3, void* stream);
+
 /* Host-side check of a HOST copy of kv_offsets: kv_offsets[0] = 0 and every
  * sample owns 1 .. n_kv rows; GDPA_OK or GDPA_ERR_INVALID_ARGUMENT. */
 gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv);
