@@ -54,10 +54,13 @@ def parse():
     ap.add_argument("--phi", default=None, choices=[None, "softmax", "silu", "relu", "gelu", "identity"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="gdpa", choices=["gdpa", "swa", "pma", "jagged_kv"],
+    ap.add_argument("--op", default="gdpa", choices=["gdpa", "swa", "pma", "jagged_kv", "layers"],
                     help="swa: sliding-window self-attention on the stacked workload's batch; "
                          "pma: seed pooling attention over that batch; jagged_kv: GDPA fwd+bwd with "
-                         "per-sample context row counts (the fwd+bwd workload's batch)")
+                         "per-sample context row counts (the fwd+bwd workload's batch); layers: the "
+                         "Kunlun layer stack (GDPA + pooling + self-attention) on the stacked workload")
+    ap.add_argument("--schedule", default="compskip", choices=["compskip", "full"],
+                    help="layer schedule of --op layers (the other one is timed alongside)")
     ap.add_argument("--window", type=int, default=512, help="window of --op swa")
     ap.add_argument("--seeds", type=int, default=32, help="seeds of --op pma (1..32)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -435,6 +438,141 @@ def run_jagged_kv(args):
 
 
 # ---------------------------------------------------------------------------
+# the Kunlun layer stack with the CompSkip schedule (--op layers)
+# ---------------------------------------------------------------------------
+
+def run_layers(args):
+    import torch
+
+    import context_cross_attention_amd as cca
+    import gdpa_inputs as gi
+    from context_cross_attention_amd.layers import KunlunLayers
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cca.load()
+    cfg = gi.CONFIGS[5]
+    m, w = args.seeds, args.window
+    H, d, B, n, c, L = cfg.heads, cfg.head_dim, cfg.batch, cfg.n_kv, cfg.ctx_dim, cfg.layers
+    inp = gi.make_layer_stack_inputs(cfg.lengths, B, H, d, n, c, layers=L, m=m, seed=args.seed)
+    T = int(inp.offsets[-1])
+    dev = "cuda"
+    off, ctx = inp.offsets.to(dev), inp.ctx.to(dev)
+    wk, wv, sd = ([t.to(dev) for t in ts] for ts in (inp.w_k, inp.w_v, inp.seeds))
+    x0, dx = inp.x0.to(dev), inp.dx.to(dev)
+    gz_all = [t.to(dev) for t in inp.dz]
+
+    def time_schedule(schedule, marks):
+        model = KunlunLayers(off, ctx, wk, wv, sd, H, n, T, w, schedule)
+        gz = {l: gz_all[l] for l in range(L) if model.ops[l][1]}
+
+        def step():
+            model.forward(x0, mark=marks)
+            model.backward(dx, gz, mark=marks)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        marks.enabled = True
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        marks.enabled = False
+        del model
+        torch.cuda.empty_cache()
+        return ms
+
+    other = "full" if args.schedule == "compskip" else "compskip"
+    marks = Marks(torch)
+    ms = time_schedule(args.schedule, marks)
+    totals, counts = marks.totals_ms(), marks.counts()
+    ms_other = time_schedule(other, Marks(torch))
+    fl = layer_stack_flops(inp.lengths, H, d, n, c, m, w, L, args.schedule)
+    fl_other = layer_stack_flops(inp.lengths, H, d, n, c, m, w, L, other)
+    value = T / (ms * 1e-3)
+    # Roofline of the largest stage per launch (the self-attention backward for the
+    # default window), with the single-op models: SWA 8 d H FLOPs per pair and
+    # 8 T H d bf16 + 8 T H bytes, plus the residual sum (4 reads, 1 write); GDPA as
+    # gdpa_units.
+    tok = T * H * d * 2
+    per_launch = {"sa_bwd": (8.0 * d * H * swa_pairs(inp.lengths, w), 8 * tok + 8 * T * H + 5 * tok),
+                  "gdpa_bwd": gdpa_units("gdpa_bwd", T, B, H, d, n, "silu", residual=True)}
+    dom = max(totals, key=lambda x: totals[x])
+    roof = None
+    if dom in per_launch:
+        t_dom = totals[dom] / counts[dom] * 1e-3
+        f_dom, b_dom = per_launch[dom]
+        if b_dom / (PEAK_HBM_GBS * 1e9) >= f_dom / (PEAK_BF16_TFLOPS * 1e12):
+            roof = {"bound": "hbm", "achieved": round(b_dom / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        else:
+            roof = {"bound": "mfma", "achieved": round(f_dom / t_dom / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s"}
+        roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, kernel=dom,
+                    launch_ms=round(totals[dom] / counts[dom], 4),
+                    algorithmic_per_launch={"flops": f_dom, "bytes": b_dom})
+    out = {
+        "metric": "Kunlun layer stack (GDPA + HSP pooling + self-attention) fwd+bwd tokens/s, jagged batch, 1 MI355X",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded numpy draws as in gdpa_inputs.make_layer_stack_inputs)",
+        "config": {"workload": f"{L}-layer Kunlun stack, schedule {args.schedule}: B={B}, lengths log-normal "
+                               f"(median {cfg.lengths[1]}, max {cfg.lengths[2]}), T={T}, H={H}, d={d}, n_kv={n}, "
+                               f"ctx {c}, SiLU PFFN, {m} seeds, window {w}",
+                   "schedule": args.schedule, "layers": L, "tokens": T, "seeds": m, "window": w, "seed": args.seed},
+        "tflops": round(fl["total"] / (ms * 1e-3) / 1e12, 2),
+        "flops_per_step": {k: round(v / 1e12, 3) for k, v in fl.items()},
+        "breakdown_ms_per_step": {x: round(totals[x] / args.steps, 3) for x in totals},
+        "compare": {"schedule": other, "ms_per_step": round(ms_other, 3),
+                    "time_ratio": round(ms / ms_other, 4), "flop_ratio": round(fl["total"] / fl_other["total"], 4)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import compskip_oracle as cso
+        chosen, toks = [], 0
+        for b in range(B):
+            if 0 < inp.lengths[b] <= 1500:
+                chosen.append(b)
+                toks += int(inp.lengths[b])
+            if toks >= 12000:
+                break
+        rows = torch.cat([torch.arange(int(inp.offsets[b]), int(inp.offsets[b + 1])) for b in chosen])
+        sub_off = torch.zeros(len(chosen) + 1, dtype=torch.int64)
+        sub_off[1:] = torch.cumsum(torch.as_tensor(inp.lengths[chosen]), 0)
+        sub_ctx, sub_dz = inp.ctx[chosen], [z[chosen] for z in inp.dz]
+        t1 = time.perf_counter()
+        recs, _, zs = cso.forward(inp.x0[rows], sub_off, sub_ctx, inp.w_k, inp.w_v, inp.seeds, H, n, w,
+                                  args.schedule)
+        cso.backward(recs, sub_off, sub_ctx, inp.w_k, inp.w_v, inp.seeds, H, n, w, args.schedule, inp.dx[rows],
+                     {l: sub_dz[l] for l in zs})
+        dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": round(toks / dt, 1), "unit": "tokens/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"fwd+bwd of the {L}-layer stack on {len(chosen)} samples ({toks} tokens); "
+                                         f"{dt:.1f} s (numpy float64)", "seconds": round(dt, 2)}
+    print(json.dumps(out))
+
+
+def layer_stack_flops(lengths, H, d, n, c, m, w, layers, schedule):
+    """Algorithmic FLOPs of one forward + backward of the layer stack, per op kind:
+    GDPA 12 T H n d; weight generation 4 GEMMs of 2 B (n H d) c; pooling 14 T H m d;
+    self-attention 12 H d per in-window (token, key) pair."""
+    T, B = float(sum(int(x) for x in lengths)), len(lengths)
+    pairs = swa_pairs(lengths, w)
+    out = {"gdpa": 0.0, "weightgen": 0.0, "hsp": 0.0, "sa": 0.0}
+    for l in range(layers):
+        full = schedule == "full"
+        if full or l % 2 == 0:
+            out["gdpa"] += 12.0 * T * H * n * d
+            out["weightgen"] += 4 * 2.0 * B * (n * H * d) * c
+            out["hsp"] += 14.0 * T * H * m * d
+        if full or l % 2 == 1:
+            out["sa"] += 12.0 * H * d * pairs
+    out["total"] = sum(out.values())
+    return out
+
+
+# ---------------------------------------------------------------------------
 # seed pooling attention (--op pma)
 # ---------------------------------------------------------------------------
 
@@ -560,6 +698,9 @@ def main():
         return
     if args.op == "jagged_kv":
         run_jagged_kv(args)
+        return
+    if args.op == "layers":
+        run_layers(args)
         return
 
     import numpy as np

@@ -224,3 +224,52 @@ def test_fullsize_jagged_kv(gdpa_lib, phi):
     say("  errors:", {n_: f"{e:.2e}" for n_, e in errs.items()})
     for name, e in errs.items():
         assert e <= TOL["bf16"], (name, e)
+
+
+def test_fullsize_layers_compskip(gdpa_lib):
+    """The 4-layer Kunlun stack with the CompSkip schedule at the size `bench.py --op
+    layers` times (the stacked workload's batch; 32 seeds, window 512), on sampled
+    samples (every op keeps samples independent): final states, summaries and dX_0
+    of those samples; weight and seed gradients from a second backward whose upstream
+    gradients are zero outside them."""
+    from context_cross_attention_amd.layers import KunlunLayers
+    from oracle import compskip_oracle as cso
+    cca = gdpa_lib
+    cfg = gi.CONFIGS[5]
+    H, d, B, n, c, L, m, w = cfg.heads, cfg.head_dim, cfg.batch, cfg.n_kv, cfg.ctx_dim, cfg.layers, 32, 512
+    inp = gi.make_layer_stack_inputs(cfg.lengths, B, H, d, n, c, layers=L, m=m, seed=0)
+    T = int(inp.offsets[-1])
+    samples = pick_samples(inp.lengths, k=1)
+    say(f"case: layer stack compskip T={T} samples={samples} (lengths {[int(inp.lengths[b]) for b in samples]})")
+    dev = "cuda"
+    model = KunlunLayers(inp.offsets.to(dev), inp.ctx.to(dev), [x.to(dev) for x in inp.w_k],
+                         [x.to(dev) for x in inp.w_v], [x.to(dev) for x in inp.seeds], H, n, T, w, "compskip")
+    xl, zs = model.forward(inp.x0.to(dev))
+    xl = xl.cpu()
+    zs = {l: z.cpu() for l, z in zs.items()}
+    dx0, _, _, _ = model.backward(inp.dx.to(dev), {l: inp.dz[l].to(dev) for l in zs})
+    dx0 = dx0.cpu()
+    sel = torch.zeros(B, dtype=torch.bool)
+    sel[samples] = True
+    rows_all = torch.from_numpy(rows_of(inp.offsets, samples))
+    tok_sel = torch.zeros(T, dtype=torch.bool)
+    tok_sel[rows_all] = True
+    dx_sel = torch.where(tok_sel.view(-1, 1, 1), inp.dx, torch.zeros_like(inp.dx))
+    dz_sel = {l: torch.where(sel.view(-1, 1, 1, 1), inp.dz[l], torch.zeros_like(inp.dz[l])).to(dev) for l in zs}
+    _, dwk, dwv, dsd = model.backward(dx_sel.to(dev), dz_sel)
+    torch.cuda.synchronize()
+    sub_len = [int(inp.lengths[b]) for b in samples]
+    sub_off = np.concatenate([[0], np.cumsum(sub_len)])
+    sidx = torch.tensor(samples)
+    recs, rxl, rzs = cso.forward(inp.x0[rows_all], sub_off, inp.ctx[sidx], inp.w_k, inp.w_v, inp.seeds, H, n, w,
+                                 "compskip")
+    rdx, rwk, rwv, rsd = cso.backward(recs, sub_off, inp.ctx[sidx], inp.w_k, inp.w_v, inp.seeds, H, n, w,
+                                      "compskip", inp.dx[rows_all], {l: inp.dz[l][sidx] for l in rzs})
+    errs = {"x_last": max_abs_rel(xl[rows_all], rxl), "dx0": max_abs_rel(dx0[rows_all], rdx)}
+    errs.update({f"z{l}": max_abs_rel(zs[l][sidx], rzs[l]) for l in rzs})
+    errs.update({f"dwk{l}": max_abs_rel(dwk[l], rwk[l]) for l in rwk})
+    errs.update({f"dwv{l}": max_abs_rel(dwv[l], rwv[l]) for l in rwv})
+    errs.update({f"dseeds{l}": max_abs_rel(dsd[l], rsd[l]) for l in rsd})
+    say("  errors:", {k_: f"{e:.2e}" for k_, e in errs.items()})
+    for k_, e in errs.items():
+        assert e <= TOL["bf16"], (k_, e)
