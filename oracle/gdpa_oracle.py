@@ -132,30 +132,41 @@ def row_softmax(s: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 # ---------------------------------------------------------------------------
 
 def gdpa_forward_bh(x: np.ndarray, kb: np.ndarray, vb: np.ndarray, phi: str,
-                    scale: float) -> Tuple[np.ndarray, Optional[np.ndarray]]:
-    """O = phi(scale * x kb^T) vb for one sample and head.
+                    scale: float, sbias=None, obias=None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """O = phi(scale * x kb^T [+ sbias]) vb [+ obias] for one sample and head.
 
-    x: [L, d] query rows, kb, vb: [n, d].  Returns (O [L, d], lse [L] or None).
+    x: [L, d] query rows, kb, vb: [n, d]; sbias [n] (one per context row, the
+    FFN's hidden bias), obias [d] (the FFN's output bias).  Returns (O [L, d],
+    lse [L] or None).
     """
     s = scale * (x @ kb.T)                      # [L, n]
+    if sbias is not None:
+        s = s + sbias[None, :]
     if phi == "softmax":
         p, lse = row_softmax(s)
-        return p @ vb, lse
-    if phi in ELEMENTWISE:
-        return ELEMENTWISE[phi][0](s) @ vb, None
-    raise ValueError(phi)
+        o = p @ vb
+    elif phi in ELEMENTWISE:
+        o, lse = ELEMENTWISE[phi][0](s) @ vb, None
+    else:
+        raise ValueError(phi)
+    if obias is not None:
+        o = o + obias[None, :]
+    return o, lse
 
 
 def gdpa_backward_bh(x: np.ndarray, kb: np.ndarray, vb: np.ndarray, do: np.ndarray,
-                     phi: str, scale: float):
-    """Gradients of sum(O * dO) w.r.t. x, kb, vb for one sample and head.
+                     phi: str, scale: float, sbias=None, with_bias_grads: bool = False):
+    """Gradients of sum(O * dO) w.r.t. x, kb, vb (and the biases) for one sample and head.
 
-    Chain rule through O = P V, P = phi(S), S = scale x kb^T:
+    Chain rule through O = P V + obias, P = phi(S), S = scale x kb^T + sbias:
       dV = P^T dO;  dP = dO V^T;
-      softmax: dS = P * (dP - rowsum(dO * O));  elementwise: dS = dP * phi'(S);
-      dX = scale dS kb;  dK = scale dS^T x.
+      softmax: dS = P * (dP - rowsum(dO * (P V)));  elementwise: dS = dP * phi'(S);
+      dX = scale dS kb;  dK = scale dS^T x;  dsbias = column sums of dS;
+      dobias = column sums of dO.
     """
     s = scale * (x @ kb.T)
+    if sbias is not None:
+        s = s + sbias[None, :]
     dp = do @ vb.T
     if phi == "softmax":
         p, _ = row_softmax(s)
@@ -171,6 +182,8 @@ def gdpa_backward_bh(x: np.ndarray, kb: np.ndarray, vb: np.ndarray, do: np.ndarr
     dv = p.T @ do
     dx = scale * (ds @ kb)
     dk = scale * (ds.T @ x)
+    if with_bias_grads:
+        return dx, dk, dv, ds.sum(axis=0), do.sum(axis=0)
     return dx, dk, dv
 
 
@@ -213,8 +226,18 @@ def _context(k, v, b, h, kv_offsets):
     return k[r, h, :], v[r, h, :]
 
 
+def _score_bias(sb, b, h, kv_offsets):
+    """Score bias of sample b, head h: [B,n,H] dense or [rows,H] jagged, or None."""
+    if sb is None:
+        return None
+    if kv_offsets is None:
+        return sb[b, :, h]
+    return sb[int(kv_offsets[b]):int(kv_offsets[b + 1]), h]
+
+
 def gdpa_forward(q, offsets, k, v, phi: str = "softmax", scale: Optional[float] = None,
-                 samples: Optional[Sequence[int]] = None, kv_offsets=None):
+                 samples: Optional[Sequence[int]] = None, kv_offsets=None, score_bias=None,
+                 out_bias=None):
     """Forward over a jagged batch.
 
     q: [T,H,d]; offsets: [B+1]; k, v: [B,n,H,d], or with kv_offsets [B+1] a jagged
@@ -229,6 +252,8 @@ def gdpa_forward(q, offsets, k, v, phi: str = "softmax", scale: Optional[float] 
     else:
         kv_offsets = np.asarray(as_f64(kv_offsets), dtype=np.int64)
         T, H, d, B = _check_jagged(q, offsets, kv_offsets, k, v)
+    sb = None if score_bias is None else as_f64(score_bias)    # [B,n,H] or [rows,H]
+    ob = None if out_bias is None else as_f64(out_bias)        # [B,H,d]
     if scale is None:
         scale = default_scale(phi, d)
     o = np.full((T, H, d), np.nan)
@@ -237,19 +262,22 @@ def gdpa_forward(q, offsets, k, v, phi: str = "softmax", scale: Optional[float] 
         r0, r1 = int(offsets[b]), int(offsets[b + 1])
         for h in range(H):
             kb, vb = _context(k, v, b, h, kv_offsets)
-            ob, lb = gdpa_forward_bh(q[r0:r1, h, :], kb, vb, phi, scale)
-            o[r0:r1, h, :] = ob
+            ohb, lb = gdpa_forward_bh(q[r0:r1, h, :], kb, vb, phi, scale, _score_bias(sb, b, h, kv_offsets),
+                                      None if ob is None else ob[b, h])
+            o[r0:r1, h, :] = ohb
             if lse is not None:
                 lse[r0:r1, h] = lb
     return o, lse
 
 
 def gdpa_backward(q, offsets, k, v, do, phi: str = "softmax", scale: Optional[float] = None,
-                  samples: Optional[Sequence[int]] = None, kv_offsets=None):
-    """Backward over a jagged batch: (dQ [T,H,d], dK, dV shaped like K, V).
+                  samples: Optional[Sequence[int]] = None, kv_offsets=None, score_bias=None,
+                  bias_grads: bool = False):
+    """Backward over a jagged batch: (dQ [T,H,d], dK, dV shaped like K, V), and with
+    bias_grads also (d score_bias shaped like K without d, d out_bias [B,H,d]).
 
-    dK and dV are sums over each sample's own tokens; an empty sample gets zeros.
-    With `samples`, rows and K/V slots of other samples stay NaN.
+    dK, dV and the bias gradients are sums over each sample's own tokens; an
+    empty sample gets zeros.  With `samples`, other samples' slots stay NaN.
     """
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     offsets = np.asarray(as_f64(offsets), dtype=np.int64)
@@ -260,22 +288,31 @@ def gdpa_backward(q, offsets, k, v, do, phi: str = "softmax", scale: Optional[fl
         T, H, d, B = _check_jagged(q, offsets, kv_offsets, k, v)
     if scale is None:
         scale = default_scale(phi, d)
+    sb = None if score_bias is None else as_f64(score_bias)
     dq = np.full((T, H, d), np.nan)
     dk = np.full(k.shape, np.nan)
     dv = np.full(v.shape, np.nan)
+    dsb = np.full(k.shape[:-1], np.nan)
+    dob = np.full((B, H, d), np.nan)
     for b in (range(B) if samples is None else samples):
         r0, r1 = int(offsets[b]), int(offsets[b + 1])
         for h in range(H):
             kb, vb = _context(k, v, b, h, kv_offsets)
-            gx, gk, gv = gdpa_backward_bh(q[r0:r1, h, :], kb, vb, do[r0:r1, h, :], phi, scale)
+            gx, gk, gv, gsb, gob = gdpa_backward_bh(q[r0:r1, h, :], kb, vb, do[r0:r1, h, :], phi, scale,
+                                                    _score_bias(sb, b, h, kv_offsets), with_bias_grads=True)
             dq[r0:r1, h, :] = gx
+            dob[b, h] = gob
             if kv_offsets is None:
                 dk[b, :, h, :] = gk
                 dv[b, :, h, :] = gv
+                dsb[b, :, h] = gsb
             else:
                 c = slice(int(kv_offsets[b]), int(kv_offsets[b + 1]))
                 dk[c, h, :] = gk
                 dv[c, h, :] = gv
+                dsb[c, h] = gsb
+    if bias_grads:
+        return dq, dk, dv, dsb, dob
     return dq, dk, dv
 
 

@@ -26,8 +26,10 @@ def _wrong_softmax(s):
 
 
 def _backward_factory(kind):
-    def bwd(x, kb, vb, do, phi, scale):
+    def bwd(x, kb, vb, do, phi, scale, sbias=None, with_bias_grads=False):
         s = scale * (x @ kb.T)
+        if sbias is not None:
+            s = s + sbias[None, :]
         dp = do @ vb.T
         if phi == "softmax":
             p, _ = orc.row_softmax(s)
@@ -40,6 +42,8 @@ def _backward_factory(kind):
         dv = (do.T @ p).T if kind != "transpose_dv" else (p.T @ do)[::-1]
         dx = scale * (ds @ kb)
         dk = (ds.T @ x) if kind == "no_scale_dk" else scale * (ds.T @ x)
+        if with_bias_grads:
+            return dx, dk, dv, ds.sum(axis=0), do.sum(axis=0)
         return dx, dk, dv
     return bwd
 
