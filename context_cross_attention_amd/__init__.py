@@ -70,6 +70,7 @@ EXPORTS = ("gdpa_workspace_bytes", "gdpa_fwd", "gdpa_bwd", "gdpa_weightgen_fwd",
            "gdpa_weightgen_bwd_w", "gdpa_swa_workspace_bytes", "gdpa_swa_fwd", "gdpa_swa_bwd",
            "gdpa_pma_workspace_bytes", "gdpa_pma_fwd", "gdpa_pma_bwd",
            "gdpa_fwd_jagged_kv", "gdpa_bwd_jagged_kv", "gdpa_check_kv_offsets", "gdpa_add_bf16",
+           "gdpa_fwd_biased", "gdpa_bwd_biased", "gdpa_biased_workspace_bytes",
            "gdpa_check_offsets", "gdpa_status_str", "gdpa_last_hip_error")
 
 
@@ -111,6 +112,12 @@ def load(path: str = LIB_PATH):
     lib.gdpa_fwd_jagged_kv.restype = ctypes.c_int
     lib.gdpa_bwd_jagged_kv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_bwd_jagged_kv.restype = ctypes.c_int
+    lib.gdpa_biased_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
+    lib.gdpa_biased_workspace_bytes.restype = sz
+    lib.gdpa_fwd_biased.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_fwd_biased.restype = ctypes.c_int
+    lib.gdpa_bwd_biased.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_bwd_biased.restype = ctypes.c_int
     lib.gdpa_add_bf16.argtypes = [i64, vp, vp, vp, vp, vp, vp]
     lib.gdpa_add_bf16.restype = ctypes.c_int
     lib.gdpa_check_kv_offsets.argtypes = [vp, i32, i32]
@@ -171,11 +178,14 @@ def workspace_bytes(prob: GdpaProblem, backward: bool) -> int:
     return int(load().gdpa_workspace_bytes(ctypes.byref(prob), 1 if backward else 0))
 
 
-def _workspace(prob: GdpaProblem, backward: bool, device, workspace: Optional[torch.Tensor]):
-    need = workspace_bytes(prob, backward)
+def _sized_workspace(need: int, device, workspace: Optional[torch.Tensor]):
     if workspace is not None and workspace.numel() >= need:
         return workspace
     return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+
+def _workspace(prob: GdpaProblem, backward: bool, device, workspace: Optional[torch.Tensor]):
+    return _sized_workspace(workspace_bytes(prob, backward), device, workspace)
 
 
 def fwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
@@ -354,6 +364,80 @@ def add_bf16(out: torch.Tensor, x0: torch.Tensor, x1: torch.Tensor, x2: Optional
     _check(load().gdpa_add_bf16(out.numel(), _ptr(out), _ptr(x0), _ptr(x1), _ptr(x2), _ptr(x3), _stream()),
            "gdpa_add_bf16")
     return out
+
+
+def _biased_shapes(q, offsets, k, kv_offsets, n_kv):
+    T, H, d = q.shape
+    B = offsets.shape[0] - 1
+    if kv_offsets is None:
+        n = k.shape[1]
+        return B, n, (B, n, H, d), (B, n, H)
+    if n_kv is None:
+        raise ValueError("a jagged context needs n_kv, the largest per-sample row count")
+    return B, int(n_kv), (k.shape[0], H, d), (k.shape[0], H)
+
+
+def fwd_biased(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+               score_bias: Optional[torch.Tensor], out_bias: Optional[torch.Tensor], phi: str = "softmax",
+               scale: Optional[float] = None, kv_offsets: Optional[torch.Tensor] = None,
+               n_kv: Optional[int] = None, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """GDPA forward with FFN biases: O = phi(scale Q K^T + score_bias) V + out_bias.
+    score_bias float32 [B,n,H] (or [rows,H] with kv_offsets), out_bias float32 [B,H,d];
+    either may be None.  Returns (o, lse for softmax else None)."""
+    lib = load()
+    T, H, d = q.shape
+    dev = q.device
+    B, n, kshape, sbshape = _biased_shapes(q, offsets, k, kv_offsets, n_kv)
+    _require(offsets, "offsets", (B + 1,), torch.int32, dev)
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, kshape, q.dtype, dev)
+    if kv_offsets is not None:
+        _require(kv_offsets, "kv_offsets", (B + 1,), torch.int32, dev)
+    if score_bias is not None:
+        _require(score_bias, "score_bias", sbshape, torch.float32, dev)
+    if out_bias is not None:
+        _require(out_bias, "out_bias", (B, H, d), torch.float32, dev)
+    out = torch.empty_like(q) if out is None else out
+    _require(out, "out", (T, H, d), q.dtype, dev)
+    lse = (torch.empty((T, H), dtype=torch.float32, device=dev) if lse is None else lse) if phi == "softmax" else None
+    prob = _jagged_problem(q, offsets, k, n, phi, scale, 0)
+    ws = _workspace(prob, False, dev, workspace)
+    _check(lib.gdpa_fwd_biased(ctypes.byref(prob), _ptr(offsets), _ptr(kv_offsets), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(score_bias), _ptr(out_bias), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                               _stream()), "gdpa_fwd_biased")
+    return out, lse
+
+
+def bwd_biased(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+               score_bias: Optional[torch.Tensor], out_bias: Optional[torch.Tensor], o: Optional[torch.Tensor],
+               lse: Optional[torch.Tensor], do: torch.Tensor, phi: str = "softmax", scale: Optional[float] = None,
+               kv_offsets: Optional[torch.Tensor] = None, n_kv: Optional[int] = None,
+               workspace: Optional[torch.Tensor] = None):
+    """Backward of fwd_biased: returns (dq, dk, dv, d_score_bias, d_out_bias)."""
+    lib = load()
+    T, H, d = q.shape
+    dev = q.device
+    B, n, kshape, sbshape = _biased_shapes(q, offsets, k, kv_offsets, n_kv)
+    _require(offsets, "offsets", (B + 1,), torch.int32, dev)
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, kshape, q.dtype, dev)
+    _require(do, "do", (T, H, d), q.dtype, dev)
+    if phi == "softmax":
+        _require(o, "o", (T, H, d), q.dtype, dev)
+        _require(lse, "lse", (T, H), torch.float32, dev)
+    else:
+        o, lse = None, None
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsb = torch.empty(sbshape, dtype=torch.float32, device=dev)
+    dob = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    prob = _jagged_problem(q, offsets, k, n, phi, scale, 0)
+    need = lib.gdpa_biased_workspace_bytes(ctypes.byref(prob), 1, int(out_bias is not None))
+    ws = _sized_workspace(need, dev, workspace)
+    _check(lib.gdpa_bwd_biased(ctypes.byref(prob), _ptr(offsets), _ptr(kv_offsets), _ptr(q), _ptr(k), _ptr(v),
+                               _ptr(score_bias), _ptr(out_bias), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(dsb), _ptr(dob), _ptr(ws), ws.numel(), _stream()), "gdpa_bwd_biased")
+    return dq, dk, dv, dsb, dob
 
 
 def check_kv_offsets(kv_offsets, n_kv: int) -> bool:

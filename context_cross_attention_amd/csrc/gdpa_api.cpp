@@ -81,6 +81,29 @@ size_t fwd_workspace(const gdpa_problem* p) {
   return align_up(sizeof(int32_t) * ((size_t)p->batch + 1)) + align_up(sizeof(int32_t) * (size_t)p->batch);
 }
 
+// Biased backward, softmax, bf16, with an output bias: the softmax row term
+// sum_e (P V)[e] dO[e] cannot come from the bf16 O = P V + b_o (its rounding is
+// relative to |P V + b_o|, which a large bias makes far coarser than |P V|), so the
+// backward recomputes P V once without the bias into its workspace.  Layout after
+// the backward plan: forward workspace | P V [T*H*d] bf16 | LSE [T*H] fp32.
+struct RecomputePlan {
+  bool on = false;
+  size_t fwd_off = 0, o_off = 0, lse_off = 0, total = 0;
+};
+
+RecomputePlan recompute_plan(const gdpa_problem* p, size_t base, bool out_bias) {
+  RecomputePlan r;
+  r.total = base;
+  r.on = out_bias && p->dtype == GDPA_BF16 && p->phi == GDPA_PHI_SOFTMAX;
+  if (!r.on) return r;
+  const size_t TH = (size_t)p->total_tokens * p->heads;
+  r.fwd_off = base;
+  r.o_off = r.fwd_off + fwd_workspace(p);
+  r.lse_off = r.o_off + align_up(TH * p->head_dim * 2);
+  r.total = r.lse_off + align_up(TH * sizeof(float));
+  return r;
+}
+
 }  // namespace
 
 extern "C" {
@@ -88,6 +111,12 @@ extern "C" {
 size_t gdpa_workspace_bytes(const gdpa_problem* p, int backward) {
   if (check_problem(p) != GDPA_OK) return 0;
   return backward ? bwd_plan(p).total : fwd_workspace(p);
+}
+
+size_t gdpa_biased_workspace_bytes(const gdpa_problem* p, int backward, int out_bias) {
+  if (check_problem(p) != GDPA_OK) return 0;
+  if (!backward) return fwd_workspace(p);
+  return recompute_plan(p, bwd_plan(p).total, out_bias != 0).total;
 }
 
 }  // extern "C"
@@ -98,7 +127,8 @@ namespace {
 // with kv_offsets) context forms; kv_offsets == nullptr selects the dense one.
 gdpa_status fwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
                      const void* q, const void* k, const void* v, const void* residual, void* o,
-                     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                     const float* score_bias = nullptr, const float* out_bias = nullptr) {
   const gdpa_status st = check_problem(p);
   if (st != GDPA_OK) return st;
   if (offsets == nullptr || k == nullptr || v == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
@@ -123,6 +153,8 @@ gdpa_status fwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
   a.o = o;
   a.lse = (p->phi == GDPA_PHI_SOFTMAX) ? lse : nullptr;
   a.kv_offsets = kv_offsets;
+  a.score_bias = score_bias;
+  a.out_bias = out_bias;
   a.B = p->batch;
   a.T = p->total_tokens;
   a.n = p->n_kv;
@@ -147,7 +179,9 @@ gdpa_status fwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
 gdpa_status bwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
                      const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* d_o, void* dq, void* dk, void* dv, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     size_t workspace_bytes, void* stream, const float* score_bias = nullptr,
+                     const float* out_bias = nullptr, float* d_score_bias = nullptr,
+                     float* d_out_bias = nullptr) {
   const gdpa_status st = check_problem(p);
   if (st != GDPA_OK) return st;
   if (offsets == nullptr || k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)
@@ -164,7 +198,8 @@ gdpa_status bwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
   if (dq != nullptr && dq == d_o && !accum && !dq_resid) return GDPA_ERR_INVALID_ARGUMENT;
   if (dk == dv || dk == k || dk == v || dv == k || dv == v) return GDPA_ERR_INVALID_ARGUMENT;
   const BwdPlan pl = bwd_plan(p);
-  if (workspace == nullptr || workspace_bytes < pl.total) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  const RecomputePlan rp = recompute_plan(p, pl.total, out_bias != nullptr);
+  if (workspace == nullptr || workspace_bytes < rp.total) return GDPA_ERR_WORKSPACE_TOO_SMALL;
 
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -182,6 +217,8 @@ gdpa_status bwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
   a.dv = dv;
   a.tile_start = pl.split_dq ? (const int32_t*)(ws + pl.tile_off) : nullptr;
   a.kv_offsets = kv_offsets;
+  a.score_bias = score_bias;
+  a.d_score_bias = d_score_bias;
   a.B = p->batch;
   a.T = p->total_tokens;
   a.n = p->n_kv;
@@ -192,9 +229,24 @@ gdpa_status bwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
 
   const size_t TH = (size_t)p->total_tokens * p->heads;
   hipError_t e = hipSuccess;
-  if (softmax && TH > 0) {
+  if (softmax && TH > 0 && rp.on) {
+    gdpa_problem fp = *p;
+    fp.flags = 0;
+    const gdpa_status fs = fwd_impl(&fp, offsets, kv_offsets, q, k, v, nullptr, ws + rp.o_off,
+                                    (float*)(ws + rp.lse_off), ws + rp.fwd_off, fwd_workspace(p), stream,
+                                    score_bias, nullptr);
+    if (fs != GDPA_OK) return fs;
+    e = gdpa::launch_softmax_dvec(ws + rp.o_off, d_o, (int)TH, p->head_dim, true, (float*)(ws + pl.dvec_off),
+                                  s);
+    if (e != hipSuccess) return hip_status(e);
+  } else if (softmax && TH > 0) {
     e = gdpa::launch_softmax_dvec(o, d_o, (int)TH, p->head_dim, p->dtype == GDPA_BF16,
-                                  (float*)(ws + pl.dvec_off), s);
+                                  (float*)(ws + pl.dvec_off), s, offsets, p->batch, p->heads, out_bias);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (d_out_bias != nullptr) {
+    e = gdpa::launch_out_bias_grad(offsets, d_o, p->batch, p->heads, p->head_dim, p->dtype == GDPA_BF16,
+                                   d_out_bias, s);
     if (e != hipSuccess) return hip_status(e);
   }
   if (p->dtype == GDPA_F32) return hip_status(gdpa::launch_bwd_f32(a, p->head_dim, p->phi, s));
@@ -256,6 +308,30 @@ gdpa_status gdpa_add_bf16(int64_t count, void* out, const void* x0, const void* 
     return GDPA_ERR_INVALID_ARGUMENT;
   if (count % 8 != 0 || count / 8 >= (int64_t)INT32_MAX * 256) return GDPA_ERR_UNSUPPORTED;
   return hip_status(gdpa::launch_add_bf16((long)count, out, x0, x1, x2, x3, (hipStream_t)stream));
+}
+
+gdpa_status gdpa_fwd_biased(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
+                            const void* q, const void* k, const void* v, const float* score_bias,
+                            const float* out_bias, void* o, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (p != nullptr && p->flags != 0) return GDPA_ERR_UNSUPPORTED;  // no residual with biases
+  return fwd_impl(p, offsets, kv_offsets, q, k, v, nullptr, o, lse, workspace, workspace_bytes, stream,
+                  score_bias, out_bias);
+}
+
+gdpa_status gdpa_bwd_biased(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
+                            const void* q, const void* k, const void* v, const float* score_bias,
+                            const float* out_bias, const void* o, const float* lse, const void* d_o,
+                            void* dq, void* dk, void* dv, float* d_score_bias, float* d_out_bias,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (p != nullptr && p->flags != 0) return GDPA_ERR_UNSUPPORTED;  // plain dQ with biases
+  if (d_score_bias != nullptr && (d_score_bias == score_bias || (const void*)d_score_bias == k ||
+                                  (const void*)d_score_bias == v))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  if (d_out_bias != nullptr && (d_out_bias == out_bias || (const void*)d_out_bias == d_o))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  return bwd_impl(p, offsets, kv_offsets, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes,
+                  stream, score_bias, out_bias, d_score_bias, d_out_bias);
 }
 
 gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv) {

@@ -36,7 +36,9 @@ __device__ __forceinline__ int qpos(int t) { return (t & ~7) | ((t & 3) << 1) | 
 // outside i - window < j <= i get P = dS = 0.
 // DQ = false: dK and dV only (dQ comes from the query-tile kernel of gdpa_bwd_dq.hip,
 // used whenever several key chunks feed a query row).
-template <int D, int PHI, int NW, bool SW = false, bool DQ = true>
+// BIAS: FFN score bias a.score_bias (per context row, added to the scaled score)
+// and its gradient a.d_score_bias (the sum of the score gradient over the tokens).
+template <int D, int PHI, int NW, bool SW = false, bool DQ = true, bool BIAS = false>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   constexpr int NJ = 32 * NW;          // context rows per work-group
   constexpr int BQ = kBwdRowsPerWave;  // query rows per step
@@ -105,6 +107,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   const int jl = 32 * wave + lr;  // local context row of this lane
   const int jw = j0 + jl;
   const bool jvalid = jw < n;
+  const float sbj = (BIAS && a.score_bias != nullptr && jvalid) ? a.score_bias[(crow0 + jw) * H + h] : 0.f;
+  float dsb = 0.f;  // sum over the tokens of the score gradient of row jw (BIAS)
   bf16x8 vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -195,11 +199,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
       const int t = 8 * (r >> 2) + 4 * g + (r & 3);
       float p, ds;
       if (PHI == 0) {
-        p = fast_exp2(S[r] * sl2 - lse_s[t]);
+        p = fast_exp2(BIAS ? fmaf(sbj, kLog2e, S[r] * sl2) - lse_s[t] : S[r] * sl2 - lse_s[t]);
         ds = p * (dP[r] - dvec_s[t]);
       } else {
         float gr;
-        p = phi_value_grad<PHI>(S[r] * a.scale, gr);
+        p = phi_value_grad<PHI>(BIAS ? fmaf(S[r], a.scale, sbj) : S[r] * a.scale, gr);
         ds = dP[r] * gr;
       }
       if (!jvalid || (SW && (jw > tq + t || jw <= tq + t - a.window))) {
@@ -207,6 +211,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
         ds = 0.f;
       }
       P[r] = p;
+      if (BIAS) dsb += ds;  // rows past the sample have dO = 0, so ds = 0 there
       dS[r] = ds * a.scale;
     }
 
@@ -265,6 +270,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
     }
   }
 
+  if (BIAS && a.d_score_bias != nullptr) {
+    dsb += wave_xor32(dsb);
+    if (g == 0 && jvalid) a.d_score_bias[(crow0 + jw) * H + h] = dsb;
+  }
   // dK, dV: lane (d + 32 g), register r holds context row 32 w + 8 (r / 4) + 4 g + r % 4.
   uint16_t* dkp = (uint16_t*)a.dk + (kv0 + h) * D;
   uint16_t* dvp = (uint16_t*)a.dv + (kv0 + h) * D;
@@ -287,8 +296,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
 
 template <int D, int PHI>
 __device__ __forceinline__ void f32_ds(float s_raw, float dp, float scale, float lse, float dvec,
-                                       float& p, float& ds) {
-  const float s = s_raw * scale;
+                                       float& p, float& ds, float bias = 0.f) {
+  const float s = fmaf(s_raw, scale, bias);
   if (PHI == 0) {
     p = expf(s - lse);
     ds = p * (dp - dvec);
@@ -338,7 +347,8 @@ __global__ __launch_bounds__(128) void bwd_f32_dq_kernel(const BwdArgs a) {
       dp = fmaf(dop[e], vj[e], dp);
     }
     float p, ds;
-    f32_ds<D, PHI>(s, dp, a.scale, lse, dvec, p, ds);
+    f32_ds<D, PHI>(s, dp, a.scale, lse, dvec, p, ds,
+                   a.score_bias != nullptr ? a.score_bias[(crow0 + j) * a.H + h] : 0.f);
     ds *= a.scale;
 #pragma unroll
     for (int e = 0; e < D; ++e) acc[e] = fmaf(ds, kj[e], acc[e]);
@@ -367,6 +377,8 @@ __global__ __launch_bounds__(128) void bwd_f32_dkdv_kernel(const BwdArgs a) {
   const size_t rs = (size_t)a.H * D;
   const float* kj = (const float*)a.k + (crow0 + j) * rs + (size_t)h * D;
   const float* vj = (const float*)a.v + (crow0 + j) * rs + (size_t)h * D;
+  const float sbj = a.score_bias != nullptr ? a.score_bias[(crow0 + j) * a.H + h] : 0.f;
+  float dsb = 0.f;
   float gk[32], gv[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
@@ -385,7 +397,8 @@ __global__ __launch_bounds__(128) void bwd_f32_dkdv_kernel(const BwdArgs a) {
     const float lse = PHI == 0 ? a.lse[(size_t)t * a.H + h] : 0.f;
     const float dvec = PHI == 0 ? a.dvec[(size_t)t * a.H + h] : 0.f;
     float p, ds;
-    f32_ds<D, PHI>(s, dp, a.scale, lse, dvec, p, ds);
+    f32_ds<D, PHI>(s, dp, a.scale, lse, dvec, p, ds, sbj);
+    dsb += ds;
     ds *= a.scale;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
@@ -393,6 +406,7 @@ __global__ __launch_bounds__(128) void bwd_f32_dkdv_kernel(const BwdArgs a) {
       gk[e] = fmaf(ds, qp[32 * sl + e], gk[e]);
     }
   }
+  if (sl == 0 && a.d_score_bias != nullptr) a.d_score_bias[(crow0 + j) * a.H + h] = dsb;
   float* dkp = (float*)a.dk + (crow0 + j) * rs + (size_t)h * D + 32 * sl;
   float* dvp = (float*)a.dv + (crow0 + j) * rs + (size_t)h * D + 32 * sl;
 #pragma unroll
@@ -418,9 +432,13 @@ static hipError_t bwd_bf16_dw(const BwdArgs& a, int phi, bool with_dq, hipStream
   const long items = (long)a.B * a.H * a.n_chunks;
   if (items == 0) return hipSuccess;
   const dim3 g((unsigned)items), blk(NW * 64);
+  const bool biased = a.score_bias != nullptr || a.d_score_bias != nullptr;
   return dispatch_phi(phi, [&](auto P) {
-    if (with_dq) hipLaunchKernelGGL((bwd_bf16_kernel<D, decltype(P)::value, NW, false, true>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((bwd_bf16_kernel<D, decltype(P)::value, NW, false, false>), g, blk, 0, s, a);
+    constexpr int PH = decltype(P)::value;
+    if (biased && with_dq) hipLaunchKernelGGL((bwd_bf16_kernel<D, PH, NW, false, true, true>), g, blk, 0, s, a);
+    else if (biased) hipLaunchKernelGGL((bwd_bf16_kernel<D, PH, NW, false, false, true>), g, blk, 0, s, a);
+    else if (with_dq) hipLaunchKernelGGL((bwd_bf16_kernel<D, PH, NW, false, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_bf16_kernel<D, PH, NW, false, false>), g, blk, 0, s, a);
     return hipGetLastError();
   });
 }

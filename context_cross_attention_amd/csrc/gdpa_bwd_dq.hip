@@ -17,7 +17,8 @@
 
 namespace gdpa {
 
-template <int D, int PHI, bool SW>
+// BIAS: FFN score bias a.score_bias added to the scaled scores (never with SW).
+template <int D, int PHI, bool SW, bool BIAS = false>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   constexpr int BM = kFwdTileRows, BN = 64, KS = D / 16, DT = D / 32;
   constexpr int LD = D + 8;                   // K and V rows (16-byte reads of 16 rows: distinct banks)
@@ -25,6 +26,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   constexpr int SI = (BN * CH + 255) / 256;   // staging chunks per thread per tensor
   __shared__ __align__(16) uint16_t Ks[BN * LD];
   __shared__ __align__(16) uint16_t Vs[BN * LD];
+  __shared__ __align__(16) float Sbl[BIAS ? BN : 4];  // score bias of the block's rows
 
   const int H = a.H, B = a.B;
   const int total = a.tile_start[B];
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
       vreg[i] = ok ? gload16(Vg + (size_t)(jb + j) * rs + 8 * c) : u32x4{};
     }
   };
-  auto store_block = [&]() {
+  auto store_block = [&](int jb) {
 #pragma unroll
     for (int i = 0; i < SI; ++i) {
       const int idx = i * 256 + tid, j = idx / CH, c = idx % CH;
@@ -81,6 +83,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
         lds_write16(&Vs[j * LD + 8 * c], vreg[i]);
       }
     }
+    if (BIAS && tid < BN)
+      Sbl[tid] = (a.score_bias != nullptr && jb + tid < n) ? a.score_bias[(crow0 + jb + tid) * H + h] : 0.f;
   };
   // Transpose reads of K (as in the forward's V^T): lane 16 G + 4 r + c reads row
   // 4 (G / 2) + r, columns 16 (G % 2) + 4 c of a 32-row slab (second read: rows + 8),
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   if (jbeg < jend) gload_block(jbeg);
   for (int jb = jbeg; jb < jend; jb += BN) {
     __syncthreads();
-    store_block();
+    store_block(jb);
     __syncthreads();
     if (jb + BN < jend) gload_block(jb + BN);
 
@@ -110,16 +114,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
         dP = mfma32(lds_read8(&Vs[o]), dof[ks], dP);
       }
       // Lane (t + 32 g), register r: context row jb + 32 mt + 8 (r / 4) + 4 g + r % 4.
+      float bj[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 bv = BIAS ? *(const GDPA_LDS f32x4*)&Sbl[32 * mt + 8 * q + 4 * g] : f32x4{};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bj[4 * q + i] = bv[i];
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = jb + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
         float ds;
         if (PHI == kPhiSoftmax) {
-          const float p = fast_exp2(fmaf(S[r], sl2, -lse2));
+          const float p = fast_exp2(fmaf(S[r], sl2, BIAS ? fmaf(bj[r], kLog2e, -lse2) : -lse2));
           ds = p * (dP[r] - dvec);
         } else {
           float gr;
-          phi_value_grad<PHI>(S[r] * a.scale, gr);
+          phi_value_grad<PHI>(BIAS ? fmaf(S[r], a.scale, bj[r]) : S[r] * a.scale, gr);
           ds = dP[r] * gr;
         }
         if (j >= n || (SW && (j > irow || j <= irow - a.window))) ds = 0.f;
@@ -167,8 +178,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
 
 template <int D, bool SW>
 static hipError_t bwd_dq_d(const BwdArgs& a, int phi, int grid, hipStream_t s) {
+  const bool biased = !SW && a.score_bias != nullptr;
   return dispatch_phi(phi, [&](auto P) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D, decltype(P)::value, SW>), dim3(grid), dim3(256), 0, s, a);
+    if (biased) hipLaunchKernelGGL((bwd_dq_kernel<D, decltype(P)::value, false, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((bwd_dq_kernel<D, decltype(P)::value, SW>), dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
   });
 }

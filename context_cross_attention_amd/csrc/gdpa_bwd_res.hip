@@ -59,7 +59,8 @@ __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 
 __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 }  // namespace
 
-// DQB: 0 dQ = result, 1 dQ = dO + result (dO from LDS), 2 dQ = dQ + result.
+// DQB: 0 dQ = result, 1 dQ = dO + result (dO from LDS), 2 dQ = dQ + result,
+// 3 dQ = result with the FFN score bias (a.score_bias, gradient into a.d_score_bias).
 template <int PHI, int DQB>
 __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   constexpr int D = 128, NT = 512, NJ = 256, BQ = 32, KS = D / 16, DT = D / 32;
@@ -91,6 +92,10 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   const size_t rs = (size_t)H * D;
   const int j = 32 * wave + lr;  // this lane's context row in the S / dP C tiles
   const bool jvalid = j < n;
+  // FFN score bias of this lane's row (DQB 3), and the running sum of its score gradient.
+  const float sbj = (DQB == 3 && a.score_bias != nullptr && jvalid) ? a.score_bias[(crow0 + j) * H + h] : 0.f;
+  const float sbj2 = sbj * kLog2e;
+  float dsb = 0.f;
 
   // K and V rows of this wave as B operands (lane (j + 32 g), items d = 16 ks + 8 g + i),
   // zero past n; K^T written into LDS from the same registers (32 consecutive j per
@@ -217,7 +222,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * q4 + c;
-          float p = fast_exp2(fmaf(S[r], sl2, -ls[c] * kLog2e));
+          float p = fast_exp2(fmaf(S[r], sl2, DQB == 3 ? fmaf(-ls[c], kLog2e, sbj2) : -ls[c] * kLog2e));
           if (!jvalid) p = 0.f;
           S[r] = p;
           dP[r] = p * (dP[r] - dvv[c]);
@@ -226,8 +231,8 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
     } else if (PHI == kPhiSilu) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float sg = fast_rcp(1.0f + fast_exp2(S[r] * c1));
-        const float sv = S[r] * scale;
+        const float sv = DQB == 3 ? fmaf(S[r], scale, sbj) : S[r] * scale;
+        const float sg = fast_rcp(1.0f + fast_exp2(DQB == 3 ? -sv * kLog2e : S[r] * c1));
         const float p = sv * sg;
         S[r] = p;
         dP[r] = dP[r] * fmaf(sv - p, sg, sg);
@@ -236,9 +241,14 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float gr;
-        S[r] = phi_value_grad<PHI>(S[r] * scale, gr);
+        S[r] = phi_value_grad<PHI>(DQB == 3 ? fmaf(S[r], scale, sbj) : S[r] * scale, gr);
         dP[r] *= gr;
       }
+    }
+    if (DQB == 3) {  // score-bias gradient: the sample's tokens of this step (register r: token 8 (r/4) + 4 g + r%4)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * g + (r & 3) < rows) dsb += dP[r];
     }
     bf16x8 pa[2], sa[2];
 #pragma unroll
@@ -294,7 +304,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
           if (DQB == 1)
             base = *(const GDPA_LDS u32x4*)&dOs[wave * 1024 + slot_off(lxd, 2 * g + hh)];
           if (DQB == 2) base = gload16(dst + 8 * hh);
-          if (DQB != 0) {
+          if (DQB == 1 || DQB == 2) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] += bf2f(half_of(base, e));
           }
@@ -308,6 +318,10 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   // with it) as bf16 32 x 128 tiles per wave, then 16-byte stores of rows j < n.
   // The copies issued for the two steps past the end land before the work-group
   // releases its LDS.
+  if (DQB == 3 && a.d_score_bias != nullptr) {
+    dsb += wave_xor32(dsb);
+    if (g == 0 && jvalid) a.d_score_bias[(crow0 + j) * H + h] = dsb;
+  }
   if (wave >= 4) wait_vmcnt<0>();
   __syncthreads();
   uint16_t* Ew = Kt + wave * 32 * LDE;
@@ -338,12 +352,14 @@ hipError_t launch_bwd_res(const BwdArgs& a, int phi, hipStream_t s) {
   const long items = (long)a.B * a.H;
   if (items == 0) return hipSuccess;
   const dim3 g((unsigned)items), blk(512);
-  const int mode = a.dq_base == nullptr ? 0 : (a.dq_base == a.d_o ? 1 : 2);
+  const int mode = a.score_bias != nullptr || a.d_score_bias != nullptr ? 3
+                   : (a.dq_base == nullptr ? 0 : (a.dq_base == a.d_o ? 1 : 2));
   return dispatch_phi(phi, [&](auto P) {
     constexpr int PH = decltype(P)::value;
     if (mode == 0) hipLaunchKernelGGL((bwd_res_kernel<PH, 0>), g, blk, 0, s, a);
     else if (mode == 1) hipLaunchKernelGGL((bwd_res_kernel<PH, 1>), g, blk, 0, s, a);
-    else hipLaunchKernelGGL((bwd_res_kernel<PH, 2>), g, blk, 0, s, a);
+    else if (mode == 2) hipLaunchKernelGGL((bwd_res_kernel<PH, 2>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((bwd_res_kernel<PH, 3>), g, blk, 0, s, a);
     return hipGetLastError();
   });
 }

@@ -24,7 +24,8 @@ namespace gdpa {
 // Window Attention bullet): K and V are the sample's own token rows, and token i
 // (position in its sample) attends to positions i - window < j <= i only; the
 // context-row loop covers just that band and out-of-band scores are -inf.
-template <int D, int PHI, bool RESID, bool SW = false>
+// BIAS: FFN biases (a.score_bias and / or a.out_bias), never with RESID or SW.
+template <int D, int PHI, bool RESID, bool SW = false, bool BIAS = false>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   constexpr int BM = kFwdTileRows, BN = 64, KS = D / 16, DT = D / 32;
   // Row strides (elements), chosen for the 32-bank LDS: K rows are read 16 bytes
@@ -36,6 +37,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   constexpr int SI = (BN * CH + 255) / 256;   // staging chunks per thread per tensor
   __shared__ __align__(16) uint16_t Ks[BN * LD];
   __shared__ __align__(16) uint16_t Vs[BN * LDV];
+  __shared__ __align__(16) float Sbl[BIAS ? BN : 4];  // score bias of the block's rows
 
   const int H = a.H, B = a.B;
   const int total = a.tile_start[B];
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       vreg[i] = ok ? gload16(Vg + (size_t)(jb + j) * rs + 8 * c) : u32x4{};
     }
   };
-  auto store_block = [&]() {
+  auto store_block = [&](int jb) {
 #pragma unroll
     for (int i = 0; i < SI; ++i) {
       const int idx = i * 256 + tid, j = idx / CH, c = idx % CH;
@@ -90,6 +92,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
         lds_write16(&Vs[j * LDV + 8 * c], vreg[i]);
       }
     }
+    if (BIAS && tid < BN)
+      Sbl[tid] = (a.score_bias != nullptr && jb + tid < n) ? a.score_bias[(crow0 + jb + tid) * H + h] : 0.f;
   };
 
   // Transpose-read addressing: lane 16 G + 4 r + c reads row 4 (G / 2) + r,
@@ -108,9 +112,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   gload_block(jbeg);
   for (int jb = jbeg; jb < jend; jb += BN) {
     __syncthreads();
-    store_block();
+    store_block(jb);
     __syncthreads();
     if (jb + BN < jend) gload_block(jb + BN);
+    // Score bias (BIAS) of rows 32 mt + 8 q + 4 g + {0..3}: register 4 q + i of tile mt.
+    float bj[2][16];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 bv = BIAS ? *(const GDPA_LDS f32x4*)&Sbl[32 * mt + 8 * q + 4 * g] : f32x4{};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bj[mt][4 * q + i] = bv[i];
+      }
 
     f32x16 S[2];
 #pragma unroll
@@ -129,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float s = S[mt][r] * sl2;
+          float s = BIAS ? fmaf(bj[mt][r], kLog2e, S[mt][r] * sl2) : S[mt][r] * sl2;
           if (tail || SW) {
             const int j = jb + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
             if (j >= n || (SW && (j > irow || j <= irow - a.window))) s = -INFINITY;
@@ -159,7 +173,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[mt][r] = phi_value<PHI>(S[mt][r] * a.scale);
+        for (int r = 0; r < 16; ++r)
+          S[mt][r] = phi_value<PHI>(BIAS ? fmaf(S[mt][r], a.scale, bj[mt][r]) : S[mt][r] * a.scale);
     }
 
 #pragma unroll
@@ -203,6 +218,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
           v2 += __uint_as_float(rr[1] << 16);
           v3 += __uint_as_float(rr[1] & 0xffff0000u);
         }
+        if (BIAS && a.out_bias != nullptr) {
+          const f32x4 bv = *(const f32x4*)(a.out_bias + ((size_t)b * H + h) * D + 4 * g + col);
+          v0 += bv[0]; v1 += bv[1]; v2 += bv[2]; v3 += bv[3];
+        }
         bf16x4 ov;
         ov[0] = f2bf(v0); ov[1] = f2bf(v1); ov[2] = f2bf(v2); ov[3] = f2bf(v3);
         *(bf16x4*)(op + col) = ov;
@@ -238,6 +257,7 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < D; ++e) s = fmaf(q[e], kj[e], s);
     s *= a.scale;
+    if (a.score_bias != nullptr) s += a.score_bias[(crow0 + j) * a.H + h];
     if (PHI == 0) {
       const float m_new = fmaxf(m, s);
       const float c = expf(m - m_new), p = expf(s - m_new);
@@ -257,8 +277,9 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const FwdArgs a) {
   float* op = (float*)a.o + (size_t)t * rs + (size_t)h * D;
   const float* rp = RESID ? (const float*)a.residual + (size_t)t * rs + (size_t)h * D : nullptr;
   const float inv = (PHI == 0) ? 1.0f / l : 1.0f;
+  const float* obp = a.out_bias != nullptr ? a.out_bias + ((size_t)b * a.H + h) * D : nullptr;
 #pragma unroll
-  for (int e = 0; e < D; ++e) op[e] = acc[e] * inv + (RESID ? rp[e] : 0.f);
+  for (int e = 0; e < D; ++e) op[e] = acc[e] * inv + (RESID ? rp[e] : 0.f) + (obp != nullptr ? obp[e] : 0.f);
   if (PHI == 0 && a.lse != nullptr) a.lse[(size_t)t * a.H + h] = m + logf(l);
 }
 
@@ -272,9 +293,11 @@ int fwd_bf16_grid(int T, int B, int H) {
 template <int D>
 static hipError_t fwd_bf16_d(const FwdArgs& a, int phi, bool resid, int grid, hipStream_t s) {
   const dim3 g(grid), blk(256);
+  const bool biased = a.score_bias != nullptr || a.out_bias != nullptr;  // never with a residual
   return dispatch_phi(phi, [&](auto P) {
     constexpr int PH = decltype(P)::value;
-    if (resid) hipLaunchKernelGGL((fwd_bf16_kernel<D, PH, true>), g, blk, 0, s, a);
+    if (biased) hipLaunchKernelGGL((fwd_bf16_kernel<D, PH, false, false, true>), g, blk, 0, s, a);
+    else if (resid) hipLaunchKernelGGL((fwd_bf16_kernel<D, PH, true>), g, blk, 0, s, a);
     else hipLaunchKernelGGL((fwd_bf16_kernel<D, PH, false>), g, blk, 0, s, a);
     return hipGetLastError();
   });

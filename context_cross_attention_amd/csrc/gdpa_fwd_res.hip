@@ -35,7 +35,8 @@ __device__ __forceinline__ int vt_row(int i) { return 16 * ((i >> 2) & 1) + 4 * 
 // 16-lane phase of a ds_read_b128 fall in distinct bank groups.
 __device__ __forceinline__ int vt_chunk(int q, int d) { return q ^ (((d >> 4) & 1) << 3); }
 
-// RESID: 0 none, 1 residual is the query tensor, 2 a separate residual tensor.
+// RESID: 0 none, 1 residual is the query tensor, 2 a separate residual tensor,
+// 3 FFN biases (a.score_bias and / or a.out_bias; no residual).
 template <int D, int NMAX, int PHI, int RESID>
 __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const int32_t* __restrict__ order) {
   constexpr int NW = 8, NT = NW * 64, KS = D / 16, DT = D / 32, CH = D / 8;
@@ -43,6 +44,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
   constexpr int LDV = NMAX + 8;   // V^T rows: likewise for 8 consecutive d rows
   __shared__ __align__(16) uint16_t Kc[NMAX * LDK];
   __shared__ __align__(16) uint16_t Vt[D * LDV];
+  __shared__ __align__(16) float Sb[RESID == 3 ? NMAX : 4];  // score bias of the sample's rows
 
   const int H = a.H;
   const int item = blockIdx.x;
@@ -108,6 +110,10 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
       }
     }
   }
+  const bool sbias = RESID == 3 && a.score_bias != nullptr;
+  if (RESID == 3) {
+    for (int j = tid; j < npad; j += NT) Sb[j] = (sbias && j < n) ? a.score_bias[(crow0 + j) * H + h] : 0.f;
+  }
   __syncthreads();
 
   const float scl = a.scale, sl2 = scl * kLog2e, nsl2 = -sl2;
@@ -143,12 +149,21 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
     };
     // phi of one 32-row tile, then O^T += V^T P^T.
     auto mix = [&](int j0, f32x16& S) {
+      // Score bias of rows j0 + 8 q + 4 g + {0..3} (register 4 q + i): the scaled
+      // score becomes S * scale + b, applied in each map's own units below.
+      float bj[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 bv = RESID == 3 ? *(const GDPA_LDS f32x4*)&Sb[j0 + 8 * q + 4 * g] : f32x4{};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bj[4 * q + i] = bv[i];
+      }
       if (PHI == 0) {
         const bool tail = j0 + 32 > n;
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float s = S[r] * sl2;
+          float s = RESID == 3 ? fmaf(bj[r], kLog2e, S[r] * sl2) : S[r] * sl2;
           if (tail && j0 + 8 * (r >> 2) + 4 * g + (r & 3) >= n) s = -INFINITY;
           S[r] = s;
           mx = fmaxf(mx, s);
@@ -174,12 +189,12 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         // The constant -ln(2) is applied once to O after the last tile.
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float t = S[r] * nsl2;
+          const float t = RESID == 3 ? fmaf(-bj[r], kLog2e, S[r] * nsl2) : S[r] * nsl2;
           S[r] = t * fast_rcp(1.0f + fast_exp2(t));
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[r] = phi_value<PHI>(S[r] * scl);
+        for (int r = 0; r < 16; ++r) S[r] = phi_value<PHI>(RESID == 3 ? fmaf(S[r], scl, bj[r]) : S[r] * scl);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -234,6 +249,14 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
             const u32x4 rr = gload16((const uint16_t*)a.residual + obase + 32 * dt + 8 * hh);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] += bf2f((uint16_t)(rr[e >> 1] >> (16 * (e & 1))));
+          } else if (RESID == 3 && a.out_bias != nullptr) {
+            const float* bp = a.out_bias + ((size_t)b * H + h) * D + 32 * dt + 16 * g + 8 * hh;
+            const f32x4 b0 = *(const f32x4*)bp, b1 = *(const f32x4*)(bp + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] += b0[e];
+              v[4 + e] += b1[e];
+            }
           }
           *(bf16x8*)(op + 32 * dt + 8 * hh) = pack8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
         }
@@ -256,12 +279,14 @@ static void fwd_res_launch(const FwdArgs& a, const int32_t* order, int resid, hi
   const dim3 g((unsigned)((long)a.B * a.H)), blk(512);
   if (resid == 0) hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 0>), g, blk, 0, s, a, order);
   else if (resid == 1) hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 1>), g, blk, 0, s, a, order);
-  else hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 2>), g, blk, 0, s, a, order);
+  else if (resid == 2) hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 2>), g, blk, 0, s, a, order);
+  else hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 3>), g, blk, 0, s, a, order);
 }
 
 template <int D, int NMAX>
 static hipError_t fwd_res_d(const FwdArgs& a, const int32_t* order, int phi, bool resid, hipStream_t s) {
-  const int mode = !resid ? 0 : (a.residual == a.q ? 1 : 2);
+  const bool biased = a.score_bias != nullptr || a.out_bias != nullptr;  // never with a residual
+  const int mode = biased ? 3 : (!resid ? 0 : (a.residual == a.q ? 1 : 2));
   return dispatch_phi(phi, [&](auto P) {
     fwd_res_launch<D, NMAX, decltype(P)::value>(a, order, mode, s);
     return hipGetLastError();

@@ -47,6 +47,10 @@ struct FwdArgs {
   float scale;
   int window;                 // sliding-window self-attention: token i sees i - window < j <= i
   const int32_t* kv_offsets;  // [B+1] jagged context rows (n = the largest count), or nullptr
+  // FFN biases, fp32, or nullptr: score_bias[(row0 + j) * H + h] is added to the
+  // scaled score of context row j before phi; out_bias[(b * H + h) * d + c] to O.
+  const float* score_bias;
+  const float* out_bias;
 };
 
 struct BwdArgs {
@@ -71,6 +75,8 @@ struct BwdArgs {
   int window;
   const int32_t* tile_start;  // [B+1] query-tile prefix sums (dQ kernel)
   const int32_t* kv_offsets;  // [B+1] jagged context rows (n = the largest count), or nullptr
+  const float* score_bias;    // as in FwdArgs, or nullptr
+  float* d_score_bias;        // gradient of score_bias (written by the dK / dV kernels), or nullptr
 };
 
 // Scheduling and small passes (gdpa_sched.hip).
@@ -79,11 +85,16 @@ struct BwdArgs {
 hipError_t launch_tile_scan(const int32_t* offsets, int B, int tile_rows, int32_t* tile_start,
                             hipStream_t s, const int32_t* order = nullptr);
 hipError_t launch_longest_first(const int32_t* offsets, int B, int32_t* order, hipStream_t s);
+// d_out_bias[(b * H + h) * d + c] = sum over the tokens t of sample b of dO[t, h, c].
+hipError_t launch_out_bias_grad(const int32_t* offsets, const void* d_o, int B, int H, int d, bool bf16,
+                                float* d_out_bias, hipStream_t s);
 // out = x0 + x1 (+ x2) (+ x3), bf16, n % 8 == 0; null x2 / x3 are skipped.
 hipError_t launch_add_bf16(long n, void* out, const void* x0, const void* x1, const void* x2,
                            const void* x3, hipStream_t s);
+// rowsum(dO * O) per (token, head) row; with out_bias, rowsum(dO * (O - out_bias)).
 hipError_t launch_softmax_dvec(const void* o, const void* d_o, int rows, int d, bool bf16,
-                               float* dvec, hipStream_t s);
+                               float* dvec, hipStream_t s, const int32_t* offsets = nullptr, int B = 0,
+                               int H = 1, const float* out_bias = nullptr);
 
 // Forward (gdpa_fwd.hip).
 int fwd_bf16_grid(int T, int B, int H);

@@ -92,17 +92,35 @@ __global__ void iota_kernel(int32_t* order, int B) {
 }
 
 // dvec[row] = sum_e O[row, e] * dO[row, e] in fp32 (softmax backward term).
+// With an output bias ob ([B, H, D]), O holds P V + ob: the term is taken for P V,
+// i.e. sum_e (O - ob)[row, e] dO[row, e], row = token * H + head.
 // One row of d elements per group of d/8 lanes.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void softmax_dvec_kernel(const void* __restrict__ o,
                                                            const void* __restrict__ d_o, int rows,
-                                                           float* __restrict__ dvec) {
+                                                           float* __restrict__ dvec, const int32_t* off,
+                                                           int B, int H, const float* __restrict__ ob) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements per lane
   const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
   const int row = gtid / LPR, part = gtid % LPR;
   float acc = 0.f;
   if (row < rows) {
     const size_t base = (size_t)row * D + part * 8;
+    if (ob != nullptr) {
+      const int t = row / H, h = row - t * H;
+      const float* bp = ob + ((size_t)find_sample(off, B, t) * H + h) * D + part * 8;
+      if (BF16) {
+        const u32x4 c = *(const u32x4*)((const uint16_t*)d_o + base);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc -= bp[2 * i] * __uint_as_float(c[i] << 16);
+          acc -= bp[2 * i + 1] * __uint_as_float(c[i] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc -= bp[i] * ((const float*)d_o)[base + i];
+      }
+    }
     if (BF16) {
       const u32x4 a = *(const u32x4*)((const uint16_t*)o + base);
       const u32x4 c = *(const u32x4*)((const uint16_t*)d_o + base);
@@ -146,6 +164,57 @@ __global__ __launch_bounds__(256) void add_bf16_kernel(uint16_t* out, const uint
   *(bf16x8*)(out + 8 * i) = pack8(acc[0], acc[1], acc[2], acc[3], acc[4], acc[5], acc[6], acc[7]);
 }
 
+// Column sums of dO over each sample's tokens: one work-group per (sample, head);
+// thread t sums 8 consecutive columns of the rows t / (d / 8), + 256 / (d / 8), ...
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void out_bias_grad_kernel(const int32_t* __restrict__ off, const void* __restrict__ d_o,
+                                                            int H, float* __restrict__ dob) {
+  constexpr int CPR = D / 8, RPS = 256 / CPR;  // threads per row, rows per sweep
+  __shared__ float part[RPS][D];
+  const int b = blockIdx.x / H, h = blockIdx.x - b * H;
+  const int tid = threadIdx.x, c = tid % CPR, r0 = tid / CPR;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int t = off[b] + r0; t < off[b + 1]; t += RPS) {
+    const size_t base = ((size_t)t * H + h) * D + 8 * c;
+    if (BF16) {
+      const u32x4 v = *(const u32x4*)((const uint16_t*)d_o + base);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(v[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += ((const float*)d_o)[base + e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[r0][8 * c + e] = acc[e];
+  __syncthreads();
+  for (int col = tid; col < D; col += 256) {
+    float sum = 0.f;
+    for (int r = 0; r < RPS; ++r) sum += part[r][col];
+    dob[((size_t)b * H + h) * D + col] = sum;
+  }
+}
+
+hipError_t launch_out_bias_grad(const int32_t* offsets, const void* d_o, int B, int H, int d, bool bf16,
+                                float* d_out_bias, hipStream_t s) {
+  const dim3 grid((unsigned)((long)B * H)), block(256);
+  if ((long)B * H == 0) return hipSuccess;
+#define GDPA_OBG(D)                                                                                       \
+  if (d == D) {                                                                                           \
+    if (bf16) hipLaunchKernelGGL((out_bias_grad_kernel<D, true>), grid, block, 0, s, offsets, d_o, H, d_out_bias); \
+    else hipLaunchKernelGGL((out_bias_grad_kernel<D, false>), grid, block, 0, s, offsets, d_o, H, d_out_bias);     \
+    return hipGetLastError();                                                                             \
+  }
+  GDPA_OBG(32) GDPA_OBG(64) GDPA_OBG(128)
+#undef GDPA_OBG
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_add_bf16(long n, void* out, const void* x0, const void* x1, const void* x2,
                            const void* x3, hipStream_t s) {
   const long n8 = n / 8;
@@ -172,16 +241,17 @@ hipError_t launch_longest_first(const int32_t* offsets, int B, int32_t* order, h
 }
 
 hipError_t launch_softmax_dvec(const void* o, const void* d_o, int rows, int d, bool bf16,
-                               float* dvec, hipStream_t s) {
+                               float* dvec, hipStream_t s, const int32_t* offsets, int B, int H,
+                               const float* out_bias) {
   const long threads = (long)rows * (d / 8);
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
   if (rows == 0) return hipSuccess;
 #define GDPA_DVEC(D)                                                                            \
   if (d == D) {                                                                                 \
     if (bf16) hipLaunchKernelGGL((softmax_dvec_kernel<D, true>), grid, block, 0, s, o, d_o,     \
-                                 rows, dvec);                                                   \
+                                 rows, dvec, offsets, B, H, out_bias);                          \
     else hipLaunchKernelGGL((softmax_dvec_kernel<D, false>), grid, block, 0, s, o, d_o, rows,   \
-                            dvec);                                                              \
+                            dvec, offsets, B, H, out_bias);                                     \
     return hipGetLastError();                                                                   \
   }
   GDPA_DVEC(32) GDPA_DVEC(64) GDPA_DVEC(128)

@@ -343,3 +343,13 @@ def make_layer_stack_inputs(length_spec: tuple, batch: int, H: int, d: int, n: i
     dx = draw_normal(rng, (T, H, d), "bf16")
     dz = [draw_normal(rng, (batch, m, H, d), "bf16") for _ in range(layers)]
     return LayerStackInputs(lengths, torch.from_numpy(off.astype(np.int32)), x0, ctx, w_k, w_v, seeds, dx, dz)
+
+
+def draw_ffn_biases(seed: int, bias_rows_shape, B: int, H: int, d: int, out_scale: Optional[float] = None):
+    """FFN biases as float32: a score bias shaped `bias_rows_shape` ([B,n,H] dense or
+    [rows,H] jagged), N(0,1) like the scores, and an output bias [B,H,d], N(0,1) *
+    out_scale (default 1/sqrt(d), the scale of the V rows the output mixes)."""
+    rng = np.random.default_rng(seed)
+    sb = draw_normal(rng, tuple(bias_rows_shape), "f32")
+    ob = draw_normal(rng, (B, H, d), "f32") * (1.0 / math.sqrt(d) if out_scale is None else out_scale)
+    return sb, ob

@@ -151,6 +151,36 @@ gdpa_status gdpa_bwd_jagged_kv(const gdpa_problem* p, const int32_t* offsets, co
 gdpa_status gdpa_add_bf16(int64_t count, void* out, const void* x0, const void* x1, const void* x2,
                           const void* x3, void* stream);
 
+/* FFN biases (a variant of the same op: a two-layer FFN carries a bias per hidden
+ * unit and per output; the pages give none, so the base calls have none):
+ *
+ *     O[t,h,:] = phi(scale * <Q[t,h,:], K[j,h,:]> + score_bias[j,h])_j V[.,h,:] + out_bias[b,h,:]
+ *
+ * score_bias is float32 [B][n_kv][H] for the dense context or [rows][H] with
+ * kv_offsets (one value per context row and head, like K without d); out_bias is
+ * float32 [B][H][d] (one row per sample and head).  Either may be NULL (no bias).
+ * kv_offsets may be NULL (dense context).  The backward also returns
+ * d_score_bias (the sum over the sample's tokens of the score gradient, layout
+ * of score_bias) and d_out_bias (the sum of dO over the sample's tokens,
+ * [B][H][d]), each when non-NULL; for softmax it needs the forward's lse and o
+ * and the same biases.  p->flags must be 0 (GDPA_ERR_UNSUPPORTED otherwise).
+ * Workspace: gdpa_biased_workspace_bytes(p, backward, out_bias != NULL).  With
+ * softmax, bf16 and an output bias the backward does not read o: the softmax row
+ * term sum_e (P V)[t,h,e] dO[t,h,e] taken from the bf16 O = P V + out_bias would
+ * carry O's rounding, relative to |P V + out_bias|, so the backward recomputes
+ * P V once (one extra forward pass) into its workspace, which then also holds
+ * T*H*(2d + 4) bytes for it.  Otherwise as gdpa_fwd / gdpa_bwd. */
+size_t gdpa_biased_workspace_bytes(const gdpa_problem* p, int backward, int out_bias);
+gdpa_status gdpa_fwd_biased(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
+                            const void* q, const void* k, const void* v, const float* score_bias,
+                            const float* out_bias, void* o, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+gdpa_status gdpa_bwd_biased(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
+                            const void* q, const void* k, const void* v, const float* score_bias,
+                            const float* out_bias, const void* o, const float* lse, const void* d_o,
+                            void* dq, void* dk, void* dv, float* d_score_bias, float* d_out_bias,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Host-side check of a HOST copy of kv_offsets: kv_offsets[0] = 0 and every
  * sample owns 1 .. n_kv rows; GDPA_OK or GDPA_ERR_INVALID_ARGUMENT. */
 gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv);
