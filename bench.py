@@ -54,11 +54,14 @@ def parse():
     ap.add_argument("--phi", default=None, choices=[None, "softmax", "silu", "relu", "gelu", "identity"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="gdpa", choices=["gdpa", "swa", "pma", "jagged_kv", "layers"],
+    ap.add_argument("--op", default="gdpa", choices=["gdpa", "swa", "pma", "jagged_kv", "layers", "biased",
+                                                   "grouped"],
                     help="swa: sliding-window self-attention on the stacked workload's batch; "
                          "pma: seed pooling attention over that batch; jagged_kv: GDPA fwd+bwd with "
                          "per-sample context row counts (the fwd+bwd workload's batch); layers: the "
-                         "Kunlun layer stack (GDPA + pooling + self-attention) on the stacked workload")
+                         "Kunlun layer stack (GDPA + pooling + self-attention) on the stacked workload; "
+                         "biased: GDPA fwd+bwd with FFN biases on the fwd+bwd workload; grouped: one "
+                         "grouped call over the event types' GDPA problems")
     ap.add_argument("--schedule", default="compskip", choices=["compskip", "full"],
                     help="layer schedule of --op layers (the other one is timed alongside)")
     ap.add_argument("--window", type=int, default=512, help="window of --op swa")
@@ -438,6 +441,230 @@ def run_jagged_kv(args):
 
 
 # ---------------------------------------------------------------------------
+# GDPA with FFN biases (--op biased)
+# ---------------------------------------------------------------------------
+
+
+def run_biased(args):
+    import torch
+
+    import context_cross_attention_amd as cca
+    import gdpa_inputs as gi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cca.load()
+    cfg = gi.CONFIGS[4]
+    phi = args.phi or "silu"
+    H, d, n, B = cfg.heads, cfg.head_dim, cfg.n_kv, cfg.batch
+    inp = gi.make_gdpa_inputs(cfg, seed=args.seed)
+    T = inp.total_tokens
+    sb_h, ob_h = gi.draw_ffn_biases(args.seed + 1, (B, n, H), B, H, d)
+    q, off, k, v, do = (t.cuda() for t in (inp.q, inp.offsets, inp.k, inp.v, inp.do))
+    sb, ob = sb_h.cuda(), ob_h.cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsb, dob = torch.empty_like(sb), torch.empty_like(ob)
+    ws = torch.empty(max(cca.biased_workspace_bytes(q, off, k, phi, True, True), 1 << 20), dtype=torch.uint8,
+                     device="cuda")
+    marks = Marks(torch)
+
+    def step_biased():
+        marks("gdpa_fwd_biased", True)
+        cca.fwd_biased(q, off, k, v, sb, ob, phi=phi, out=o, lse=lse, workspace=ws)
+        marks("gdpa_fwd_biased", False)
+        marks("gdpa_bwd_biased", True)
+        cca.bwd_biased(q, off, k, v, sb, ob, o, lse, do, phi=phi, workspace=ws, dq=dq, dk=dk, dv=dv,
+                       d_score_bias=dsb, d_out_bias=dob)
+        marks("gdpa_bwd_biased", False)
+
+    def step_plain():
+        cca.fwd(q, off, k, v, phi=phi, out=o, lse=lse, workspace=ws)
+        cca.bwd(q, off, k, v, o, lse, do, phi=phi, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    def timed(step, use_marks):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        marks.enabled = use_marks
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        marks.enabled = False
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms_plain = timed(step_plain, False)
+    ms_per_step = timed(step_biased, True)
+    pairs = float(inp.lengths.sum()) * n
+    tok, kvb, sbb = T * H * d * 2, B * n * H * d * 2, B * n * H * 4
+    f_fwd, f_bwd = 4.0 * d * H * pairs, 8.0 * d * H * pairs
+    extra_fwd = 4.0 * d * H * pairs if phi == "softmax" else 0.0  # P V recomputed in the backward
+    b_fwd = 2 * tok + 2 * kvb + sbb + (T * H * 4 if phi == "softmax" else 0)
+    b_bwd = 3 * tok + 4 * kvb + 2 * sbb + tok + ((2 * T * H * 4) if phi == "softmax" else 0)
+    units = {"gdpa_fwd_biased": (f_fwd, b_fwd), "gdpa_bwd_biased": (f_bwd + extra_fwd, b_bwd)}
+    totals, counts = marks.totals_ms(), marks.counts()
+    dom = max(totals, key=lambda x: totals[x])
+    t_dom = totals[dom] / counts[dom] * 1e-3
+    f_dom, b_dom = units[dom]
+    roof = {"bound": "mfma", "achieved": round(f_dom / t_dom / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s"}
+    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, kernel=dom,
+                launch_ms=round(totals[dom] / counts[dom], 4),
+                algorithmic_per_launch={"flops": f_dom, "bytes": b_dom})
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "GDPA fwd+bwd TFLOP/s with FFN biases, jagged batch, 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws as in gdpa_inputs.make_gdpa_inputs and draw_ffn_biases)",
+        "config": {"workload": f"GDPA fwd+bwd with a score bias per context row and an output bias, phi={phi}: "
+                               f"B={B}, L~U[256,2048], T={T}, H={H}, d={d}, n={n}",
+                   "tokens": T, "heads": H, "head_dim": d, "n_kv": n, "phi": phi, "seed": args.seed},
+        "unbiased_ms_per_step": round(ms_plain, 4),
+        "bias_overhead": round(ms_per_step / ms_plain - 1.0, 4),
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "breakdown_ms_per_step": {x: round(totals[x] / args.steps, 4) for x in totals},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import gdpa_oracle as orc
+        chosen, cost = [], 0.0
+        for b in range(B):
+            chosen.append(b)
+            cost += 12.0 * float(inp.lengths[b]) * n * H * d
+            if cost >= 1.5e11:
+                break
+        t1 = time.perf_counter()
+        orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=chosen, score_bias=sb_h, out_bias=ob_h)
+        orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi, samples=chosen, score_bias=sb_h,
+                          bias_grads=True)
+        dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": cost / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"fwd+bwd on samples 0..{chosen[-1]} ({len(chosen)} of {B}); "
+                                         f"{cost / 1e9:.1f} GFLOP in {dt:.1f} s (numpy float64)",
+                               "seconds": round(dt, 2)}
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------------------
+# grouped launch over the event types (--op grouped)
+# ---------------------------------------------------------------------------
+
+
+def run_grouped(args):
+    import torch
+
+    import context_cross_attention_amd as cca
+    import gdpa_inputs as gi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cca.load()
+    phi = args.phi or "silu"
+    events = gi.make_event_inputs(seed=args.seed)
+    specs, dos = [], []
+    for inp in events.values():
+        specs.append(cca.GroupSpec(inp.q.cuda(), inp.offsets.cuda(), inp.k.cuda(), inp.v.cuda(), phi=phi))
+        dos.append(inp.do.cuda())
+    outs = [(torch.empty_like(sp.q), torch.empty((sp.q.shape[0], sp.q.shape[1]), dtype=torch.float32,
+                                                 device="cuda")) for sp in specs]
+    grads = [(torch.empty_like(sp.q), torch.empty_like(sp.k), torch.empty_like(sp.v)) for sp in specs]
+    ws_f = torch.empty(cca.grouped_workspace_bytes(specs, False), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(cca.grouped_workspace_bytes(specs, True), dtype=torch.uint8, device="cuda")
+    ws_1 = torch.empty(max(max(cca.workspace_bytes(cca.make_problem(sp.q, sp.offsets, sp.k, phi, None), bw)
+                               for sp in specs for bw in (False, True)), 1), dtype=torch.uint8, device="cuda")
+    marks = Marks(torch)
+
+    def step_grouped():
+        marks("gdpa_fwd_grouped", True)
+        cca.fwd_grouped(specs, outs, ws_f)
+        marks("gdpa_fwd_grouped", False)
+        marks("gdpa_bwd_grouped", True)
+        cca.bwd_grouped(specs, outs, dos, grads, ws_b)
+        marks("gdpa_bwd_grouped", False)
+
+    def step_serial():
+        for i, sp in enumerate(specs):
+            o, lse = outs[i]
+            cca.fwd(sp.q, sp.offsets, sp.k, sp.v, phi=phi, out=o, lse=lse, workspace=ws_1)
+            cca.bwd(sp.q, sp.offsets, sp.k, sp.v, o, lse, dos[i], phi=phi, dq=grads[i][0], dk=grads[i][1],
+                    dv=grads[i][2], workspace=ws_1)
+
+    def timed(step, use_marks):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        marks.enabled = use_marks
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        marks.enabled = False
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms_serial = timed(step_serial, False)
+    ms_per_step = timed(step_grouped, True)
+    f_fwd = f_bwd = 0.0
+    per_event = {}
+    for name, inp in events.items():
+        cfg = inp.cfg
+        pairs = float(inp.lengths.sum()) * cfg.n_kv
+        f = 4.0 * cfg.heads * cfg.head_dim * pairs
+        f_fwd += f
+        f_bwd += 2 * f
+        per_event[name] = {"tokens": int(inp.lengths.sum()), "heads": cfg.heads, "head_dim": cfg.head_dim,
+                           "n_kv": cfg.n_kv, "gflop_fwd_bwd": round(3 * f / 1e9, 1)}
+    totals, counts = marks.totals_ms(), marks.counts()
+    units = {"gdpa_fwd_grouped": f_fwd, "gdpa_bwd_grouped": f_bwd}
+    dom = max(totals, key=lambda x: totals[x])
+    t_dom = totals[dom] / counts[dom] * 1e-3
+    roof = {"bound": "mfma", "achieved": round(units[dom] / t_dom / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s"}
+    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=None, kernel=dom,
+                launch_ms=round(totals[dom] / counts[dom], 4), algorithmic_per_launch={"flops": units[dom]},
+                note="one call of several kernels on up to four streams; the time is the call's span")
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "GDPA fwd+bwd TFLOP/s over several event types in one grouped call, 1 MI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws as in gdpa_inputs.make_event_inputs)",
+        "config": {"workload": "GDPA fwd+bwd, phi=" + phi + ", one problem per event type: "
+                               + "; ".join(cfg.name for cfg in gi.EVENT_TYPES.values()),
+                   "events": per_event, "phi": phi, "seed": args.seed},
+        "serial_ms_per_step": round(ms_serial, 4),
+        "grouped_speedup": round(ms_serial / ms_per_step, 4),
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "breakdown_ms_per_step": {x: round(totals[x] / args.steps, 4) for x in totals},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import gdpa_oracle as orc
+        inp = events["conversion"]
+        cfg = inp.cfg
+        chosen, cost = [], 0.0
+        for b in range(cfg.batch):
+            chosen.append(b)
+            cost += 12.0 * float(inp.lengths[b]) * cfg.n_kv * cfg.heads * cfg.head_dim
+            if cost >= 1.5e11:
+                break
+        t1 = time.perf_counter()
+        orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=chosen)
+        orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi, samples=chosen)
+        dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": cost / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"fwd+bwd of the conversion events on samples 0..{chosen[-1]} "
+                                         f"({len(chosen)} of {cfg.batch}); {cost / 1e9:.1f} GFLOP in {dt:.1f} s "
+                                         f"(numpy float64)",
+                               "seconds": round(dt, 2)}
+    print(json.dumps(out))
+
+
+# ---------------------------------------------------------------------------
 # the Kunlun layer stack with the CompSkip schedule (--op layers)
 # ---------------------------------------------------------------------------
 
@@ -701,6 +928,12 @@ def main():
         return
     if args.op == "layers":
         run_layers(args)
+        return
+    if args.op == "biased":
+        run_biased(args)
+        return
+    if args.op == "grouped":
+        run_grouped(args)
         return
 
     import numpy as np

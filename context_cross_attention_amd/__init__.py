@@ -13,7 +13,8 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import Optional, Tuple
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -37,6 +38,15 @@ class GdpaProblem(ctypes.Structure):
                 ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("phi", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class GdpaGroup(ctypes.Structure):
+    """Mirror of gdpa_group in include/gdpa.h."""
+    _fields_ = [("problem", GdpaProblem), ("offsets", ctypes.c_void_p), ("kv_offsets", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("residual", ctypes.c_void_p), ("o", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("d_o", ctypes.c_void_p), ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p),
+                ("dv", ctypes.c_void_p)]
 
 
 class SwaProblem(ctypes.Structure):
@@ -71,6 +81,7 @@ EXPORTS = ("gdpa_workspace_bytes", "gdpa_fwd", "gdpa_bwd", "gdpa_weightgen_fwd",
            "gdpa_pma_workspace_bytes", "gdpa_pma_fwd", "gdpa_pma_bwd",
            "gdpa_fwd_jagged_kv", "gdpa_bwd_jagged_kv", "gdpa_check_kv_offsets", "gdpa_add_bf16",
            "gdpa_fwd_biased", "gdpa_bwd_biased", "gdpa_biased_workspace_bytes",
+           "gdpa_grouped_workspace_bytes", "gdpa_fwd_grouped", "gdpa_bwd_grouped",
            "gdpa_check_offsets", "gdpa_status_str", "gdpa_last_hip_error")
 
 
@@ -112,6 +123,12 @@ def load(path: str = LIB_PATH):
     lib.gdpa_fwd_jagged_kv.restype = ctypes.c_int
     lib.gdpa_bwd_jagged_kv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_bwd_jagged_kv.restype = ctypes.c_int
+    GP = ctypes.POINTER(GdpaGroup)
+    lib.gdpa_grouped_workspace_bytes.argtypes = [ctypes.c_int32, GP, ctypes.c_int]
+    lib.gdpa_grouped_workspace_bytes.restype = sz
+    for name in ("gdpa_fwd_grouped", "gdpa_bwd_grouped"):
+        getattr(lib, name).argtypes = [ctypes.c_int32, GP, vp, sz, vp]
+        getattr(lib, name).restype = ctypes.c_int
     lib.gdpa_biased_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
     lib.gdpa_biased_workspace_bytes.restype = sz
     lib.gdpa_fwd_biased.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -377,6 +394,15 @@ def _biased_shapes(q, offsets, k, kv_offsets, n_kv):
     return B, int(n_kv), (k.shape[0], H, d), (k.shape[0], H)
 
 
+def biased_workspace_bytes(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, phi: str, backward: bool,
+                           out_bias: bool, kv_offsets: Optional[torch.Tensor] = None,
+                           n_kv: Optional[int] = None) -> int:
+    """Workspace bytes of fwd_biased / bwd_biased (out_bias: an output bias is given)."""
+    _, n, _, _ = _biased_shapes(q, offsets, k, kv_offsets, n_kv)
+    prob = _jagged_problem(q, offsets, k, n, phi, None, 0)
+    return int(load().gdpa_biased_workspace_bytes(ctypes.byref(prob), int(backward), int(out_bias)))
+
+
 def fwd_biased(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                score_bias: Optional[torch.Tensor], out_bias: Optional[torch.Tensor], phi: str = "softmax",
                scale: Optional[float] = None, kv_offsets: Optional[torch.Tensor] = None,
@@ -413,7 +439,9 @@ def bwd_biased(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch
                score_bias: Optional[torch.Tensor], out_bias: Optional[torch.Tensor], o: Optional[torch.Tensor],
                lse: Optional[torch.Tensor], do: torch.Tensor, phi: str = "softmax", scale: Optional[float] = None,
                kv_offsets: Optional[torch.Tensor] = None, n_kv: Optional[int] = None,
-               workspace: Optional[torch.Tensor] = None):
+               workspace: Optional[torch.Tensor] = None, dq: Optional[torch.Tensor] = None,
+               dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+               d_score_bias: Optional[torch.Tensor] = None, d_out_bias: Optional[torch.Tensor] = None):
     """Backward of fwd_biased: returns (dq, dk, dv, d_score_bias, d_out_bias)."""
     lib = load()
     T, H, d = q.shape
@@ -428,9 +456,15 @@ def bwd_biased(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch
         _require(lse, "lse", (T, H), torch.float32, dev)
     else:
         o, lse = None, None
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dsb = torch.empty(sbshape, dtype=torch.float32, device=dev)
-    dob = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, shape in (("dq", dq, (T, H, d)), ("dk", dk, kshape), ("dv", dv, kshape)):
+        _require(t, name, shape, q.dtype, dev)
+    dsb = torch.empty(sbshape, dtype=torch.float32, device=dev) if d_score_bias is None else d_score_bias
+    dob = torch.empty((B, H, d), dtype=torch.float32, device=dev) if d_out_bias is None else d_out_bias
+    _require(dsb, "d_score_bias", sbshape, torch.float32, dev)
+    _require(dob, "d_out_bias", (B, H, d), torch.float32, dev)
     prob = _jagged_problem(q, offsets, k, n, phi, scale, 0)
     need = lib.gdpa_biased_workspace_bytes(ctypes.byref(prob), 1, int(out_bias is not None))
     ws = _sized_workspace(need, dev, workspace)
@@ -438,6 +472,116 @@ def bwd_biased(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch
                                _ptr(score_bias), _ptr(out_bias), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
                                _ptr(dv), _ptr(dsb), _ptr(dob), _ptr(ws), ws.numel(), _stream()), "gdpa_bwd_biased")
     return dq, dk, dv, dsb, dob
+
+
+@dataclass
+class GroupSpec:
+    """One problem of a grouped call: q [T,H,d], offsets int32 [B+1], k, v [B,n,H,d]
+    (or [rows,H,d] with kv_offsets and n_kv), its own score map and scale."""
+    q: torch.Tensor
+    offsets: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    phi: str = "softmax"
+    scale: Optional[float] = None
+    kv_offsets: Optional[torch.Tensor] = None
+    n_kv: Optional[int] = None
+
+    def problem(self) -> GdpaProblem:
+        T, H, d = self.q.shape
+        dev = self.q.device
+        B = self.offsets.shape[0] - 1
+        _require(self.offsets, "offsets", (B + 1,), torch.int32, dev)
+        if self.kv_offsets is None:
+            n = self.k.shape[1]
+            kshape = (B, n, H, d)
+        else:
+            if self.n_kv is None:
+                raise ValueError("a jagged context needs n_kv")
+            _require(self.kv_offsets, "kv_offsets", (B + 1,), torch.int32, dev)
+            n, kshape = int(self.n_kv), (self.k.shape[0], H, d)
+        _require(self.k, "k", kshape, self.q.dtype, dev)
+        _require(self.v, "v", kshape, self.q.dtype, dev)
+        return _jagged_problem(self.q, self.offsets, self.k, n, self.phi, self.scale, 0)
+
+
+def _groups(specs: Sequence[GroupSpec]):
+    arr = (GdpaGroup * len(specs))()
+    for i, sp in enumerate(specs):
+        g = arr[i]
+        g.problem = sp.problem()
+        g.offsets, g.kv_offsets = sp.offsets.data_ptr(), _addr(sp.kv_offsets)
+        g.q, g.k, g.v = sp.q.data_ptr(), sp.k.data_ptr(), sp.v.data_ptr()
+    return arr
+
+
+def _addr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def grouped_workspace_bytes(specs: Sequence[GroupSpec], backward: bool) -> int:
+    arr = _groups(specs)
+    return int(load().gdpa_grouped_workspace_bytes(len(specs), arr, int(backward)))
+
+
+def fwd_grouped(specs: Sequence[GroupSpec], outs: Optional[Sequence[Tuple[torch.Tensor, Optional[torch.Tensor]]]] = None,
+                workspace: Optional[torch.Tensor] = None):
+    """Forward of several independent GDPA problems in one call (they run
+    concurrently).  Returns [(o, lse or None)] per group."""
+    lib = load()
+    arr = _groups(specs)
+    res = []
+    for i, sp in enumerate(specs):
+        T, H, d = sp.q.shape
+        o, lse = (None, None) if outs is None else outs[i]
+        o = torch.empty_like(sp.q) if o is None else o
+        _require(o, "o", (T, H, d), sp.q.dtype, sp.q.device)
+        if sp.phi == "softmax":
+            lse = torch.empty((T, H), dtype=torch.float32, device=sp.q.device) if lse is None else lse
+            _require(lse, "lse", (T, H), torch.float32, sp.q.device)
+        else:
+            lse = None
+        arr[i].o, arr[i].lse = o.data_ptr(), _addr(lse)
+        res.append((o, lse))
+    need = lib.gdpa_grouped_workspace_bytes(len(specs), arr, 0)
+    ws = _sized_workspace(need, specs[0].q.device, workspace)
+    _check(lib.gdpa_fwd_grouped(len(specs), arr, _ptr(ws), ws.numel(), _stream()), "gdpa_fwd_grouped")
+    return res
+
+
+def bwd_grouped(specs: Sequence[GroupSpec], fwd_outs: Sequence[Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]],
+                dos: Sequence[torch.Tensor], grads: Optional[Sequence[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]]] = None,
+                workspace: Optional[torch.Tensor] = None):
+    """Backward of fwd_grouped: fwd_outs[i] = (o, lse) (softmax groups), dos[i] = dO.
+    Returns [(dq, dk, dv)] per group."""
+    lib = load()
+    arr = _groups(specs)
+    res = []
+    for i, sp in enumerate(specs):
+        T, H, d = sp.q.shape
+        dev = sp.q.device
+        _require(dos[i], "do", (T, H, d), sp.q.dtype, dev)
+        o, lse = fwd_outs[i]
+        if sp.phi == "softmax":
+            _require(o, "o", (T, H, d), sp.q.dtype, dev)
+            _require(lse, "lse", (T, H), torch.float32, dev)
+        else:
+            o, lse = None, None
+        dq, dk, dv = (None, None, None) if grads is None else grads[i]
+        dq = torch.empty_like(sp.q) if dq is None else dq
+        dk = torch.empty_like(sp.k) if dk is None else dk
+        dv = torch.empty_like(sp.v) if dv is None else dv
+        _require(dq, "dq", (T, H, d), sp.q.dtype, dev)
+        _require(dk, "dk", tuple(sp.k.shape), sp.q.dtype, dev)
+        _require(dv, "dv", tuple(sp.v.shape), sp.q.dtype, dev)
+        g = arr[i]
+        g.o, g.lse, g.d_o = _addr(o), _addr(lse), dos[i].data_ptr()
+        g.dq, g.dk, g.dv = dq.data_ptr(), dk.data_ptr(), dv.data_ptr()
+        res.append((dq, dk, dv))
+    need = lib.gdpa_grouped_workspace_bytes(len(specs), arr, 1)
+    ws = _sized_workspace(need, specs[0].q.device, workspace)
+    _check(lib.gdpa_bwd_grouped(len(specs), arr, _ptr(ws), ws.numel(), _stream()), "gdpa_bwd_grouped")
+    return res
 
 
 def check_kv_offsets(kv_offsets, n_kv: int) -> bool:

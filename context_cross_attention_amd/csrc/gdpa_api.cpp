@@ -3,8 +3,12 @@
 // arguments are reported without touching the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <map>
+#include <mutex>
+#include <vector>
 
 #include "gdpa.h"
 #include "gdpa_launch.h"
@@ -128,7 +132,8 @@ namespace {
 gdpa_status fwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_t* kv_offsets,
                      const void* q, const void* k, const void* v, const void* residual, void* o,
                      float* lse, void* workspace, size_t workspace_bytes, void* stream,
-                     const float* score_bias = nullptr, const float* out_bias = nullptr) {
+                     const float* score_bias = nullptr, const float* out_bias = nullptr,
+                     bool launch = true) {
   const gdpa_status st = check_problem(p);
   if (st != GDPA_OK) return st;
   if (offsets == nullptr || k == nullptr || v == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
@@ -141,7 +146,7 @@ gdpa_status fwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
   const size_t need = fwd_workspace(p);
   if (p->dtype == GDPA_BF16 && (workspace == nullptr || workspace_bytes < need))
     return GDPA_ERR_WORKSPACE_TOO_SMALL;
-  if (p->total_tokens == 0) return GDPA_OK;
+  if (!launch || p->total_tokens == 0) return GDPA_OK;
 
   hipStream_t s = (hipStream_t)stream;
   gdpa::FwdArgs a{};
@@ -181,7 +186,7 @@ gdpa_status bwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
                      const void* d_o, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, void* stream, const float* score_bias = nullptr,
                      const float* out_bias = nullptr, float* d_score_bias = nullptr,
-                     float* d_out_bias = nullptr) {
+                     float* d_out_bias = nullptr, bool launch = true) {
   const gdpa_status st = check_problem(p);
   if (st != GDPA_OK) return st;
   if (offsets == nullptr || k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)
@@ -200,6 +205,7 @@ gdpa_status bwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
   const BwdPlan pl = bwd_plan(p);
   const RecomputePlan rp = recompute_plan(p, pl.total, out_bias != nullptr);
   if (workspace == nullptr || workspace_bytes < rp.total) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  if (!launch) return GDPA_OK;
 
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -332,6 +338,144 @@ gdpa_status gdpa_bwd_biased(const gdpa_problem* p, const int32_t* offsets, const
     return GDPA_ERR_INVALID_ARGUMENT;
   return bwd_impl(p, offsets, kv_offsets, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes,
                   stream, score_bias, out_bias, d_score_bias, d_out_bias);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Event-level personalisation (Kunlun paper summary, section 2.3): each event type
+// runs GDPA with its own heads, head width, context size and batch.  One grouped
+// call spreads the groups over the caller's stream and kLanes - 1 library-owned
+// streams of the current device (default priority, created on first use and kept
+// until the process ends), so that small problems share the machine instead of
+// running one after another.  The fork and the join are stream events, so the
+// call stays asynchronous and capturable; the enqueue is serialised per process.
+constexpr int kLanes = 4;
+
+struct Lanes {
+  hipStream_t s[kLanes - 1] = {};
+  hipEvent_t fork = nullptr, join[kLanes - 1] = {};
+};
+
+std::mutex g_lanes_mu;
+std::map<int, Lanes> g_lanes;
+
+hipError_t lanes_for_device(Lanes*& out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  auto it = g_lanes.find(dev);
+  if (it != g_lanes.end()) {
+    out = &it->second;
+    return hipSuccess;
+  }
+  Lanes l;
+  for (int i = 0; i < kLanes - 1 && e == hipSuccess; ++i) {
+    e = hipStreamCreateWithFlags(&l.s[i], hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&l.join[i], hipEventDisableTiming);
+  }
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&l.fork, hipEventDisableTiming);
+  if (e != hipSuccess) return e;  // a partial set is leaked, not half-used
+  out = &(g_lanes[dev] = l);
+  return hipSuccess;
+}
+
+size_t group_workspace(const gdpa_group& g, bool backward) {
+  if (check_problem(&g.problem) != GDPA_OK) return 0;
+  return backward ? bwd_plan(&g.problem).total : fwd_workspace(&g.problem);
+}
+
+double group_cost(const gdpa_group& g) {  // work estimate for the lane assignment
+  const gdpa_problem& p = g.problem;
+  return (double)p.total_tokens * p.heads * p.n_kv * p.head_dim + 1.0;
+}
+
+gdpa_status group_call(const gdpa_group& g, bool backward, char* ws, size_t bytes, void* stream, bool launch) {
+  const gdpa_problem* p = &g.problem;
+  if (!backward)
+    return fwd_impl(p, g.offsets, g.kv_offsets, g.q, g.k, g.v, g.residual, g.o, g.lse, ws, bytes, stream,
+                    nullptr, nullptr, launch);
+  return bwd_impl(p, g.offsets, g.kv_offsets, g.q, g.k, g.v, g.o, g.lse, g.d_o, g.dq, g.dk, g.dv, ws, bytes,
+                  stream, nullptr, nullptr, nullptr, nullptr, launch);
+}
+
+gdpa_status grouped_impl(int32_t groups, const gdpa_group* g, bool backward, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (groups < 1 || g == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  // Every group's arguments are checked before anything is launched; each group
+  // works in its own slice of the workspace (they run concurrently).
+  std::vector<size_t> off((size_t)groups + 1, 0);
+  for (int32_t i = 0; i < groups; ++i) {
+    const gdpa_status st = check_problem(&g[i].problem);
+    if (st != GDPA_OK) return st;
+    off[i + 1] = off[i] + align_up(group_workspace(g[i], backward));
+  }
+  if (workspace == nullptr || workspace_bytes < off[groups]) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = (char*)workspace;
+  for (int32_t i = 0; i < groups; ++i) {
+    const gdpa_status st = group_call(g[i], backward, ws + off[i], off[i + 1] - off[i], stream, false);
+    if (st != GDPA_OK) return st;
+  }
+  if (groups == 1) return group_call(g[0], backward, ws, off[1], stream, true);
+
+  // Largest groups first, each to the lane with the least work so far.
+  std::vector<int32_t> order(groups);
+  for (int32_t i = 0; i < groups; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return group_cost(g[a]) > group_cost(g[b]); });
+  std::lock_guard<std::mutex> lock(g_lanes_mu);
+  Lanes* lanes = nullptr;
+  hipError_t e = lanes_for_device(lanes);
+  if (e != hipSuccess) return hip_status(e);
+  hipStream_t caller = (hipStream_t)stream;
+  const int used = groups < kLanes ? groups : kLanes;
+  e = hipEventRecord(lanes->fork, caller);
+  for (int l = 1; l < used && e == hipSuccess; ++l) e = hipStreamWaitEvent(lanes->s[l - 1], lanes->fork, 0);
+  if (e != hipSuccess) return hip_status(e);
+  double load[kLanes] = {};
+  gdpa_status result = GDPA_OK;
+  for (int32_t i : order) {
+    int l = 0;
+    for (int c = 1; c < used; ++c)
+      if (load[c] < load[l]) l = c;
+    load[l] += group_cost(g[i]);
+    void* st = l == 0 ? stream : (void*)lanes->s[l - 1];
+    const gdpa_status r = group_call(g[i], backward, ws + off[i], off[i + 1] - off[i], st, true);
+    if (r != GDPA_OK && result == GDPA_OK) result = r;
+  }
+  // The join is enqueued whatever happened above, so the caller's stream never
+  // runs ahead of work already queued on a lane.
+  for (int l = 1; l < used; ++l) {
+    hipError_t j = hipEventRecord(lanes->join[l - 1], lanes->s[l - 1]);
+    if (j == hipSuccess) j = hipStreamWaitEvent(caller, lanes->join[l - 1], 0);
+    if (j != hipSuccess && result == GDPA_OK) result = hip_status(j);
+  }
+  return result;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdpa_grouped_workspace_bytes(int32_t groups, const gdpa_group* g, int backward) {
+  if (groups < 1 || g == nullptr) return 0;
+  size_t total = 0;
+  for (int32_t i = 0; i < groups; ++i) {
+    if (check_problem(&g[i].problem) != GDPA_OK) return 0;
+    total += align_up(group_workspace(g[i], backward != 0));
+  }
+  return total;
+}
+
+gdpa_status gdpa_fwd_grouped(int32_t groups, const gdpa_group* g, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return grouped_impl(groups, g, false, workspace, workspace_bytes, stream);
+}
+
+gdpa_status gdpa_bwd_grouped(int32_t groups, const gdpa_group* g, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return grouped_impl(groups, g, true, workspace, workspace_bytes, stream);
 }
 
 gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv) {

@@ -353,3 +353,31 @@ def draw_ffn_biases(seed: int, bias_rows_shape, B: int, H: int, d: int, out_scal
     sb = draw_normal(rng, tuple(bias_rows_shape), "f32")
     ob = draw_normal(rng, (B, H, d), "f32") * (1.0 / math.sqrt(d) if out_scale is None else out_scale)
     return sb, ob
+
+
+# Event-level personalisation: one GDPA problem per event type over the same
+# users, with sizes that follow the event's value (larger head width, more heads
+# and more context rows for the valuable, rarer events; a narrow, long sequence
+# for the plentiful low-value one).  The pages name the knobs, not their values:
+# these sizes are a synthetic reading.
+EVENT_TYPES = {
+    "click": GdpaConfig("click B=256 L~U[64,1024] H=8 d=128 n=512", 256, 8, 128, 512,
+                        ("uniform", 64, 1024), "bf16", ("silu",), backward=True),
+    "impression": GdpaConfig("impression B=256 L~U[256,2048] H=4 d=64 n=128", 256, 4, 64, 128,
+                             ("uniform", 256, 2048), "bf16", ("silu",), backward=True),
+    "conversion": GdpaConfig("conversion B=256 L~U[16,256] H=8 d=128 n=256", 256, 8, 128, 256,
+                             ("uniform", 16, 256), "bf16", ("silu",), backward=True),
+}
+
+
+def make_event_inputs(seed: int = 0, shrink: int = 1, sharp: bool = False):
+    """{event type: GdpaInputs} for EVENT_TYPES; shrink > 1 divides the batch and
+    the sequence lengths (small parity cases of the same mix)."""
+    out = {}
+    for i, (name, cfg) in enumerate(EVENT_TYPES.items()):
+        if shrink > 1:
+            kind, lo, hi = cfg.lengths
+            cfg = small_config(cfg, batch=max(cfg.batch // shrink, 2),
+                               lengths=(kind, max(lo // shrink, 1), max(hi // shrink, 2)))
+        out[name] = make_gdpa_inputs(cfg, seed=seed + 101 * i, sharp=sharp)
+    return out

@@ -181,6 +181,47 @@ gdpa_status gdpa_bwd_biased(const gdpa_problem* p, const int32_t* offsets, const
                             void* dq, void* dk, void* dv, float* d_score_bias, float* d_out_bias,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Grouped launch (event-level personalisation, Kunlun paper summary section 2.3:
+ * each event type, e.g. clicks and impressions, gets its own width, head count
+ * and other sizes).  One call runs several independent GDPA problems, each with
+ * its own gdpa_problem (heads, head_dim, n_kv, phi, dtype, scale, flags), jagged
+ * batch and tensors, as gdpa_fwd / gdpa_bwd (or the _jagged_kv forms when
+ * kv_offsets is non-NULL) would for that group alone.
+ *
+ * `groups` is a HOST array of n >= 1 descriptors; the pointers inside are device
+ * pointers with the meaning of the same-named arguments of gdpa_fwd / gdpa_bwd
+ * (the forward reads offsets, kv_offsets, q, k, v, residual and writes o, lse;
+ * the backward reads offsets, kv_offsets, q, k, v, o, lse, d_o and writes dq, dk,
+ * dv).  No two groups may write the same memory.  Workspace:
+ * gdpa_grouped_workspace_bytes (the sum of the groups' own, each 256-byte
+ * aligned).  All groups are checked before anything is launched; an invalid
+ * group fails the call with its status and launches nothing.  The groups run
+ * concurrently: the call forks from `stream` onto up to three streams that the
+ * library creates on the current device (default priority; created on first
+ * use, kept until the process ends) and joins back, all through stream events,
+ * so it stays asynchronous on `stream` and may be captured into a HIP graph.
+ * `stream` must belong to the current device. */
+typedef struct {
+  gdpa_problem problem;
+  const int32_t* offsets;    /* [B+1] token offsets */
+  const int32_t* kv_offsets; /* [B+1] context row offsets, or NULL (dense [B, n_kv, H, d]) */
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* residual;      /* forward with GDPA_FWD_RESIDUAL, else NULL */
+  void* o;                   /* forward output; backward input (softmax) */
+  float* lse;                /* forward output; backward input (softmax) */
+  const void* d_o;           /* backward */
+  void* dq;
+  void* dk;
+  void* dv;
+} gdpa_group;
+size_t gdpa_grouped_workspace_bytes(int32_t n, const gdpa_group* groups, int backward);
+gdpa_status gdpa_fwd_grouped(int32_t n, const gdpa_group* groups, void* workspace, size_t workspace_bytes,
+                             void* stream);
+gdpa_status gdpa_bwd_grouped(int32_t n, const gdpa_group* groups, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* Host-side check of a HOST copy of kv_offsets: kv_offsets[0] = 0 and every
  * sample owns 1 .. n_kv rows; GDPA_OK or GDPA_ERR_INVALID_ARGUMENT. */
 gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv);

@@ -159,3 +159,40 @@ def test_status_strings_and_offsets_check(lib):
     assert not cca.check_offsets([1, 3, 10], 10, 8)        # does not start at 0
     assert not cca.check_offsets([0, 3, 10], 11, 8)        # wrong total
     assert not cca.check_offsets([0, 3, 10], 10, 6)        # longer than max_seqlen
+
+
+def test_group_struct_matches_header(tmp_path):
+    # The ctypes mirror of gdpa_group has the C layout (size and field offsets).
+    src = tmp_path / "layout.c"
+    fields = [f for f, _ in cca.GdpaGroup._fields_]
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gdpa.h"\nint main(void) {\n'
+                   '  printf("%zu", sizeof(gdpa_group));\n'
+                   + "".join(f'  printf(" %zu", offsetof(gdpa_group, {f}));\n' for f in fields) + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(cca.GdpaGroup)] + [getattr(cca.GdpaGroup, f).offset for f in fields]
+    assert got == want
+
+
+def test_grouped_checks_every_group_first(lib):
+    arr = (cca.GdpaGroup * 3)()
+    for i, d in enumerate((32, 64, 128)):
+        arr[i].problem = P(head_dim=d)
+        arr[i].offsets, arr[i].q, arr[i].k, arr[i].v, arr[i].o = 256, 256, 256, 256, 512 + i * 64
+    one = int(lib.gdpa_workspace_bytes(ctypes.byref(P()), 0))
+    total = int(lib.gdpa_grouped_workspace_bytes(3, arr, 0))
+    assert total >= 3 * one and total % 256 == 0
+    assert int(lib.gdpa_grouped_workspace_bytes(3, arr, 1)) > 0
+    assert lib.gdpa_fwd_grouped(3, arr, V, total - 1, None) == WS_SMALL
+    assert lib.gdpa_fwd_grouped(0, arr, V, total, None) == INVALID
+    arr[2].problem = P(head_dim=48)                 # the last group is unsupported:
+    assert lib.gdpa_fwd_grouped(3, arr, V, 1 << 30, None) == UNSUPPORTED   # nothing launched
+    assert int(lib.gdpa_grouped_workspace_bytes(3, arr, 0)) == 0
+    arr[2].problem = P(head_dim=128)
+    arr[1].o = None                                 # a group without its output
+    assert lib.gdpa_fwd_grouped(3, arr, V, 1 << 30, None) == INVALID
+    arr[1].o = 2048
+    arr[0].dq = None                                # backward needs dq
+    assert lib.gdpa_bwd_grouped(3, arr, V, 1 << 30, None) == INVALID
