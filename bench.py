@@ -76,27 +76,45 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stacked_b1024_h8_d128_n25
 PMA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pma_b1024_h8_d128_m32.json")
 
 
-def kernel_source_hash():
-    """sha256 over the library's kernel sources, to tie counter readings to a kernel version."""
+# The sources each timed call's kernels are built from (plus the shared device and
+# launch headers): a committed counter reading is used only while they are unchanged.
+KERNEL_SOURCES = {
+    "gdpa_fwd": ("gdpa_fwd_res.hip", "gdpa_sched.hip"),
+    "gdpa_bwd": ("gdpa_bwd_res.hip", "gdpa_sched.hip"),
+    "weightgen_fwd": ("gdpa_gemm.hip",),
+    "weightgen_bwd": ("gdpa_gemm.hip",),
+    "pma_fwd": ("gdpa_pma.hip", "gdpa_sched.hip"),
+    "pma_bwd": ("gdpa_pma.hip", "gdpa_sched.hip"),
+}
+COMMON_SOURCES = ("gdpa_device.h", "gdpa_launch.h")
+
+
+def kernel_source_hash(kernel=None):
+    """sha256 over the sources of `kernel`'s call (every kernel source when None),
+    to tie counter readings to a kernel version."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    if kernel is None:
+        names = sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".h", ".cpp")))
+    else:
+        names = sorted(set(KERNEL_SOURCES[kernel]) | set(COMMON_SOURCES))
+    for name in names:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
 def measured_traffic(kernel, path=TRAFFIC_FILE):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None."""
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    (no reading, or the kernel's sources changed since it was taken)."""
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != kernel_source_hash():
-        return None
     k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    if k is None or kernel not in KERNEL_SOURCES or k.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return k.get("bytes_per_launch")
 
 
 def calibrate_copy(mib):

@@ -273,3 +273,62 @@ def test_fullsize_layers_compskip(gdpa_lib):
     say("  errors:", {k_: f"{e:.2e}" for k_, e in errs.items()})
     for k_, e in errs.items():
         assert e <= TOL["bf16"], (k_, e)
+
+
+@pytest.mark.parametrize("phi", ["softmax", "silu"])
+def test_fullsize_biased(gdpa_lib, phi):
+    """GDPA with FFN biases at the size `bench.py --op biased` times (the fwd+bwd
+    workload: B=256, L~U[256,2048], H=4, d=128, n=1024), on sampled samples: O, LSE,
+    dQ, dK, dV and both bias gradients of those samples."""
+    cca = gdpa_lib
+    cfg = gi.CONFIGS[4]
+    B, n, H, d = cfg.batch, cfg.n_kv, cfg.heads, cfg.head_dim
+    inp = gi.make_gdpa_inputs(cfg, seed=0)
+    sb, ob = gi.draw_ffn_biases(1, (B, n, H), B, H, d)
+    samples = pick_samples(inp.lengths)
+    say(f"case: biased phi={phi} T={inp.total_tokens} samples={samples}")
+    q, off, k, v, do = (t.cuda() for t in (inp.q, inp.offsets, inp.k, inp.v, inp.do))
+    o, lse = cca.fwd_biased(q, off, k, v, sb.cuda(), ob.cuda(), phi=phi)
+    dq, dk, dv, dsb, dob = cca.bwd_biased(q, off, k, v, sb.cuda(), ob.cuda(), o, lse, do, phi=phi)
+    torch.cuda.synchronize()
+    o_r, lse_r = orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=samples, score_bias=sb,
+                                  out_bias=ob)
+    dq_r, dk_r, dv_r, dsb_r, dob_r = orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi,
+                                                       samples=samples, score_bias=sb, bias_grads=True)
+    rows = rows_of(inp.offsets, samples)
+    s = np.asarray(samples)
+    errs = {"o": max_abs_rel(gather(o, rows), o_r[rows]), "dq": max_abs_rel(gather(dq, rows), dq_r[rows]),
+            "dk": max_abs_rel(dk.cpu()[s], dk_r[s]), "dv": max_abs_rel(dv.cpu()[s], dv_r[s]),
+            "dsb": max_abs_rel(dsb.cpu()[s], dsb_r[s]), "dob": max_abs_rel(dob.cpu()[s], dob_r[s])}
+    if lse is not None:
+        errs["lse"] = max_abs_rel(gather(lse, rows), lse_r[rows])
+    say("  errors:", {n_: f"{e:.2e}" for n_, e in errs.items()})
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (name, e)
+
+
+def test_fullsize_grouped(gdpa_lib):
+    """The grouped call over the event types at the size `bench.py --op grouped`
+    times (SiLU), each group checked on its own sampled samples."""
+    cca = gdpa_lib
+    events = gi.make_event_inputs(seed=0)
+    specs, dos = [], []
+    for inp in events.values():
+        specs.append(cca.GroupSpec(inp.q.cuda(), inp.offsets.cuda(), inp.k.cuda(), inp.v.cuda(), phi="silu"))
+        dos.append(inp.do.cuda())
+    outs = cca.fwd_grouped(specs)
+    grads = cca.bwd_grouped(specs, outs, dos)
+    torch.cuda.synchronize()
+    for i, (name, inp) in enumerate(events.items()):
+        samples = pick_samples(inp.lengths, k=2)
+        o_r, _ = orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, "silu", samples=samples)
+        dq_r, dk_r, dv_r = orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, "silu", samples=samples)
+        rows = rows_of(inp.offsets, samples)
+        s = np.asarray(samples)
+        o, _ = outs[i]
+        dq, dk, dv = grads[i]
+        errs = {"o": max_abs_rel(gather(o, rows), o_r[rows]), "dq": max_abs_rel(gather(dq, rows), dq_r[rows]),
+                "dk": max_abs_rel(dk.cpu()[s], dk_r[s]), "dv": max_abs_rel(dv.cpu()[s], dv_r[s])}
+        say(f"case: grouped {name} samples={samples}", {n_: f"{e:.2e}" for n_, e in errs.items()})
+        for key, e in errs.items():
+            assert e <= TOL["bf16"], (name, key, e)
