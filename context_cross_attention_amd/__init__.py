@@ -82,6 +82,7 @@ EXPORTS = ("gdpa_workspace_bytes", "gdpa_fwd", "gdpa_bwd", "gdpa_weightgen_fwd",
            "gdpa_fwd_jagged_kv", "gdpa_bwd_jagged_kv", "gdpa_check_kv_offsets", "gdpa_add_bf16",
            "gdpa_fwd_biased", "gdpa_bwd_biased", "gdpa_biased_workspace_bytes",
            "gdpa_grouped_workspace_bytes", "gdpa_fwd_grouped", "gdpa_bwd_grouped",
+           "gdpa_swa_block_fwd", "gdpa_swa_block_bwd",
            "gdpa_check_offsets", "gdpa_status_str", "gdpa_last_hip_error")
 
 
@@ -129,6 +130,11 @@ def load(path: str = LIB_PATH):
     for name in ("gdpa_fwd_grouped", "gdpa_bwd_grouped"):
         getattr(lib, name).argtypes = [ctypes.c_int32, GP, vp, sz, vp]
         getattr(lib, name).restype = ctypes.c_int
+    SP = ctypes.POINTER(SwaProblem)
+    lib.gdpa_swa_block_fwd.argtypes = [SP, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_swa_block_fwd.restype = ctypes.c_int
+    lib.gdpa_swa_block_bwd.argtypes = [SP, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_swa_block_bwd.restype = ctypes.c_int
     lib.gdpa_biased_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
     lib.gdpa_biased_workspace_bytes.restype = sz
     lib.gdpa_fwd_biased.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -657,6 +663,49 @@ def swa_bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Te
                             _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
                             _stream()), "gdpa_swa_bwd")
     return dq, dk, dv
+
+
+def swa_block_fwd(x: torch.Tensor, offsets: torch.Tensor, window: int, scale: Optional[float] = None,
+                  o: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Self-attention block with its residual: y = x + SWA(x, x, x).  Returns (y, o, lse);
+    o and lse are what swa_block_bwd needs."""
+    lib = load()
+    T, H, d = x.shape
+    dev = x.device
+    _require(x, "x", (T, H, d), x.dtype, dev)
+    _require(offsets, "offsets", (offsets.shape[0],), torch.int32, dev)
+    o = torch.empty_like(x) if o is None else o
+    y = torch.empty_like(x) if y is None else y
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev) if lse is None else lse
+    for name, t in (("o", o), ("y", y)):
+        _require(t, name, (T, H, d), x.dtype, dev)
+    _require(lse, "lse", (T, H), torch.float32, dev)
+    prob = _swa_problem(x, offsets, window, scale)
+    ws = _swa_workspace(prob, False, dev, workspace)
+    _check(lib.gdpa_swa_block_fwd(ctypes.byref(prob), _ptr(offsets), _ptr(x), _ptr(o), _ptr(y), _ptr(lse),
+                                  _ptr(ws), ws.numel(), _stream()), "gdpa_swa_block_fwd")
+    return y, o, lse
+
+
+def swa_block_bwd(x: torch.Tensor, offsets: torch.Tensor, o: torch.Tensor, lse: torch.Tensor, dy: torch.Tensor,
+                  window: int, scale: Optional[float] = None, dx: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Backward of swa_block_fwd: dx = dy + dQ + dK + dV.  Returns dx."""
+    lib = load()
+    T, H, d = x.shape
+    dev = x.device
+    for name, t in (("x", x), ("o", o), ("dy", dy)):
+        _require(t, name, (T, H, d), x.dtype, dev)
+    _require(lse, "lse", (T, H), torch.float32, dev)
+    _require(offsets, "offsets", (offsets.shape[0],), torch.int32, dev)
+    dx = torch.empty_like(x) if dx is None else dx
+    _require(dx, "dx", (T, H, d), x.dtype, dev)
+    prob = _swa_problem(x, offsets, window, scale)
+    ws = _swa_workspace(prob, True, dev, workspace)
+    _check(lib.gdpa_swa_block_bwd(ctypes.byref(prob), _ptr(offsets), _ptr(x), _ptr(o), _ptr(lse), _ptr(dy),
+                                  _ptr(dx), _ptr(ws), ws.numel(), _stream()), "gdpa_swa_block_bwd")
+    return dx
 
 
 def _pma_problem(seeds: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, scale: Optional[float]):

@@ -558,9 +558,15 @@ size_t gdpa_swa_workspace_bytes(const gdpa_swa_problem* p, int backward) {
   return backward ? swa_bwd_plan(p).total : align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
 }
 
-gdpa_status gdpa_swa_fwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* q,
-                         const void* k, const void* v, void* o, float* lse, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Sliding-window forward; o_plus_q != nullptr (self-attention block, q == k == v)
+// also writes the block's residual output O + Q there.
+gdpa_status swa_fwd_impl(const gdpa_swa_problem* p, const int32_t* offsets, const void* q, const void* k,
+                         const void* v, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream, void* o_plus_q) {
   const gdpa_status st = check_swa(p);
   if (st != GDPA_OK) return st;
   if (offsets == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
@@ -583,6 +589,7 @@ gdpa_status gdpa_swa_fwd(const gdpa_swa_problem* p, const int32_t* offsets, cons
   a.H = p->heads;
   a.scale = p->scale;
   a.window = p->window;
+  a.o_plus_q = o_plus_q;
   int32_t* tile_start = (int32_t*)workspace;
   hipError_t e = gdpa::launch_tile_scan(offsets, p->batch, gdpa::kFwdTileRows, tile_start, s);
   if (e != hipSuccess) return hip_status(e);
@@ -591,10 +598,13 @@ gdpa_status gdpa_swa_fwd(const gdpa_swa_problem* p, const int32_t* offsets, cons
   return hip_status(gdpa::launch_fwd_swa(a, p->head_dim, grid, s));
 }
 
-gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* q,
-                         const void* k, const void* v, const void* o, const float* lse,
-                         const void* d_o, void* dq, void* dk, void* dv, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+// Sliding-window backward; block (self-attention block, q == k == v, dk == dv ==
+// dq): dq receives d_o + dQ + dK + dV (the residual's gradient plus the three
+// attention inputs'), through the key-chunk kernel's summed epilogue and the
+// dQ kernel accumulating onto it.
+gdpa_status swa_bwd_impl(const gdpa_swa_problem* p, const int32_t* offsets, const void* q, const void* k,
+                         const void* v, const void* o, const float* lse, const void* d_o, void* dq, void* dk,
+                         void* dv, void* workspace, size_t workspace_bytes, void* stream, bool block) {
   const gdpa_status st = check_swa(p);
   if (st != GDPA_OK) return st;
   if (offsets == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
@@ -602,6 +612,10 @@ gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, cons
       (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr ||
        d_o == nullptr || dq == nullptr || dk == nullptr || dv == nullptr))
     return GDPA_ERR_INVALID_ARGUMENT;
+  if (block) {
+    if (q != k || q != v || dq != dk || dq != dv || dq == q || dq == o || dq == d_o)
+      return GDPA_ERR_INVALID_ARGUMENT;
+  } else {
   const void* outs[3] = {dq, dk, dv};
   const void* ins[5] = {q, k, v, o, d_o};
   for (int i = 0; i < 3; ++i) {
@@ -609,6 +623,7 @@ gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, cons
       if (outs[i] != nullptr && outs[i] == ins[j]) return GDPA_ERR_INVALID_ARGUMENT;
     for (int j = i + 1; j < 3; ++j)
       if (outs[i] != nullptr && outs[i] == outs[j]) return GDPA_ERR_INVALID_ARGUMENT;
+  }
   }
   const SwaBwdPlan pl = swa_bwd_plan(p);
   if (workspace == nullptr || workspace_bytes < pl.total) return GDPA_ERR_WORKSPACE_TOO_SMALL;
@@ -634,6 +649,8 @@ gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, cons
   a.chunk_start = (const int32_t*)(ws + pl.chunk_off);
   a.tile_start = (const int32_t*)(ws + pl.tile_off);
   a.window = p->window;
+  a.kv_sum_base = block ? d_o : nullptr;
+  a.dq_base = block ? dq : nullptr;
   const size_t TH = (size_t)p->total_tokens * p->heads;
   hipError_t e = gdpa::launch_softmax_dvec(o, d_o, (int)TH, p->head_dim, true, (float*)(ws + pl.dvec_off), s);
   if (e != hipSuccess) return hip_status(e);
@@ -646,6 +663,36 @@ gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, cons
   if (e != hipSuccess) return hip_status(e);
   return hip_status(gdpa::launch_bwd_dq(a, p->head_dim, gdpa::kPhiSoftmax, true,
                                         gdpa::fwd_bf16_grid(p->total_tokens, p->batch, p->heads), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdpa_status gdpa_swa_fwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* q,
+                         const void* k, const void* v, void* o, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return swa_fwd_impl(p, offsets, q, k, v, o, lse, workspace, workspace_bytes, stream, nullptr);
+}
+
+gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* q,
+                         const void* k, const void* v, const void* o, const float* lse,
+                         const void* d_o, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return swa_bwd_impl(p, offsets, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes, stream, false);
+}
+
+gdpa_status gdpa_swa_block_fwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* x, void* o,
+                               void* y, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (p != nullptr && p->total_tokens > 0 && (y == nullptr || y == x || y == o))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  return swa_fwd_impl(p, offsets, x, x, x, o, lse, workspace, workspace_bytes, stream, y);
+}
+
+gdpa_status gdpa_swa_block_bwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* x, const void* o,
+                               const float* lse, const void* d_y, void* d_x, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return swa_bwd_impl(p, offsets, x, x, x, o, lse, d_y, d_x, d_x, d_x, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

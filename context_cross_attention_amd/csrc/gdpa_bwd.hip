@@ -38,7 +38,9 @@ __device__ __forceinline__ int qpos(int t) { return (t & ~7) | ((t & 3) << 1) | 
 // used whenever several key chunks feed a query row).
 // BIAS: FFN score bias a.score_bias (per context row, added to the scaled score)
 // and its gradient a.d_score_bias (the sum of the score gradient over the tokens).
-template <int D, int PHI, int NW, bool SW = false, bool DQ = true, bool BIAS = false>
+// KVSUM (self-attention block, with SW): dk receives a.kv_sum_base + dK + dV, dv is
+// not written.
+template <int D, int PHI, int NW, bool SW = false, bool DQ = true, bool BIAS = false, bool KVSUM = false>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   constexpr int NJ = 32 * NW;          // context rows per work-group
   constexpr int BQ = kBwdRowsPerWave;  // query rows per step
@@ -277,6 +279,32 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   // dK, dV: lane (d + 32 g), register r holds context row 32 w + 8 (r / 4) + 4 g + r % 4.
   uint16_t* dkp = (uint16_t*)a.dk + (kv0 + h) * D;
   uint16_t* dvp = (uint16_t*)a.dv + (kv0 + h) * D;
+  if (KVSUM) {  // self-attention block: base + dK + dV in one tensor
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dK[dt][r] += dV[dt][r];
+    // A column block's base values are loaded before its stores: the compiler
+    // cannot prove that the stores leave the base alone, so interleaved, every
+    // load would wait for the store before it.
+    const uint16_t* bp = (const uint16_t*)a.kv_sum_base + (kv0 + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      uint16_t base[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = min(j0 + 32 * wave + 8 * (r >> 2) + 4 * g + (r & 3), n - 1);
+        base[r] = bp[(size_t)j * rs + 32 * dt + lr];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 32 * wave + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (j < n)
+          dkp[(size_t)j * rs + 32 * dt + lr] = __builtin_bit_cast(uint16_t, f2bf(bf2f(base[r]) + dK[dt][r]));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -449,8 +477,12 @@ template <int D, int NW>
 static hipError_t bwd_swa_dw(const BwdArgs& a, int max_chunks, hipStream_t s) {
   const long items = (long)max_chunks * a.H;
   if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_bf16_kernel<D, kPhiSoftmax, NW, true, false>), dim3((unsigned)items), dim3(NW * 64), 0,
-                     s, a);
+  if (a.kv_sum_base != nullptr)
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, kPhiSoftmax, NW, true, false, false, true>), dim3((unsigned)items),
+                       dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_bf16_kernel<D, kPhiSoftmax, NW, true, false>), dim3((unsigned)items), dim3(NW * 64),
+                       0, s, a);
   return hipGetLastError();
 }
 

@@ -225,6 +225,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
         bf16x4 ov;
         ov[0] = f2bf(v0); ov[1] = f2bf(v1); ov[2] = f2bf(v2); ov[3] = f2bf(v3);
         *(bf16x4*)(op + col) = ov;
+        if (SW && a.o_plus_q != nullptr) {  // the block's residual sum X + O
+          const u32x2 xq = *(const u32x2*)((const uint16_t*)a.q + base + col);
+          bf16x4 yv;
+          yv[0] = f2bf(v0 + __uint_as_float(xq[0] << 16));
+          yv[1] = f2bf(v1 + __uint_as_float(xq[0] & 0xffff0000u));
+          yv[2] = f2bf(v2 + __uint_as_float(xq[1] << 16));
+          yv[3] = f2bf(v3 + __uint_as_float(xq[1] & 0xffff0000u));
+          *(bf16x4*)((uint16_t*)a.o_plus_q + base + col) = yv;
+        }
       }
   }
 }

@@ -51,6 +51,9 @@ struct FwdArgs {
   // scaled score of context row j before phi; out_bias[(b * H + h) * d + c] to O.
   const float* score_bias;
   const float* out_bias;
+  // Self-attention block (Q = K = V = X, sliding-window forward only): when
+  // non-null, O + Q (the block's residual output) is written here as well.
+  void* o_plus_q;
 };
 
 struct BwdArgs {
@@ -69,6 +72,9 @@ struct BwdArgs {
   int n_chunks;       // work-groups per (sample, head)
   float scale;
   const void* dq_base;  // dq = dq_base + dQ when non-null (may alias dq or d_o)
+  // Self-attention block (K = V, bf16 key-chunk kernel): when non-null, dk receives
+  // kv_sum_base + dK + dV and dv is not written.
+  const void* kv_sum_base;
   // Sliding-window self-attention: K, V, dK, dV are [T,H,d] token tensors,
   // chunk_start[B+1] the prefix sums of each sample's 32 * waves-row chunks.
   const int32_t* chunk_start;

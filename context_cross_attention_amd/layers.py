@@ -26,8 +26,8 @@ from typing import Callable, Dict, List, Optional
 
 import torch
 
-from . import (add_bf16, bwd, fwd, make_problem, pma_bwd, pma_fwd, pma_workspace_bytes, swa_bwd, swa_fwd,
-               swa_workspace_bytes, weightgen_bwd_w, weightgen_fwd, workspace_bytes)
+from . import (add_bf16, bwd, fwd, make_problem, pma_bwd, pma_fwd, pma_workspace_bytes, swa_block_bwd,
+               swa_block_fwd, swa_workspace_bytes, weightgen_bwd_w, weightgen_fwd, workspace_bytes)
 
 SCHEDULES = ("full", "compskip")
 
@@ -70,9 +70,9 @@ class KunlunLayers:
         self.sa_lse = [torch.empty((T, H), dtype=torch.float32, device=dev) if s else None for _, _, s in self.ops]
         self.z = [torch.empty((B, m, H, d), dtype=bf, device=dev) if h else None for _, h, _ in self.ops]
         self.z_lse = [torch.empty((B, m, H), dtype=torch.float32, device=dev) if h else None for _, h, _ in self.ops]
-        # Backward: two gradient states, self-attention / pooling gradients, K / V gradients.
+        # Backward: two gradient states, pooling gradients, K / V gradients.
         self.gx = [tok(), tok()]
-        self.g1, self.g2, self.g3 = tok(), tok(), tok()
+        self.g2, self.g3 = tok(), tok()
         self.dk = torch.empty((B, n, H, d), dtype=bf, device=dev)
         self.dv = torch.empty((B, n, H, d), dtype=bf, device=dev)
         self.dw_k = {l: torch.empty_like(w_k[l]) for l in range(self.L) if self.ops[l][0]}
@@ -108,8 +108,8 @@ class KunlunLayers:
                 mark("hsp_fwd", False)
             if run_s:
                 mark("sa_fwd", True)
-                swa_fwd(x, self.offsets, x, x, self.w, out=self.sa_o[l], lse=self.sa_lse[l], workspace=self.ws)
-                add_bf16(self.x_out[l], x, self.sa_o[l])
+                swa_block_fwd(x, self.offsets, self.w, o=self.sa_o[l], y=self.x_out[l], lse=self.sa_lse[l],
+                              workspace=self.ws)
                 mark("sa_fwd", False)
                 x = self.x_out[l]
         return x, {l: self.z[l] for l in range(self.L) if self.z[l] is not None}
@@ -124,12 +124,10 @@ class KunlunLayers:
         for l in reversed(range(self.L)):
             run_g, run_h, run_s = self.ops[l]
             xm = self.x_mid[l] if run_g else self.x_in[l]
-            if run_s:  # X'' = X' + SWA(X', X', X')
+            if run_s:  # X'' = X' + SWA(X', X', X'): dX' = dX'' + dQ + dK + dV
                 mark("sa_bwd", True)
-                swa_bwd(xm, self.offsets, xm, xm, self.sa_o[l], self.sa_lse[l], src, self.w, dq=self.g1,
-                        dk=self.g2, dv=self.g3, workspace=self.ws)
                 dst = self.gx[flip]
-                add_bf16(dst, src, self.g1, self.g2, self.g3)
+                swa_block_bwd(xm, self.offsets, self.sa_o[l], self.sa_lse[l], src, self.w, dx=dst, workspace=self.ws)
                 mark("sa_bwd", False)
                 src, flip = dst, flip ^ 1
             if run_h:  # Z = Pool(Seeds; X', X')

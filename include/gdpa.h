@@ -285,6 +285,21 @@ gdpa_status gdpa_swa_bwd(const gdpa_swa_problem* p, const int32_t* offsets, cons
                          const void* d_o, void* dq, void* dk, void* dv, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/* Self-attention block of a Kunlun layer with its residual (Telegram review,
+ * layer step 5; the projections sit outside the op): Q = K = V = x [T,H,d] and
+ *     y = x + O,   O = SWA(x, x, x)
+ * The forward writes O (kept for the backward's softmax row term) and y in one
+ * pass; y must not alias x or o.  The backward takes the block's upstream
+ * gradient d_y (it reaches x through the residual and through O) and writes
+ *     d_x = d_y + dQ + dK + dV
+ * without separate dQ, dK, dV tensors; d_x must not alias x, o or d_y.  Problem,
+ * workspace (gdpa_swa_workspace_bytes) and errors as for gdpa_swa_fwd / _bwd. */
+gdpa_status gdpa_swa_block_fwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* x, void* o,
+                               void* y, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+gdpa_status gdpa_swa_block_bwd(const gdpa_swa_problem* p, const int32_t* offsets, const void* x, const void* o,
+                               const float* lse, const void* d_y, void* d_x, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Seed pooling attention over the same jagged batch: the attention core of
  * Pooling by Multihead Attention, whose learnable seed queries Hierarchical

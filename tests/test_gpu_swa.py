@@ -69,3 +69,32 @@ def test_swa_rejects_bad_arguments(gdpa_lib):
         cca.swa_fwd(q, off, k, v, 0)            # window < 1
     with pytest.raises(cca.GdpaError):
         cca.swa_fwd(q.float(), off, k.float(), v.float(), 4)   # fp32 not supported
+
+
+BLOCK_CASES = [((300, 0, 1, 129, 517), 2, 128, 64), ((600, 40), 1, 128, 257), ((260, 513, 33), 2, 64, 100),
+               ((260, 513, 33), 3, 32, 37)]
+
+
+@pytest.mark.parametrize("case", BLOCK_CASES, ids=lambda c: f"H{c[1]}d{c[2]}w{c[3]}L{max(c[0])}")
+def test_swa_block_parity(gdpa_lib, case):
+    # Self-attention block with its residual: y = x + SWA(x, x, x) and
+    # dx = dy + dQ + dK + dV, against the oracle composed the same way.
+    cca = gdpa_lib
+    lengths, H, d, w = case
+    inp = gi.make_swa_inputs(("explicit", list(lengths)), len(lengths), H, d, seed=6)
+    say(f"case: swa block lengths={lengths} H={H} d={d} window={w}")
+    x, dy, off = inp.q.cuda(), inp.do.cuda(), inp.offsets.cuda()
+    y, o, lse = cca.swa_block_fwd(x, off, w)
+    dx = cca.swa_block_bwd(x, off, o, lse, dy, w)
+    o2, lse2 = cca.swa_fwd(x, off, x, x, w)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = swa.swa_forward(inp.q, inp.offsets, inp.q, inp.q, w)
+    gq, gk, gv = swa.swa_backward(inp.q, inp.offsets, inp.q, inp.q, inp.do, w)
+    y_ref = inp.q.double().numpy() + o_ref
+    dx_ref = inp.do.double().numpy() + gq + gk + gv
+    errs = {"y": max_abs_rel(y, y_ref), "o": max_abs_rel(o, o_ref), "lse": max_abs_rel(lse, lse_ref),
+            "dx": max_abs_rel(dx, dx_ref)}
+    say("  errors:", {n_: f"{e:.2e}" for n_, e in errs.items()})
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], (name, e)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)   # the block's O is the plain call's
