@@ -104,7 +104,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
     __syncthreads();
     if (jb + BN < jend) gload_block(jb + BN);
 
-#pragma unroll
+    // Both 32-row halves unrolled for the maps with more elementwise work to
+    // overlap; softmax and ReLU keep one half live (unrolled, they spill).
+#pragma unroll (PHI == kPhiSoftmax || PHI == kPhiRelu ? 1 : 2)
     for (int mt = 0; mt < 2; ++mt) {
       f32x16 S = f32x16{}, dP = f32x16{};
 #pragma unroll
