@@ -65,6 +65,15 @@ BF16_SHAPES = [
     ((70, 0, 131), 2, 64, 40),
     ((64, 200, 1), 2, 32, 64),
     ((33, 97), 1, 128, 1),              # a single context row
+    # kernel-selection boundaries: largest resident forward context per head width
+    # (n d = 32768) and one row more (streaming forward), backward chunk counts
+    # with a one-row tail chunk
+    ((300, 2, 77), 2, 64, 512),
+    ((300, 2, 77), 2, 64, 513),
+    ((100, 40), 1, 32, 1024),
+    ((100, 40), 1, 32, 1025),
+    ((130, 70), 2, 128, 129),
+    ((40, 300), 1, 128, 2049),
 ]
 
 
