@@ -412,6 +412,30 @@ gdpa_status grouped_impl(int32_t groups, const gdpa_group* g, bool backward, voi
     off[i + 1] = off[i] + align_up(group_workspace(g[i], backward));
   }
   if (workspace == nullptr || workspace_bytes < off[groups]) return GDPA_ERR_WORKSPACE_TOO_SMALL;
+  // Groups run concurrently: no output may be another group's output or input.
+  auto outs_of = [&](const gdpa_group& x, const void* (&o)[3]) {
+    o[0] = backward ? x.dq : x.o;
+    o[1] = backward ? x.dk : (const void*)x.lse;
+    o[2] = backward ? x.dv : nullptr;
+  };
+  for (int32_t i = 0; i < groups; ++i) {
+    const void* oi[3];
+    outs_of(g[i], oi);
+    for (int32_t j = 0; j < groups; ++j) {
+      if (j == i) continue;
+      const void* oj[3];
+      outs_of(g[j], oj);
+      const void* ins[8] = {g[j].q, g[j].k, g[j].v, g[j].residual, g[j].d_o, g[j].offsets, g[j].kv_offsets,
+                            backward ? (const void*)g[j].o : nullptr};
+      for (const void* p : oi) {
+        if (p == nullptr) continue;
+        for (const void* q : oj)
+          if (p == q) return GDPA_ERR_INVALID_ARGUMENT;
+        for (const void* q : ins)
+          if (p == q) return GDPA_ERR_INVALID_ARGUMENT;
+      }
+    }
+  }
   char* ws = (char*)workspace;
   for (int32_t i = 0; i < groups; ++i) {
     const gdpa_status st = group_call(g[i], backward, ws + off[i], off[i + 1] - off[i], stream, false);

@@ -192,7 +192,9 @@ gdpa_status gdpa_bwd_biased(const gdpa_problem* p, const int32_t* offsets, const
  * pointers with the meaning of the same-named arguments of gdpa_fwd / gdpa_bwd
  * (the forward reads offsets, kv_offsets, q, k, v, residual and writes o, lse;
  * the backward reads offsets, kv_offsets, q, k, v, o, lse, d_o and writes dq, dk,
- * dv).  No two groups may write the same memory.  Workspace:
+ * dv).  No group's output may be another group's output or input (such a call
+ * fails with GDPA_ERR_INVALID_ARGUMENT; only equal base pointers are detected,
+ * not partial overlaps).  Workspace:
  * gdpa_grouped_workspace_bytes (the sum of the groups' own, each 256-byte
  * aligned).  All groups are checked before anything is launched; an invalid
  * group fails the call with its status and launches nothing.  The groups run

@@ -194,5 +194,10 @@ def test_grouped_checks_every_group_first(lib):
     arr[1].o = None                                 # a group without its output
     assert lib.gdpa_fwd_grouped(3, arr, V, 1 << 30, None) == INVALID
     arr[1].o = 2048
+    arr[2].o = 2048                                 # two groups writing one buffer
+    assert lib.gdpa_fwd_grouped(3, arr, V, 1 << 30, None) == INVALID
+    arr[2].o = arr[0].q                             # a group writing another's input
+    assert lib.gdpa_fwd_grouped(3, arr, V, 1 << 30, None) == INVALID
+    arr[2].o = 4096
     arr[0].dq = None                                # backward needs dq
     assert lib.gdpa_bwd_grouped(3, arr, V, 1 << 30, None) == INVALID
