@@ -41,7 +41,7 @@ __device__ __forceinline__ int qpos(int t) { return (t & ~7) | ((t & 3) << 1) | 
 // KVSUM (self-attention block, with SW): dk receives a.kv_sum_base + dK + dV, dv is
 // not written.
 template <int D, int PHI, int NW, bool SW = false, bool DQ = true, bool BIAS = false, bool KVSUM = false>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_bf16_kernel(const BwdArgs a) {
   constexpr int NJ = 32 * NW;          // context rows per work-group
   constexpr int BQ = kBwdRowsPerWave;  // query rows per step
   constexpr int KS = D / 16, DT = D / 32, LD = D + 8, CH = D / 8;
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_bf16_kernel(const BwdArgs a) {
   __shared__ __align__(16) uint16_t Kc[NJ * LD];
   __shared__ __align__(16) uint16_t Qs[BQ * LD];
   __shared__ __align__(16) uint16_t dOs[BQ * LD];
-  __shared__ __align__(16) uint16_t dSt[NJ * LDT];
+  __shared__ __align__(16) uint16_t dSt[DQ ? NJ * LDT : 8];
   __shared__ float lse_s[BQ], dvec_s[BQ];
 
   const int H = a.H, nch = a.n_chunks;
@@ -471,7 +471,12 @@ static hipError_t bwd_bf16_dw(const BwdArgs& a, int phi, bool with_dq, hipStream
   });
 }
 
-int swa_bwd_waves(int d) { return d == 32 ? 4 : 8; }
+// Sliding window: 4-wave work-groups of 128 key rows.  Without the dS^T tile
+// (dQ comes from the query-tile kernel) one takes 52 KiB of LDS, so two share a
+// CU and one's barriers and staging overlap the other's MFMAs.  The 8-wave form
+// fills a CU alone and spills registers (measured: window-512 backward 23.3 ->
+// 18.7 ms on a batch of 1.44 M tokens, H = 8, d = 128).
+int swa_bwd_waves(int d) { (void)d; return 4; }
 
 template <int D, int NW>
 static hipError_t bwd_swa_dw(const BwdArgs& a, int max_chunks, hipStream_t s) {
@@ -489,8 +494,8 @@ static hipError_t bwd_swa_dw(const BwdArgs& a, int max_chunks, hipStream_t s) {
 hipError_t launch_bwd_swa(const BwdArgs& a, int d, int max_chunks, hipStream_t s) {
   switch (d) {
     case 32: return bwd_swa_dw<32, 4>(a, max_chunks, s);
-    case 64: return bwd_swa_dw<64, 8>(a, max_chunks, s);
-    case 128: return bwd_swa_dw<128, 8>(a, max_chunks, s);
+    case 64: return bwd_swa_dw<64, 4>(a, max_chunks, s);
+    case 128: return bwd_swa_dw<128, 4>(a, max_chunks, s);
   }
   return hipErrorInvalidValue;
 }
