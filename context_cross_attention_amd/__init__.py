@@ -754,11 +754,16 @@ def pma_fwd(seeds: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torc
     return out, lse
 
 
+PMA_BWD_KV_SUM = 0x1  # gdpa_pma_bwd: dk receives dK + dV
+
+
 def pma_bwd(seeds: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             o: torch.Tensor, lse: torch.Tensor, do: torch.Tensor, scale: Optional[float] = None,
             d_seeds: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-            dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """Seed pooling attention backward of sum(O * dO).  Returns (d_seeds [m,H,d], dk, dv)."""
+            dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            kv_sum: bool = False):
+    """Seed pooling attention backward of sum(O * dO).  Returns (d_seeds [m,H,d], dk, dv);
+    with kv_sum (a sequence pooled with itself, k is v) dk holds dK + dV and dv is None."""
     lib = load()
     m, H, d = seeds.shape
     T = k.shape[0]
@@ -773,11 +778,14 @@ def pma_bwd(seeds: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torc
     _require(offsets, "offsets", (B + 1,), torch.int32, dev)
     d_seeds = torch.empty_like(seeds) if d_seeds is None else d_seeds
     dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dv = None if kv_sum else (torch.empty_like(v) if dv is None else dv)
     _require(d_seeds, "d_seeds", (m, H, d), seeds.dtype, dev)
     for name, t in (("dk", dk), ("dv", dv)):
-        _require(t, name, (T, H, d), seeds.dtype, dev)
+        if t is not None:
+            _require(t, name, (T, H, d), seeds.dtype, dev)
     prob = _pma_problem(seeds, offsets, k, scale)
+    if kv_sum:
+        prob.flags = PMA_BWD_KV_SUM
     ws = _pma_workspace(prob, True, dev, workspace)
     _check(lib.gdpa_pma_bwd(ctypes.byref(prob), _ptr(offsets), _ptr(seeds), _ptr(k), _ptr(v), _ptr(o),
                             _ptr(lse), _ptr(do), _ptr(d_seeds), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),

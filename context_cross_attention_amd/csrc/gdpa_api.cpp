@@ -733,7 +733,7 @@ gdpa_status check_pma(const gdpa_pma_problem* p) {
   if ((int64_t)p->total_tokens * p->heads > INT32_MAX) return GDPA_ERR_INVALID_ARGUMENT;
   if ((int64_t)p->batch * p->seeds * p->heads > INT32_MAX) return GDPA_ERR_INVALID_ARGUMENT;
   if (p->head_dim != 32 && p->head_dim != 64 && p->head_dim != 128) return GDPA_ERR_UNSUPPORTED;
-  if (p->seeds > 32 || p->dtype != GDPA_BF16 || p->flags != 0) return GDPA_ERR_UNSUPPORTED;
+  if (p->seeds > 32 || p->dtype != GDPA_BF16 || (p->flags & ~GDPA_PMA_BWD_KV_SUM) != 0) return GDPA_ERR_UNSUPPORTED;
   // Work-group ids: (chunks upper bound) x heads must fit a grid dimension.
   if (((int64_t)p->total_tokens / 1024 + p->batch) * p->heads + 8 > INT32_MAX)
     return GDPA_ERR_UNSUPPORTED;
@@ -802,6 +802,7 @@ gdpa_status gdpa_pma_fwd(const gdpa_pma_problem* p, const int32_t* offsets, cons
                          size_t workspace_bytes, void* stream) {
   const gdpa_status st = check_pma(p);
   if (st != GDPA_OK) return st;
+  if (p->flags != 0) return GDPA_ERR_UNSUPPORTED;  // the one flag is the backward's
   if (offsets == nullptr || seeds == nullptr || o == nullptr || lse == nullptr)
     return GDPA_ERR_INVALID_ARGUMENT;
   if (p->total_tokens > 0 && (k == nullptr || v == nullptr)) return GDPA_ERR_INVALID_ARGUMENT;
@@ -832,7 +833,9 @@ gdpa_status gdpa_pma_bwd(const gdpa_pma_problem* p, const int32_t* offsets, cons
   if (offsets == nullptr || seeds == nullptr || o == nullptr || lse == nullptr || d_o == nullptr ||
       d_seeds == nullptr)
     return GDPA_ERR_INVALID_ARGUMENT;
-  if (p->total_tokens > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+  const bool kv_sum = (p->flags & GDPA_PMA_BWD_KV_SUM) != 0;
+  if (kv_sum && dv != nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  if (p->total_tokens > 0 && (k == nullptr || v == nullptr || dk == nullptr || (!kv_sum && dv == nullptr)))
     return GDPA_ERR_INVALID_ARGUMENT;
   const void* outs[3] = {d_seeds, dk, dv};
   const void* ins[6] = {seeds, k, v, o, d_o, lse};
@@ -859,7 +862,7 @@ gdpa_status gdpa_pma_bwd(const gdpa_pma_problem* p, const int32_t* offsets, cons
   hipError_t e = pma_schedule(p, offsets, ws, pl, s);
   if (e != hipSuccess) return hip_status(e);
   const int grid = p->total_tokens > 0 ? gdpa::pma_grid(p->total_tokens, p->batch, p->heads, a.chunk) : 0;
-  return hip_status(gdpa::launch_pma_bwd(a, p->head_dim, grid, (float*)(ws + pl.extra_off), s));
+  return hip_status(gdpa::launch_pma_bwd(a, p->head_dim, grid, (float*)(ws + pl.extra_off), kv_sum, s));
 }
 
 gdpa_status gdpa_check_offsets(const int32_t* host_offsets, int32_t batch, int32_t total_tokens,

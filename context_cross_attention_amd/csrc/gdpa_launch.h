@@ -157,7 +157,8 @@ int pma_grid(int T, int B, int H, int chunk);
 hipError_t launch_pma_fwd(const PmaArgs& a, int d, int grid, hipStream_t s);
 // Backward: chunk kernel (dK, dV, dSeeds partials), then the two-level dSeeds
 // reduction through part2 [kPmaSlices][H][32][d] fp32.
-hipError_t launch_pma_bwd(const PmaArgs& a, int d, int grid, float* part2, hipStream_t s);
+// kv_sum: a.dk receives dK + dV (a.dv unused).
+hipError_t launch_pma_bwd(const PmaArgs& a, int d, int grid, float* part2, bool kv_sum, hipStream_t s);
 
 // Sliding-window self-attention on the jagged sequence (softmax, bf16): the
 // streaming kernels with K and V taken from the sample's own tokens and the

@@ -308,7 +308,8 @@ __global__ __launch_bounds__(256) void pma_combine_kernel(const PmaArgs a) {
   if ((tid & 7) == 0) *lp = (M + log2f(L)) * kLn2;
 }
 
-template <int D>
+// KVSUM: the sequence is pooled with itself (K = V); dK + dV leave as one tensor.
+template <int D, bool KVSUM>
 __global__ __launch_bounds__(64) void pma_bwd_kernel(const PmaArgs a) {
   constexpr int KS = D / 16, DT = D / 32, TS = kPmaBlock * D, NPB = D / 8;
   __shared__ __align__(1024) uint16_t ring[4 * TS];  // [slot][K | V][TS]
@@ -401,7 +402,7 @@ __global__ __launch_bounds__(64) void pma_bwd_kernel(const PmaArgs a) {
   // j + 1's NPB copies; waiting for exactly block j keeps both in flight (the
   // stores of a full block are NST instructions; only the last block can be
   // partial, and nothing waits past it).
-  constexpr int NST = 2 * (D / 16);
+  constexpr int NST = (KVSUM ? 1 : 2) * (D / 16);
   for (int j = 0; j < nb; ++j) {
     if (j == 0) {
       if (nb > 1) slot_wait<NPB>(); else slot_wait<0>();
@@ -479,14 +480,22 @@ __global__ __launch_bounds__(64) void pma_bwd_kernel(const PmaArgs a) {
     {
       constexpr int CH = D / 8, RPI = 64 / CH;
       const int c = lane % CH;
-      uint16_t* dvg = (uint16_t*)a.dv + (size_t)(ci.seq0 + tok0) * rs + (size_t)h * D + 8 * c;
+      uint16_t* dvg = KVSUM ? nullptr : (uint16_t*)a.dv + (size_t)(ci.seq0 + tok0) * rs + (size_t)h * D + 8 * c;
       uint16_t* dkg = (uint16_t*)a.dk + (size_t)(ci.seq0 + tok0) * rs + (size_t)h * D + 8 * c;
 #pragma unroll
       for (int i2 = 0; i2 < 32 / RPI; ++i2) {
         const int row = RPI * i2 + lane / CH;
         const u32x4 vv = __builtin_bit_cast(u32x4, lds_read8(Vw + tile_off<D>(row, c)));
         const u32x4 kv = __builtin_bit_cast(u32x4, lds_read8(Kt + tile_off<D>(row, c)));
-        if (row < nvalid) {
+        if (KVSUM) {
+          bf16x8 sv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sv[2 * e] = f2bf(__uint_as_float(vv[e] << 16) + __uint_as_float(kv[e] << 16));
+            sv[2 * e + 1] = f2bf(__uint_as_float(vv[e] & 0xffff0000u) + __uint_as_float(kv[e] & 0xffff0000u));
+          }
+          if (row < nvalid) *(bf16x8*)(dkg + (size_t)row * rs) = sv;
+        } else if (row < nvalid) {
           *(u32x4*)(dvg + (size_t)row * rs) = vv;
           *(u32x4*)(dkg + (size_t)row * rs) = kv;
         }
@@ -565,14 +574,20 @@ hipError_t launch_pma_fwd(const PmaArgs& a, int d, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_pma_bwd(const PmaArgs& a, int d, int grid, float* part2, hipStream_t s) {
+hipError_t launch_pma_bwd(const PmaArgs& a, int d, int grid, float* part2, bool kv_sum, hipStream_t s) {
   if (grid > 0) {
+#define GDPA_PMA_BWD(DD)                                                                               \
+  case DD:                                                                                             \
+    if (kv_sum) hipLaunchKernelGGL((pma_bwd_kernel<DD, true>), dim3(grid), dim3(64), 0, s, a);        \
+    else hipLaunchKernelGGL((pma_bwd_kernel<DD, false>), dim3(grid), dim3(64), 0, s, a);              \
+    break;
     switch (d) {
-      case 32: hipLaunchKernelGGL(pma_bwd_kernel<32>, dim3(grid), dim3(64), 0, s, a); break;
-      case 64: hipLaunchKernelGGL(pma_bwd_kernel<64>, dim3(grid), dim3(64), 0, s, a); break;
-      case 128: hipLaunchKernelGGL(pma_bwd_kernel<128>, dim3(grid), dim3(64), 0, s, a); break;
+      GDPA_PMA_BWD(32)
+      GDPA_PMA_BWD(64)
+      GDPA_PMA_BWD(128)
       default: return hipErrorInvalidValue;
     }
+#undef GDPA_PMA_BWD
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -70,9 +70,9 @@ class KunlunLayers:
         self.sa_lse = [torch.empty((T, H), dtype=torch.float32, device=dev) if s else None for _, _, s in self.ops]
         self.z = [torch.empty((B, m, H, d), dtype=bf, device=dev) if h else None for _, h, _ in self.ops]
         self.z_lse = [torch.empty((B, m, H), dtype=torch.float32, device=dev) if h else None for _, h, _ in self.ops]
-        # Backward: two gradient states, pooling gradients, K / V gradients.
+        # Backward: two gradient states, the pooling's dK + dV, GDPA's dK / dV.
         self.gx = [tok(), tok()]
-        self.g2, self.g3 = tok(), tok()
+        self.g2 = tok()
         self.dk = torch.empty((B, n, H, d), dtype=bf, device=dev)
         self.dv = torch.empty((B, n, H, d), dtype=bf, device=dev)
         self.dw_k = {l: torch.empty_like(w_k[l]) for l in range(self.L) if self.ops[l][0]}
@@ -133,9 +133,9 @@ class KunlunLayers:
             if run_h:  # Z = Pool(Seeds; X', X')
                 mark("hsp_bwd", True)
                 pma_bwd(self.seeds[l], self.offsets, xm, xm, self.z[l], self.z_lse[l], gz[l],
-                        d_seeds=self.dseeds[l], dk=self.g2, dv=self.g3, workspace=self.ws)
+                        d_seeds=self.dseeds[l], dk=self.g2, workspace=self.ws, kv_sum=True)
                 dst = self.gx[flip]
-                add_bf16(dst, src, self.g2, self.g3)
+                add_bf16(dst, src, self.g2)
                 mark("hsp_bwd", False)
                 src, flip = dst, flip ^ 1
             if run_g:  # X' = X + GDPA(X; K, V): dX = dX' + dQ

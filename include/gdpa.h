@@ -328,8 +328,12 @@ typedef struct {
   int32_t seeds;         /* m, 1 .. 32 */
   float scale;           /* finite; 1/sqrt(d) is the usual value */
   int32_t dtype;         /* GDPA_BF16 (GDPA_F32: GDPA_ERR_UNSUPPORTED) */
-  uint32_t flags;        /* must be 0 */
+  uint32_t flags;        /* 0, or GDPA_PMA_BWD_KV_SUM for gdpa_pma_bwd */
 } gdpa_pma_problem;
+
+/* gdpa_pma_bwd flag for pooling a sequence with itself (K = V = X, as HSP pools
+ * the token states): dk receives dK + dV in one tensor and dv must be NULL. */
+#define GDPA_PMA_BWD_KV_SUM 0x1u
 
 /* Workspace bytes for gdpa_pma_fwd (backward = 0) or gdpa_pma_bwd (backward != 0);
  * 0 for an invalid problem.  At most about (T / 1024 + B) * H * 128 * d bytes
@@ -345,7 +349,8 @@ gdpa_status gdpa_pma_fwd(const gdpa_pma_problem* p, const int32_t* offsets, cons
 
 /* Backward of sum(O * dO): seeds, k, v, o and lse (from gdpa_pma_fwd) and d_o
  * [B,m,H,d] in; d_seeds [m,H,d] (summed over every sample), dk and dv [T,H,d]
- * out (overwritten; distinct from the inputs and from each other). */
+ * out (overwritten; distinct from the inputs and from each other; with
+ * GDPA_PMA_BWD_KV_SUM, dk = dK + dV and dv NULL). */
 gdpa_status gdpa_pma_bwd(const gdpa_pma_problem* p, const int32_t* offsets, const void* seeds,
                          const void* k, const void* v, const void* o, const float* lse,
                          const void* d_o, void* d_seeds, void* dk, void* dv, void* workspace,

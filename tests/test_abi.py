@@ -138,7 +138,8 @@ def test_pma_workspace_sizes_and_checks(lib):
     assert W(0) >= part + chunks * 2 * 32 * 2 * 4 and W(0) % 256 == 0
     assert W(1) >= part + 32 * 2 * 32 * 128 * 4     # second-level dSeeds slices
     assert W(0, seeds=0) == 0 and W(0, seeds=33) == 0 and W(0, head_dim=48) == 0
-    assert W(1, dtype=0) == 0 and W(1, flags=1) == 0 and W(0, scale=float("inf")) == 0
+    assert W(1, dtype=0) == 0 and W(1, flags=2) == 0 and W(0, scale=float("inf")) == 0
+    assert W(1, flags=cca.PMA_BWD_KV_SUM) == W(1)   # the summed backward needs nothing more
     # Invalid arguments are reported before any HIP call.
     st = lib.gdpa_pma_fwd(ctypes.byref(prob(seeds=40)), V, V, V, V, V, V, V, 1 << 30, None)
     assert st == 2
@@ -148,6 +149,13 @@ def test_pma_workspace_sizes_and_checks(lib):
     assert st == 3                                  # workspace too small
     st = lib.gdpa_pma_bwd(ctypes.byref(prob()), V, V, V, V, V, V, V, V, V, V, V, 1 << 30, None)
     assert st == 1                                  # outputs alias inputs
+    st = lib.gdpa_pma_fwd(ctypes.byref(prob(flags=cca.PMA_BWD_KV_SUM)), V, V, V, V, ctypes.c_void_p(512), V, V,
+                          1 << 30, None)
+    assert st == 2                                  # the summed mode is the backward's
+    ks = prob(flags=cca.PMA_BWD_KV_SUM)
+    st = lib.gdpa_pma_bwd(ctypes.byref(ks), V, V, V, V, V, V, V, ctypes.c_void_p(512), ctypes.c_void_p(1024),
+                          ctypes.c_void_p(2048), V, 1 << 30, None)
+    assert st == 1                                  # dv must be NULL with dK + dV in dk
 
 
 def test_status_strings_and_offsets_check(lib):

@@ -111,3 +111,26 @@ def test_pma_rejects_bad_arguments(gdpa_lib):
     with pytest.raises(cca.GdpaError):
         cca.pma_fwd(odd, off, torch.zeros((5, 1, 48), dtype=torch.bfloat16, device="cuda"),
                     torch.zeros((5, 1, 48), dtype=torch.bfloat16, device="cuda"))
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if sum(c[0]) > 0], ids=lambda c: f"H{c[1]}d{c[2]}m{c[3]}L{max(c[0])}")
+def test_pma_self_pooling_kv_sum(gdpa_lib, case):
+    # A sequence pooled with itself (K = V = X, as HSP pools the token states): the
+    # summed backward's dk is dK + dV of the oracle, and the seed gradient and the
+    # forward are those of the plain call.
+    cca = gdpa_lib
+    lengths, H, d, m = case
+    inp = gi.make_pma_inputs(("explicit", list(lengths)), len(lengths), H, d, m, seed=9, sharp=True)
+    say(f"case: pma self-pooling lengths={lengths} H={H} d={d} m={m}")
+    seeds, x, do, off = inp.seeds.cuda(), inp.k.cuda(), inp.do.cuda(), inp.offsets.cuda()
+    o, lse = cca.pma_fwd(seeds, off, x, x)
+    ds, dkv, dv = cca.pma_bwd(seeds, off, x, x, o, lse, do, kv_sum=True)
+    ds2, dk2, dv2 = cca.pma_bwd(seeds, off, x, x, o, lse, do)
+    torch.cuda.synchronize()
+    assert dv is None and torch.equal(ds, ds2)
+    ds_ref, dk_ref, dv_ref = pma.pma_backward(inp.seeds, inp.offsets, inp.k, inp.k, inp.do)
+    err = max_abs_rel(dkv, dk_ref + dv_ref)
+    say(f"  dK + dV error {err:.2e}")
+    assert err <= TOL["bf16"]
+    # One rounding of the two bf16 results' sum.
+    assert torch.equal(dkv, (dk2.float() + dv2.float()).to(torch.bfloat16))
