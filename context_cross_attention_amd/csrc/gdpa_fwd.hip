@@ -28,11 +28,11 @@ namespace gdpa {
 template <int D, int PHI, bool RESID, bool SW = false, bool BIAS = false>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   constexpr int BM = kFwdTileRows, BN = 64, KS = D / 16, DT = D / 32;
-  // Row strides (elements), chosen for the 32-bank LDS: K rows are read 16 bytes
-  // per lane by 8 consecutive rows at a time (stride = 4 mod 32 dwords); V rows are
-  // read by transpose loads, 4 consecutive rows x 32 bytes per 16 lanes (stride =
-  // 8 or 24 mod 32 dwords).
-  constexpr int LD = D + 8, LDV = D + 16;
+  // Row strides (elements) for gfx950's 64 LDS banks: K rows are read 16 bytes per
+  // lane by 16 consecutive rows per phase (stride = 4 mod 8 dwords: 16 distinct
+  // 4-bank groups); V rows by transpose loads, 4 consecutive rows x 64 bytes per
+  // 32-lane phase (stride = 16 or 48 mod 64 dwords: the 4 rows fill all 64 banks).
+  constexpr int LD = D + 8, LDV = D == 32 ? 32 : D + 32;
   constexpr int CH = D / 8;                   // 16-byte chunks per K/V row
   constexpr int SI = (BN * CH + 255) / 256;   // staging chunks per thread per tensor
   __shared__ __align__(16) uint16_t Ks[BN * LD];
