@@ -22,6 +22,7 @@ template <int D, int PHI, bool SW, bool BIAS = false>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   constexpr int BM = kFwdTileRows, BN = 64, KS = D / 16, DT = D / 32;
   constexpr int LD = D + 8;                   // K and V rows (16-byte reads of 16 rows: distinct banks)
+  constexpr int kHalves = (PHI == kPhiSoftmax || PHI == kPhiRelu) ? 1 : 2;  // unrolled 32-row halves
   constexpr int CH = D / 8;
   constexpr int SI = (BN * CH + 255) / 256;   // staging chunks per thread per tensor
   __shared__ __align__(16) uint16_t Ks[BN * LD];
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
 
     // Both 32-row halves unrolled for the maps with more elementwise work to
     // overlap; softmax and ReLU keep one half live (unrolled, they spill).
-#pragma unroll (PHI == kPhiSoftmax || PHI == kPhiRelu ? 1 : 2)
+#pragma unroll kHalves
     for (int mt = 0; mt < 2; ++mt) {
       f32x16 S = f32x16{}, dP = f32x16{};
 #pragma unroll
