@@ -444,7 +444,7 @@ def run_jagged_kv(args):
         for b in range(B):
             chosen.append(b)
             cost += 12.0 * float(inp.lengths[b]) * float(inp.kv_counts[b]) * H * d
-            if cost >= 1.5e11:
+            if cost >= 9.0e11:
                 break
         t1 = time.perf_counter()
         orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=chosen, kv_offsets=inp.kv_offsets)
@@ -552,7 +552,7 @@ def run_biased(args):
         for b in range(B):
             chosen.append(b)
             cost += 12.0 * float(inp.lengths[b]) * n * H * d
-            if cost >= 1.5e11:
+            if cost >= 4.5e11:
                 break
         t1 = time.perf_counter()
         orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=chosen, score_bias=sb_h, out_bias=ob_h)
@@ -661,13 +661,13 @@ def run_grouped(args):
     }
     if not args.no_cpu_baseline:
         from oracle import gdpa_oracle as orc
-        inp = events["conversion"]
+        inp = events["click"]
         cfg = inp.cfg
         chosen, cost = [], 0.0
         for b in range(cfg.batch):
             chosen.append(b)
             cost += 12.0 * float(inp.lengths[b]) * cfg.n_kv * cfg.heads * cfg.head_dim
-            if cost >= 1.5e11:
+            if cost >= 3.5e11:
                 break
         t1 = time.perf_counter()
         orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=chosen)
@@ -675,7 +675,7 @@ def run_grouped(args):
         dt = time.perf_counter() - t1
         out["cpu_baseline"] = {"value": cost / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
                                "kind": "oracle",
-                               "sample": f"fwd+bwd of the conversion events on samples 0..{chosen[-1]} "
+                               "sample": f"fwd+bwd of the click events on samples 0..{chosen[-1]} "
                                          f"({len(chosen)} of {cfg.batch}); {cost / 1e9:.1f} GFLOP in {dt:.1f} s "
                                          f"(numpy float64)",
                                "seconds": round(dt, 2)}
@@ -779,7 +779,7 @@ def run_layers(args):
             if 0 < inp.lengths[b] <= 1500:
                 chosen.append(b)
                 toks += int(inp.lengths[b])
-            if toks >= 12000:
+            if toks >= 20000:
                 break
         rows = torch.cat([torch.arange(int(inp.offsets[b]), int(inp.offsets[b + 1])) for b in chosen])
         sub_off = torch.zeros(len(chosen) + 1, dtype=torch.int64)
@@ -904,7 +904,7 @@ def run_pma(args):
                 continue
             chosen.append(b)
             toks += int(inp.lengths[b])
-            if toks >= 600000:
+            if toks >= 900000:
                 break
         t1 = time.perf_counter()
         pmo.pma_forward(inp.seeds, inp.offsets, inp.k, inp.v, samples=chosen)
