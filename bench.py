@@ -444,7 +444,7 @@ def run_jagged_kv(args):
         for b in range(B):
             chosen.append(b)
             cost += 12.0 * float(inp.lengths[b]) * float(inp.kv_counts[b]) * H * d
-            if cost >= 9.0e11:
+            if cost >= 1.3e12:
                 break
         t1 = time.perf_counter()
         orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=chosen, kv_offsets=inp.kv_offsets)
