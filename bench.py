@@ -927,7 +927,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         msg = ("bench.py runs on one GPU only: GDPA shards by sample with no exchange in the "
-               "op itself, and this build measures the one-GPU share. Use --gpus 1.")
+               "op itself; the benchmark measures one GPU's share. Use --gpus 1.")
         print(msg, file=sys.stderr)
         print(json.dumps({"error": msg, "n_gpus": args.gpus}))
         sys.exit(2)
