@@ -834,7 +834,7 @@ gdpa_status gdpa_pma_bwd(const gdpa_pma_problem* p, const int32_t* offsets, cons
       d_seeds == nullptr)
     return GDPA_ERR_INVALID_ARGUMENT;
   const bool kv_sum = (p->flags & GDPA_PMA_BWD_KV_SUM) != 0;
-  if (kv_sum && dv != nullptr) return GDPA_ERR_INVALID_ARGUMENT;
+  if (kv_sum && (dv != nullptr || k != v)) return GDPA_ERR_INVALID_ARGUMENT;  // one sequence as K and V
   if (p->total_tokens > 0 && (k == nullptr || v == nullptr || dk == nullptr || (!kv_sum && dv == nullptr)))
     return GDPA_ERR_INVALID_ARGUMENT;
   const void* outs[3] = {d_seeds, dk, dv};

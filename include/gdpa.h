@@ -332,7 +332,8 @@ typedef struct {
 } gdpa_pma_problem;
 
 /* gdpa_pma_bwd flag for pooling a sequence with itself (K = V = X, as HSP pools
- * the token states): dk receives dK + dV in one tensor and dv must be NULL. */
+ * the token states): k and v must be the same pointer; dk receives dK + dV in
+ * one tensor and dv must be NULL (GDPA_ERR_INVALID_ARGUMENT otherwise). */
 #define GDPA_PMA_BWD_KV_SUM 0x1u
 
 /* Workspace bytes for gdpa_pma_fwd (backward = 0) or gdpa_pma_bwd (backward != 0);

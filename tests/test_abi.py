@@ -156,6 +156,9 @@ def test_pma_workspace_sizes_and_checks(lib):
     st = lib.gdpa_pma_bwd(ctypes.byref(ks), V, V, V, V, V, V, V, ctypes.c_void_p(512), ctypes.c_void_p(1024),
                           ctypes.c_void_p(2048), V, 1 << 30, None)
     assert st == 1                                  # dv must be NULL with dK + dV in dk
+    st = lib.gdpa_pma_bwd(ctypes.byref(ks), V, V, ctypes.c_void_p(4096), V, V, V, V, ctypes.c_void_p(512),
+                          ctypes.c_void_p(1024), None, V, 1 << 30, None)
+    assert st == 1                                  # K and V must be one sequence
 
 
 def test_status_strings_and_offsets_check(lib):
