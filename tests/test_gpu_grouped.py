@@ -114,3 +114,25 @@ def test_grouped_graph_replays(gdpa_lib):
         for g, eg in zip(grads, eager_g):
             for a, b in zip(g, eg):
                 assert torch.equal(a, b), rep
+
+
+def test_grouped_with_an_empty_group(gdpa_lib):
+    # A group whose samples are all empty runs nothing and leaves the others intact.
+    cca = gdpa_lib
+    a = gi.make_gdpa_inputs(gi.small_config(gi.EVENT_TYPES["conversion"], batch=3, lengths=("explicit", [40, 0, 77])),
+                            seed=35, sharp=True)
+    e = gi.make_gdpa_inputs(gi.small_config(gi.EVENT_TYPES["impression"], batch=2, lengths=("explicit", [0, 0])),
+                            seed=36)
+    specs = [cca.GroupSpec(x.q.cuda(), x.offsets.cuda(), x.k.cuda(), x.v.cuda(), phi=phi)
+             for x, phi in ((a, "softmax"), (e, "silu"), (a, "silu"))]
+    dos = [x.do.cuda() for x in (a, e, a)]
+    outs = cca.fwd_grouped(specs)
+    grads = cca.bwd_grouped(specs, outs, dos)
+    torch.cuda.synchronize()
+    assert outs[1][0].numel() == 0
+    assert torch.count_nonzero(grads[1][1]) == 0 or grads[1][1].numel() == 0   # empty samples: dK = 0
+    for i, phi in ((0, "softmax"), (2, "silu")):
+        o_r, _ = orc.gdpa_forward(a.q, a.offsets, a.k, a.v, phi)
+        dq_r, dk_r, dv_r = orc.gdpa_backward(a.q, a.offsets, a.k, a.v, a.do, phi)
+        for got, ref in ((outs[i][0], o_r), (grads[i][0], dq_r), (grads[i][1], dk_r), (grads[i][2], dv_r)):
+            assert max_abs_rel(got, ref) <= TOL["bf16"]
