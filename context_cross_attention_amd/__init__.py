@@ -82,7 +82,7 @@ EXPORTS = ("gdpa_workspace_bytes", "gdpa_fwd", "gdpa_bwd", "gdpa_weightgen_fwd",
            "gdpa_fwd_jagged_kv", "gdpa_bwd_jagged_kv", "gdpa_check_kv_offsets", "gdpa_add_bf16",
            "gdpa_fwd_biased", "gdpa_bwd_biased", "gdpa_biased_workspace_bytes",
            "gdpa_grouped_workspace_bytes", "gdpa_fwd_grouped", "gdpa_bwd_grouped",
-           "gdpa_swa_block_fwd", "gdpa_swa_block_bwd",
+           "gdpa_swa_block_fwd", "gdpa_swa_block_bwd", "gdpa_bwd_noalloc",
            "gdpa_check_offsets", "gdpa_status_str", "gdpa_last_hip_error")
 
 
@@ -102,6 +102,8 @@ def load(path: str = LIB_PATH):
     lib.gdpa_fwd.restype = ctypes.c_int
     lib.gdpa_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gdpa_bwd.restype = ctypes.c_int
+    lib.gdpa_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdpa_bwd_noalloc.restype = ctypes.c_int
     lib.gdpa_weightgen_fwd.argtypes = [i32, i32, i64, vp, vp, vp, vp]
     lib.gdpa_weightgen_fwd.restype = ctypes.c_int
     lib.gdpa_weightgen_bwd_w.argtypes = [i32, i32, i64, vp, vp, vp, vp]
@@ -293,6 +295,37 @@ def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                       _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
                       _stream())
     _check(st, "gdpa_bwd")
+    return dq, dk, dv
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDPA_NOALLOC_SCRATCH_BYTES of include/gdpa.h
+
+
+def bwd_noalloc(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                o: Optional[torch.Tensor], lse: Optional[torch.Tensor], do: torch.Tensor, dq: torch.Tensor,
+                dk: torch.Tensor, dv: torch.Tensor, phi: str = "softmax", scale: Optional[float] = None,
+                accumulate_dq: bool = False, residual: bool = False):
+    """gdpa_bwd_noalloc: bwd() into caller-given dq, dk, dv with the library's per-GPU
+    scratch as workspace; allocates nothing (calls on one GPU must not overlap)."""
+    lib = load()
+    B, n, H, d = k.shape
+    T = q.shape[0]
+    dev = q.device
+    for name, t in (("q", q), ("do", do), ("dq", dq)):
+        _require(t, name, (T, H, d), q.dtype, dev)
+    for name, t in (("k", k), ("v", v), ("dk", dk), ("dv", dv)):
+        _require(t, name, (B, n, H, d), q.dtype, dev)
+    _require(offsets, "offsets", (B + 1,), torch.int32, dev)
+    if phi == "softmax":
+        _require(o, "o", (T, H, d), q.dtype, dev)
+        _require(lse, "lse", (T, H), torch.float32, dev)
+    else:
+        o, lse = None, None
+    flags = (BWD_ACCUM_DQ if accumulate_dq else 0) | (BWD_RESIDUAL if residual else 0)
+    prob = make_problem(q, offsets, k, phi, scale, flags)
+    st = lib.gdpa_bwd_noalloc(ctypes.byref(prob), _ptr(offsets), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                              _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), _stream())
+    _check(st, "gdpa_bwd_noalloc")
     return dq, dk, dv
 
 

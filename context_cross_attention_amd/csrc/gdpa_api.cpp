@@ -502,6 +502,59 @@ gdpa_status gdpa_bwd_grouped(int32_t groups, const gdpa_group* g, void* workspac
   return grouped_impl(groups, g, true, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+// Scratch of gdpa_bwd_noalloc: the backward's workspace (longest-first order,
+// softmax row dots, query-tile prefix sums) for callers that cannot allocate.
+// One copy per GPU, created when the library's device code is loaded there and
+// kept until the process ends.  In host code `scratch` only names the variable;
+// its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[GDPA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on its first use).
+gdpa_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return GDPA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr) return hip_status(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdpa_status gdpa_bwd_noalloc(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
+                             const void* v, const void* o, const float* lse, const void* d_o, void* dq,
+                             void* dk, void* dv, void* stream) {
+  // Every argument check first, against the scratch size (no device call yet):
+  // a problem whose workspace exceeds it fails with GDPA_ERR_WORKSPACE_TOO_SMALL.
+  void* const unchecked = (void*)(uintptr_t)kAlign;  // stands in for the scratch address while checking
+  gdpa_status st = bwd_impl(p, offsets, nullptr, q, k, v, o, lse, d_o, dq, dk, dv, unchecked,
+                            GDPA_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, nullptr, nullptr, false);
+  if (st != GDPA_OK) return st;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != GDPA_OK) return st;
+  return bwd_impl(p, offsets, nullptr, q, k, v, o, lse, d_o, dq, dk, dv, ws, GDPA_NOALLOC_SCRATCH_BYTES,
+                  stream);
+}
+
 gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv) {
   if (host_kv_offsets == nullptr || batch < 1 || n_kv < 1) return GDPA_ERR_INVALID_ARGUMENT;
   if (host_kv_offsets[0] != 0) return GDPA_ERR_INVALID_ARGUMENT;

@@ -224,6 +224,25 @@ gdpa_status gdpa_fwd_grouped(int32_t n, const gdpa_group* groups, void* workspac
 gdpa_status gdpa_bwd_grouped(int32_t n, const gdpa_group* groups, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Backward without allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops and harnesses that forbid it):
+ * gdpa_bwd with the workspace taken from a scratch array that the library keeps
+ * on each GPU, GDPA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, set up on the first
+ * call on that GPU and held until the process ends.  Same arguments, results
+ * and errors as gdpa_bwd without the workspace; a problem whose gdpa_bwd
+ * workspace (gdpa_workspace_bytes(p, 1)) exceeds the scratch fails with
+ * GDPA_ERR_WORKSPACE_TOO_SMALL before anything is launched (for the softmax map
+ * it holds 4 * total_tokens * heads bytes of row dots, so up to about 16.7 M
+ * token-head rows; the elementwise maps need only a few bytes per sample).
+ * `stream` must belong to the current device.  The call allocates nothing and
+ * nothing in the scratch needs to start at zero.  All calls on one GPU share
+ * its scratch: two calls that overlap in time on one GPU (on different streams,
+ * or from different threads without ordering) race and give undefined results. */
+#define GDPA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdpa_status gdpa_bwd_noalloc(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
+                             const void* v, const void* o, const float* lse, const void* d_o, void* dq,
+                             void* dk, void* dv, void* stream);
+
 /* Host-side check of a HOST copy of kv_offsets: kv_offsets[0] = 0 and every
  * sample owns 1 .. n_kv rows; GDPA_OK or GDPA_ERR_INVALID_ARGUMENT. */
 gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv);

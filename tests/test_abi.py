@@ -212,3 +212,29 @@ def test_grouped_checks_every_group_first(lib):
     arr[2].o = 4096
     arr[0].dq = None                                # backward needs dq
     assert lib.gdpa_bwd_grouped(3, arr, V, 1 << 30, None) == INVALID
+
+
+def noalloc(lib, p, **ptrs):
+    a = dict(offsets=V, q=V, k=V, v=V, o=V, lse=V, do=V, dq=ctypes.c_void_p(1024),
+             dk=ctypes.c_void_p(2048), dv=ctypes.c_void_p(4096))
+    a.update(ptrs)
+    return lib.gdpa_bwd_noalloc(ctypes.byref(p), a["offsets"], a["q"], a["k"], a["v"], a["o"], a["lse"],
+                                a["do"], a["dq"], a["dk"], a["dv"], None)
+
+
+def test_bwd_noalloc_checks_before_any_device_call(lib):
+    # The allocation-free backward validates like gdpa_bwd, and rejects a problem whose
+    # workspace exceeds the per-GPU scratch, all before touching the device.
+    assert cca.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert noalloc(lib, P(head_dim=48)) == UNSUPPORTED
+    assert noalloc(lib, P(), lse=None) == INVALID
+    assert noalloc(lib, P(), dk=None) == INVALID
+    assert noalloc(lib, P(), dq=V, do=V) == INVALID
+    assert lib.gdpa_bwd_noalloc(None, V, V, V, V, V, V, V, V, V, V, None) == INVALID
+    # softmax keeps 4 bytes of row dots per (token, head): 2^24 rows no longer fit with the
+    # sample order next to them; the elementwise maps need only the order.
+    big = P(batch=4, total_tokens=1 << 22, max_seqlen=1 << 22, heads=4, head_dim=32, phi=0)
+    assert cca.workspace_bytes(big, True) > cca.NOALLOC_SCRATCH_BYTES
+    assert noalloc(lib, big) == WS_SMALL
+    fits = P(batch=4, total_tokens=(1 << 22) - 4096, max_seqlen=1 << 22, heads=4, head_dim=32, phi=0)
+    assert cca.workspace_bytes(fits, True) <= cca.NOALLOC_SCRATCH_BYTES
