@@ -242,6 +242,8 @@ def fwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     if phi != "softmax":
         lse = None
+    if lse is not None:
+        _require(lse, "lse", (T, H), torch.float32, dev)
     prob = make_problem(q, offsets, k, phi, scale, flags)
     ws = _workspace(prob, False, dev, workspace)
     st = lib.gdpa_fwd(ctypes.byref(prob), _ptr(offsets), _ptr(q), _ptr(k), _ptr(v), _ptr(residual),
@@ -357,6 +359,7 @@ def fwd_jagged_kv(q: torch.Tensor, offsets: torch.Tensor, kv_offsets: torch.Tens
     T, H, d = q.shape
     B = offsets.shape[0] - 1
     dev = q.device
+    _require(q, "q", (T, H, d), q.dtype, dev)
     _require(offsets, "offsets", (B + 1,), torch.int32, dev)
     _require(kv_offsets, "kv_offsets", (B + 1,), torch.int32, dev)
     for name, t in (("k", k), ("v", v)):
@@ -369,6 +372,7 @@ def fwd_jagged_kv(q: torch.Tensor, offsets: torch.Tensor, kv_offsets: torch.Tens
     _require(out, "out", (T, H, d), q.dtype, dev)
     if phi == "softmax":
         lse = torch.empty((T, H), dtype=torch.float32, device=dev) if lse is None else lse
+        _require(lse, "lse", (T, H), torch.float32, dev)
     else:
         lse = None
     prob = _jagged_problem(q, offsets, k, n_kv, phi, scale, flags)
@@ -389,6 +393,7 @@ def bwd_jagged_kv(q: torch.Tensor, offsets: torch.Tensor, kv_offsets: torch.Tens
     T, H, d = q.shape
     B = offsets.shape[0] - 1
     dev = q.device
+    _require(q, "q", (T, H, d), q.dtype, dev)
     _require(offsets, "offsets", (B + 1,), torch.int32, dev)
     _require(kv_offsets, "kv_offsets", (B + 1,), torch.int32, dev)
     for name, t in (("k", k), ("v", v)):
@@ -402,6 +407,9 @@ def bwd_jagged_kv(q: torch.Tensor, offsets: torch.Tensor, kv_offsets: torch.Tens
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _require(dq, "dq", (T, H, d), q.dtype, dev)
+    _require(dk, "dk", (k.shape[0], H, d), q.dtype, dev)
+    _require(dv, "dv", (k.shape[0], H, d), q.dtype, dev)
     prob = _jagged_problem(q, offsets, k, n_kv, phi, scale, 0)
     ws = _workspace(prob, True, dev, workspace)
     _check(lib.gdpa_bwd_jagged_kv(ctypes.byref(prob), _ptr(offsets), _ptr(kv_offsets), _ptr(q), _ptr(k),
@@ -453,6 +461,7 @@ def fwd_biased(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch
     lib = load()
     T, H, d = q.shape
     dev = q.device
+    _require(q, "q", (T, H, d), q.dtype, dev)
     B, n, kshape, sbshape = _biased_shapes(q, offsets, k, kv_offsets, n_kv)
     _require(offsets, "offsets", (B + 1,), torch.int32, dev)
     for name, t in (("k", k), ("v", v)):
@@ -466,6 +475,8 @@ def fwd_biased(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch
     out = torch.empty_like(q) if out is None else out
     _require(out, "out", (T, H, d), q.dtype, dev)
     lse = (torch.empty((T, H), dtype=torch.float32, device=dev) if lse is None else lse) if phi == "softmax" else None
+    if lse is not None:
+        _require(lse, "lse", (T, H), torch.float32, dev)
     prob = _jagged_problem(q, offsets, k, n, phi, scale, 0)
     ws = _workspace(prob, False, dev, workspace)
     _check(lib.gdpa_fwd_biased(ctypes.byref(prob), _ptr(offsets), _ptr(kv_offsets), _ptr(q), _ptr(k), _ptr(v),
@@ -485,6 +496,7 @@ def bwd_biased(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch
     lib = load()
     T, H, d = q.shape
     dev = q.device
+    _require(q, "q", (T, H, d), q.dtype, dev)
     B, n, kshape, sbshape = _biased_shapes(q, offsets, k, kv_offsets, n_kv)
     _require(offsets, "offsets", (B + 1,), torch.int32, dev)
     for name, t in (("k", k), ("v", v)):
@@ -529,6 +541,7 @@ class GroupSpec:
     def problem(self) -> GdpaProblem:
         T, H, d = self.q.shape
         dev = self.q.device
+        _require(self.q, "q", (T, H, d), self.q.dtype, dev)
         B = self.offsets.shape[0] - 1
         _require(self.offsets, "offsets", (B + 1,), torch.int32, dev)
         if self.kv_offsets is None:

@@ -156,16 +156,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // `src` land at LDS byte address `lds_base + 16 i` (lds_base wave-uniform).  No
 // VGPR receives data; completion is tracked by the wave's vmcnt like any vector
 // memory load, so the caller waits with s_waitcnt vmcnt before a barrier that
-// publishes the data.  M0 is not used by the compiler in the kernels that call
-// this (checked in their assembly), so it is set here without being restored.
+// publishes the data.  The compiler builtin sets M0 (the instruction's LDS base)
+// itself.
 __device__ __forceinline__ void dma16(uint32_t lds_base, const void* src) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds_base), "v"(src) : "memory");
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (GDPA_LDS void*)(uintptr_t)lds_base, 16, 0, 0);
 }
 // Same with 4 bytes per lane (lane i -> lds_base + 4 i).
 __device__ __forceinline__ void dma4(uint32_t lds_base, const void* src) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds_base), "v"(src) : "memory");
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (GDPA_LDS void*)(uintptr_t)lds_base, 4, 0, 0);
 }
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited for); N < 64 (vmcnt is split
 // over bits 3:0 and 15:14 of the immediate).

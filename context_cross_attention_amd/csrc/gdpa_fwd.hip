@@ -242,9 +242,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
 // in fp32 (the device library's expf / erff).
 template <int D, int PHI, bool RESID>
 __global__ __launch_bounds__(128) void fwd_f32_kernel(const FwdArgs a) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.T * a.H) return;
-  const int t = idx / a.H, h = idx - t * a.H;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // the grid's last block overhangs T * H
+  if (idx >= (int64_t)a.T * a.H) return;
+  const int t = (int)(idx / a.H), h = (int)(idx - (int64_t)t * a.H);
   const int b = find_sample(a.offsets, a.B, t);
   const size_t rs = (size_t)a.H * D;
   const float* qp = (const float*)a.q + (size_t)t * rs + (size_t)h * D;

@@ -1,9 +1,9 @@
 // Jagged-batch scheduling and small auxiliary passes.
 //
-// The jagged batch (per-sample user histories of irregular length, the source
-// of the "irregular tensor shapes" that the Kunlun paper summary blames for low
-// utilisation in section 1) is turned into work lists on the device, so the host
-// never has to read the offsets back.
+// The jagged batch (per-sample user histories of irregular length; Kunlun paper
+// summary, section 1, names such uneven shapes as a cause of low hardware
+// utilisation) is turned into work lists on the device, so the host never has to
+// read the offsets back.
 #include "gdpa_device.h"
 #include "gdpa_launch.h"
 
@@ -101,13 +101,15 @@ __global__ __launch_bounds__(256) void softmax_dvec_kernel(const void* __restric
                                                            float* __restrict__ dvec, const int32_t* off,
                                                            int B, int H, const float* __restrict__ ob) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements per lane
-  const int gtid = blockIdx.x * blockDim.x + threadIdx.x;
-  const int row = gtid / LPR, part = gtid % LPR;
+  // rows * LPR reaches past 2^31 for large batches (T * H >= 2^27 at d = 128): 64-bit indices.
+  const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gtid / LPR;
+  const int part = (int)(gtid % LPR);
   float acc = 0.f;
   if (row < rows) {
     const size_t base = (size_t)row * D + part * 8;
     if (ob != nullptr) {
-      const int t = row / H, h = row - t * H;
+      const int t = (int)(row / H), h = (int)(row - (int64_t)t * H);
       const float* bp = ob + ((size_t)find_sample(off, B, t) * H + h) * D + part * 8;
       if (BF16) {
         const u32x4 c = *(const u32x4*)((const uint16_t*)d_o + base);

@@ -1,8 +1,8 @@
 """Stacked residual GDPA layers with generated K/V, driven through the C ABI.
 
 Each layer (Telegram review of the Kunlun paper, layer steps 1-2; paper summary
-section 2.2: GDPA "allows stable stacking of the PFFN", read here as a plain
-residual with no normalisation):
+section 2.2, GDPA bullet: the personalised FFN becomes stable to stack, read here
+as a plain residual with no normalisation):
 
     K_l = C W_K^l^T,  V_l = C W_V^l^T             (weight generation, W: [n*H*d, c])
     X_{l+1} = X_l + GDPA_phi(X_l; K_l, V_l)       (queries are the token states)

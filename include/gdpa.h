@@ -1,12 +1,12 @@
 /*
  * gdpa.h - C ABI of the MI355X (gfx950) Generalized Dot-Product Attention library.
  *
- * GDPA (Kunlun paper summary, section 2.2 "low-level module optimisations",
+ * GDPA (Kunlun paper summary, section 2.2 on low-level module optimisations,
  * GDPA bullet) recasts the personalised FFN as one fused multi-head attention
  * operator: the tokens of a sample's user history are the queries, and weights
  * derived from that sample's non-sequential context are the keys and values
  * (Telegram review of the paper, layer steps 1 and 2: K and V are made from the
- * context features, the event sequence becomes Q and "looks at" them).
+ * context features, and the event sequence, turned into Q, attends to them).
  *
  * For a jagged batch, sample b owns token rows offsets[b] .. offsets[b+1]-1.
  * For every token t of sample b and head h:
@@ -41,8 +41,12 @@
  *     stream) and never synchronises it.  Errors in the arguments are reported
  *     before anything is launched.  A launch failure returns GDPA_ERR_HIP and
  *     stores the hipError_t for gdpa_last_hip_error() (per thread).
- *   - No exceptions cross the ABI.  The library keeps no mutable global state
- *     and is safe to call from several threads.
+ *   - No exceptions cross the ABI.  The calls are safe from several threads.
+ *     Two pieces of state live for the whole process: the grouped calls create
+ *     three streams and their events per device on first use (kept until the
+ *     process ends, guarded by a mutex), and gdpa_bwd_noalloc keeps one scratch
+ *     array per device (its address looked up once, guarded by a mutex).
+ *     Nothing else is global.
  */
 #ifndef GDPA_H
 #define GDPA_H
@@ -273,7 +277,8 @@ gdpa_status gdpa_weightgen_bwd_w(int32_t batch, int32_t ctx_dim, int64_t cols, c
  *     O[i,h,:] = sum_j softmax(s)_j V[j,h,:]
  *
  * The window is causal and holds the token and the window - 1 tokens before it
- * (the pages' "most recent interactions"; they give no formula).  bf16 only,
+ * (the pages restrict attention to a token's latest interactions and give no
+ * formula).  bf16 only,
  * fp32 accumulation; head_dim in {32, 64, 128}.
  * ------------------------------------------------------------------------- */
 typedef struct {

@@ -60,7 +60,7 @@ BF16_SHAPES = [
     ((0, 1, 127, 128, 129, 300), 2, 128, 64),
     ((5, 260, 0, 33), 3, 128, 100),     # n not a multiple of the 64-row block
     ((200, 1, 77), 2, 128, 256),        # one 8-wave backward work-group per head
-    ((150, 64, 9), 2, 128, 300),        # context rows over two backward work-groups (atomics)
+    ((150, 64, 9), 2, 128, 300),        # context rows over two backward work-groups (dQ per query tile)
     ((129, 3, 250), 4, 64, 256),
     ((70, 0, 131), 2, 64, 40),
     ((64, 200, 1), 2, 32, 64),
@@ -148,7 +148,8 @@ def test_residual_and_accumulated_dq(gdpa_lib, dtype, d, n, mode):
 
 
 def test_accumulated_dq_split_context(gdpa_lib):
-    """Accumulating dQ through the fp32 partial-sum path (context over two work-groups)."""
+    """Accumulating dQ when the context spans two key-chunk work-groups: dQ then comes
+    from the query-tile kernel, which adds the existing dq in its epilogue."""
     cca = gdpa_lib
     cfg = custom_config((100, 40), H=2, d=128, n=300, phi="softmax")
     inp = gi.make_gdpa_inputs(cfg, seed=4, sharp=True)
