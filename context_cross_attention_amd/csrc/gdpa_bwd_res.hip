@@ -19,9 +19,9 @@
 //   * The same wave writes its block transposed, with the tokens in C-tile order
 //     (B operands of dK += dS^T Q and dV += P^T dO; zero past the sample's last
 //     row), for the next step while waves 0..3 compute dQ: it waits only for its
-//     own copies, and the transposition costs the step no barrier.  Every MFMA
-//     operand read is a 16-byte, bank-conflict-free LDS read; there are no
-//     transpose loads in the loop.
+//     own copies, and the transposition costs the step no barrier.  The transposed
+//     tiles are built with transpose reads (ds_read_b64_tr_b16) and 16-byte
+//     writes.  Every MFMA operand read is a 16-byte, bank-conflict-free LDS read.
 //   * Waves 0..3 then compute dQ^T for head columns 32 w .. 32 w + 31 over all
 //     context rows (dQ^T = K^T dS^T), whose C tile (rows permuted) gives each lane
 //     16 consecutive columns of one token: 16-byte stores, residual added in fp32.
@@ -158,25 +158,41 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   };
 
   // Transposed copies of the block a copying wave brought in itself (so it only waits
-  // for its own copies): lane -> token t = lane % 32, local chunks lane / 32 and + 2;
-  // rows past the sample are zero.
+  // for its own copies).  Lane l produces head column 32 G + 16 (l / 16 % 2) + l % 16
+  // at token positions 16 kk + 8 g .. + 7 (g = l / 32) for kk = 0, 1: two transpose
+  // reads of 4 token rows each (ds_read_b64_tr_b16, conflict free on the swizzled
+  // 64-byte block rows) and one 16-byte write per tile, instead of 2-byte writes.
+  // Tokens past the sample are zeroed.
   auto transpose = [&](int st) {
     const int tq = st * BQ, rows = min(BQ, L - tq), G = wave - 4;
-    const uint16_t* Qs = (const uint16_t*)(ring + (st % NSLOT) * SLOT_B) + G * 1024;
-    const uint16_t* dOs = Qs + TILE_B / 2;
-    const int t = opaque(lr), p = tok_pos(t);
-    const bool ok = t < rows;
+    const uint8_t* Qb = ring + (st % NSLOT) * SLOT_B + G * 2048;
+    const int ln = opaque(lane), u = ln & 15, G16 = ln >> 4, gp = ln >> 5;
+    const int ch = 2 * (G16 & 1) + ((u & 3) >> 1);
+    const int col = 32 * G + 16 * (G16 & 1) + u;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int cl = (lane >> 5) + 2 * u, c = 4 * G + cl;
-      const int o = slot_off(t, cl);
-      const u32x4 qv = ok ? *(const GDPA_LDS u32x4*)&Qs[o] : u32x4{};
-      const u32x4 dv = ok ? *(const GDPA_LDS u32x4*)&dOs[o] : u32x4{};
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x4 qh[2], dh[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        Qt[(8 * c + e) * LDT + p] = half_of(qv, e);
-        dOt[(8 * c + e) * LDT + p] = half_of(dv, e);
+      for (int hh = 0; hh < 2; ++hh) {
+        // lane 4 r + c of each 16-lane group: token 16 kk + 8 hh + 4 g + r, columns
+        // 16 (G16 % 2) + 4 c .. + 3 of the block
+        const int t = 16 * kk + 8 * hh + 4 * gp + (u >> 2);
+        const int o = t * 64 + 16 * (ch ^ ((t >> 2) & 3)) + 8 * (u & 1);
+        qh[hh] = lds_read_tr4((const uint16_t*)(Qb + o));
+        dh[hh] = lds_read_tr4((const uint16_t*)(Qb + TILE_B + o));
       }
+      bf16x8 qv = cat8(qh[0], qh[1]), dv = cat8(dh[0], dh[1]);
+      if (rows < BQ) {
+        // item i is token 16 kk + 8 (i / 4) + 4 g + i % 4
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (16 * kk + 8 * (i >> 2) + 4 * gp + (i & 3) >= rows) {
+            qv[i] = (__bf16)0.f;
+            dv[i] = (__bf16)0.f;
+          }
+      }
+      *(GDPA_LDS bf16x8*)&Qt[col * LDT + 16 * kk + 8 * gp] = qv;
+      *(GDPA_LDS bf16x8*)&dOt[col * LDT + 16 * kk + 8 * gp] = dv;
     }
   };
 

@@ -156,16 +156,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // `src` land at LDS byte address `lds_base + 16 i` (lds_base wave-uniform).  No
 // VGPR receives data; completion is tracked by the wave's vmcnt like any vector
 // memory load, so the caller waits with s_waitcnt vmcnt before a barrier that
-// publishes the data.  The compiler builtin sets M0 (the instruction's LDS base)
-// itself.
+// publishes the data.  The copy takes its LDS base from M0: the asm saves M0,
+// sets it and restores it, so whatever the compiler keeps in M0 survives.  The
+// copy is written as asm rather than with the compiler builtin on purpose: the
+// builtin makes the compiler treat the LDS write as possibly aliasing every
+// later LDS read (the destination is computed), and it then waits for all
+// copies in flight (vmcnt(0)) before such reads, which serialises the prefetch
+// ring with HBM latency.  Ordering against readers is the caller's, through
+// vmcnt and a barrier.
 __device__ __forceinline__ void dma16(uint32_t lds_base, const void* src) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (GDPA_LDS void*)(uintptr_t)lds_base, 16, 0, 0);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_base), "v"(src) : "memory");
 }
 // Same with 4 bytes per lane (lane i -> lds_base + 4 i).
 __device__ __forceinline__ void dma4(uint32_t lds_base, const void* src) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (GDPA_LDS void*)(uintptr_t)lds_base, 4, 0, 0);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "s"(lds_base), "v"(src) : "memory");
 }
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt not waited for); N < 64 (vmcnt is split
 // over bits 3:0 and 15:14 of the immediate).
