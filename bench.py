@@ -194,6 +194,42 @@ def blas_threads():
     return os.cpu_count() or 1
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class CpuClock:
+    """Wall time and this process's CPU time (all its threads, user + system) over a
+    region: their ratio is the number of cores the region kept busy on average."""
+
+    def __enter__(self):
+        import resource
+        self._r = resource
+        u = resource.getrusage(resource.RUSAGE_SELF)
+        self.cpu0, self.t0 = u.ru_utime + u.ru_stime, time.perf_counter()
+        return self
+
+    def __exit__(self, *exc):
+        u = self._r.getrusage(self._r.RUSAGE_SELF)
+        self.wall = time.perf_counter() - self.t0
+        self.cpu = u.ru_utime + u.ru_stime - self.cpu0
+        return False
+
+    def fields(self):
+        eff = self.cpu / self.wall if self.wall > 0 else 0.0
+        return {"cores": max(1, int(round(eff))), "cores_effective": round(eff, 2),
+                "threads_available": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                else (os.cpu_count() or 1),
+                "blas_threads": blas_threads(), "cpu_model": cpu_model(), "processes": 1}
+
+
 def pick_samples(lengths, per_token_flops, budget_flops, cap):
     chosen, acc = [], 0.0
     for b, L in enumerate(lengths):
@@ -217,16 +253,17 @@ def cpu_baseline_stacked(inp, cfg, phi):
     x0 = inp.x0[rows]
     g = inp.do[rows]
     ctx = inp.ctx[samples]
-    t0 = time.perf_counter()
-    xs = orc.stacked_forward(x0, sub_off, ctx, inp.w_k, inp.w_v, cfg.heads, cfg.n_kv, phi)
-    orc.stacked_backward(xs, sub_off, ctx, inp.w_k, inp.w_v, g, cfg.heads, cfg.n_kv, phi)
-    dt = time.perf_counter() - t0
+    with CpuClock() as clk:
+        xs = orc.stacked_forward(x0, sub_off, ctx, inp.w_k, inp.w_v, cfg.heads, cfg.n_kv, phi)
+        orc.stacked_backward(xs, sub_off, ctx, inp.w_k, inp.w_v, g, cfg.heads, cfg.n_kv, phi)
+    dt = clk.wall
     tokens = int(sub_off[-1])
     flops = per_tok * tokens
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", **clk.fields(), "kind": "oracle",
             "sample": f"stacked {cfg.layers}-layer {phi} fwd+bwd incl. weight generation on samples "
                       f"{samples[0]}..{samples[-1]} ({len(samples)} of {cfg.batch}, {tokens} tokens); "
-                      f"GDPA FLOPs {flops / 1e9:.1f} G in {dt:.1f} s (numpy float64)",
+                      f"GDPA FLOPs {flops / 1e9:.1f} G in {dt:.1f} s (numpy float64, one process; "
+                      f"BLAS products multithreaded, elementwise work on one thread)",
             "seconds": round(dt, 2)}
 
 
@@ -235,16 +272,17 @@ def cpu_baseline_single(inp, cfg, phi):
     from oracle import gdpa_oracle as orc
     per_tok = (12.0 if cfg.backward else 4.0) * cfg.heads * cfg.n_kv * cfg.head_dim
     samples = pick_samples(inp.lengths, per_tok, 2.5e11, cfg.batch)
-    t0 = time.perf_counter()
-    orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=samples)
-    if cfg.backward:
-        orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi, samples=samples)
-    dt = time.perf_counter() - t0
+    with CpuClock() as clk:
+        orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=samples)
+        if cfg.backward:
+            orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi, samples=samples)
+    dt = clk.wall
     tokens = int(sum(inp.lengths[b] for b in samples))
     flops = per_tok * tokens
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", **clk.fields(), "kind": "oracle",
             "sample": f"{'fwd+bwd' if cfg.backward else 'fwd'} {phi} on {len(samples)} of {cfg.batch} "
-                      f"samples ({tokens} tokens); {flops / 1e9:.1f} GFLOP in {dt:.1f} s (numpy float64)",
+                      f"samples ({tokens} tokens); {flops / 1e9:.1f} GFLOP in {dt:.1f} s (numpy float64, "
+                      f"one process)",
             "seconds": round(dt, 2)}
 
 
@@ -342,13 +380,14 @@ def run_swa(args):
             cost += 12.0 * float(inp.lengths[b]) ** 2 * H * d   # the oracle forms whole L x L products
             if cost >= 3.0e11:
                 break
-        t1 = time.perf_counter()
+        clk = CpuClock().__enter__()
         swo.swa_forward(inp.q, inp.offsets, inp.k, inp.v, w, samples=chosen)
         swo.swa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, w, samples=chosen)
-        dt = time.perf_counter() - t1
+        clk.__exit__(None, None, None)
+        dt = clk.wall
         p_s = swa_pairs([inp.lengths[b] for b in chosen], w)
         fl = 12.0 * d * H * p_s
-        out["cpu_baseline"] = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+        out["cpu_baseline"] = {"value": fl / dt / 1e12, "unit": "TFLOP/s", **clk.fields(),
                                "kind": "oracle",
                                "sample": f"fwd+bwd on samples {chosen[0]}..{chosen[-1]} ({len(chosen)} of {B}); "
                                          f"{fl / 1e9:.1f} GFLOP of window pairs in {dt:.1f} s (numpy float64, "
@@ -446,11 +485,12 @@ def run_jagged_kv(args):
             cost += 12.0 * float(inp.lengths[b]) * float(inp.kv_counts[b]) * H * d
             if cost >= 1.3e12:
                 break
-        t1 = time.perf_counter()
+        clk = CpuClock().__enter__()
         orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=chosen, kv_offsets=inp.kv_offsets)
         orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi, samples=chosen, kv_offsets=inp.kv_offsets)
-        dt = time.perf_counter() - t1
-        out["cpu_baseline"] = {"value": cost / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+        clk.__exit__(None, None, None)
+        dt = clk.wall
+        out["cpu_baseline"] = {"value": cost / dt / 1e12, "unit": "TFLOP/s", **clk.fields(),
                                "kind": "oracle",
                                "sample": f"fwd+bwd on samples 0..{chosen[-1]} ({len(chosen)} of {B}); "
                                          f"{cost / 1e9:.1f} GFLOP in {dt:.1f} s (numpy float64)",
@@ -554,12 +594,13 @@ def run_biased(args):
             cost += 12.0 * float(inp.lengths[b]) * n * H * d
             if cost >= 4.5e11:
                 break
-        t1 = time.perf_counter()
+        clk = CpuClock().__enter__()
         orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=chosen, score_bias=sb_h, out_bias=ob_h)
         orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi, samples=chosen, score_bias=sb_h,
                           bias_grads=True)
-        dt = time.perf_counter() - t1
-        out["cpu_baseline"] = {"value": cost / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+        clk.__exit__(None, None, None)
+        dt = clk.wall
+        out["cpu_baseline"] = {"value": cost / dt / 1e12, "unit": "TFLOP/s", **clk.fields(),
                                "kind": "oracle",
                                "sample": f"fwd+bwd on samples 0..{chosen[-1]} ({len(chosen)} of {B}); "
                                          f"{cost / 1e9:.1f} GFLOP in {dt:.1f} s (numpy float64)",
@@ -669,11 +710,12 @@ def run_grouped(args):
             cost += 12.0 * float(inp.lengths[b]) * cfg.n_kv * cfg.heads * cfg.head_dim
             if cost >= 3.5e11:
                 break
-        t1 = time.perf_counter()
+        clk = CpuClock().__enter__()
         orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, phi, samples=chosen)
         orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, phi, samples=chosen)
-        dt = time.perf_counter() - t1
-        out["cpu_baseline"] = {"value": cost / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+        clk.__exit__(None, None, None)
+        dt = clk.wall
+        out["cpu_baseline"] = {"value": cost / dt / 1e12, "unit": "TFLOP/s", **clk.fields(),
                                "kind": "oracle",
                                "sample": f"fwd+bwd of the click events on samples 0..{chosen[-1]} "
                                          f"({len(chosen)} of {cfg.batch}); {cost / 1e9:.1f} GFLOP in {dt:.1f} s "
@@ -785,13 +827,14 @@ def run_layers(args):
         sub_off = torch.zeros(len(chosen) + 1, dtype=torch.int64)
         sub_off[1:] = torch.cumsum(torch.as_tensor(inp.lengths[chosen]), 0)
         sub_ctx, sub_dz = inp.ctx[chosen], [z[chosen] for z in inp.dz]
-        t1 = time.perf_counter()
+        clk = CpuClock().__enter__()
         recs, _, zs = cso.forward(inp.x0[rows], sub_off, sub_ctx, inp.w_k, inp.w_v, inp.seeds, H, n, w,
                                   args.schedule)
         cso.backward(recs, sub_off, sub_ctx, inp.w_k, inp.w_v, inp.seeds, H, n, w, args.schedule, inp.dx[rows],
                      {l: sub_dz[l] for l in zs})
-        dt = time.perf_counter() - t1
-        out["cpu_baseline"] = {"value": round(toks / dt, 1), "unit": "tokens/s", "cores": blas_threads(),
+        clk.__exit__(None, None, None)
+        dt = clk.wall
+        out["cpu_baseline"] = {"value": round(toks / dt, 1), "unit": "tokens/s", **clk.fields(),
                                "kind": "oracle",
                                "sample": f"fwd+bwd of the {L}-layer stack on {len(chosen)} samples ({toks} tokens); "
                                          f"{dt:.1f} s (numpy float64)", "seconds": round(dt, 2)}
@@ -906,12 +949,13 @@ def run_pma(args):
             toks += int(inp.lengths[b])
             if toks >= 900000:
                 break
-        t1 = time.perf_counter()
+        clk = CpuClock().__enter__()
         pmo.pma_forward(inp.seeds, inp.offsets, inp.k, inp.v, samples=chosen)
         pmo.pma_backward(inp.seeds, inp.offsets, inp.k, inp.v, inp.do, samples=chosen)
-        dt = time.perf_counter() - t1
+        clk.__exit__(None, None, None)
+        dt = clk.wall
         (_, bf), (_, bb) = pma_units(toks, len(chosen), H, d, m)
-        out["cpu_baseline"] = {"value": round((bf + bb) / dt / 1e9, 3), "unit": "GB/s", "cores": blas_threads(),
+        out["cpu_baseline"] = {"value": round((bf + bb) / dt / 1e9, 3), "unit": "GB/s", **clk.fields(),
                                "kind": "oracle",
                                "sample": f"fwd+bwd on samples {chosen[0]}..{chosen[-1]} ({len(chosen)} of {B}, "
                                          f"{toks} tokens); {(bf + bb) / 1e9:.2f} GB algorithmic in {dt:.1f} s "
@@ -969,6 +1013,7 @@ def main():
     marks = Marks(torch)
 
     t_gen = time.perf_counter()
+    rotate = 1
     if cfg.layers:
         inp = gi.make_stacked_inputs(cfg, seed=args.seed)
         T = int(inp.offsets[-1])
@@ -978,46 +1023,73 @@ def main():
         ctx = inp.ctx.to(dev)
         wk = [w.to(dev) for w in inp.w_k]
         wv = [w.to(dev) for w in inp.w_v]
-        if phi == "softmax":
-            sys.exit("the stacked workload uses an elementwise score map (the FFN form)")
         model = StackedGdpa(off, ctx, wk, wv, cfg.heads, cfg.n_kv, T, phi=phi)
 
-        def step():
-            model.forward(x0, marks)
-            model.backward(g, marks)
+        def step(i, mk):
+            model.forward(x0, mk)
+            model.backward(g, mk)
     else:
         inp = gi.make_gdpa_inputs(cfg, seed=args.seed)
         T = inp.total_tokens
         q, off, k, v = (t.to(dev) for t in (inp.q, inp.offsets, inp.k, inp.v))
         do = inp.do.to(dev) if inp.do is not None else None
-        o = torch.empty_like(q)
-        lse = torch.empty((T, cfg.heads), dtype=torch.float32, device=dev)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        # Working sets that the 256 MB last-level cache could hold between steps are
+        # rotated over enough copies (>= 1 GB in all) that every step reads from HBM.
+        per_step = sum(t.numel() * t.element_size() for t in (q, k, v, q) + ((do, q, q) if do is not None else ()))
+        rotate = 1 if per_step >= (512 << 20) else int(math.ceil((1 << 30) / per_step))
+        sets = []
+        for r in range(rotate):
+            qq, kk_, vv = (t.clone() for t in (q, k, v)) if r else (q, k, v)
+            sets.append(dict(q=qq, k=kk_, v=vv, do=None if do is None else (do.clone() if r else do),
+                             o=torch.empty_like(q), lse=torch.empty((T, cfg.heads), dtype=torch.float32, device=dev),
+                             dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v)))
         ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
 
-        def step():
-            marks("gdpa_fwd", True)
-            cca.fwd(q, off, k, v, phi=phi, out=o, lse=lse, workspace=ws)
-            marks("gdpa_fwd", False)
+        def step(i, mk):
+            z = sets[i % rotate]
+            mk("gdpa_fwd", True)
+            cca.fwd(z["q"], off, z["k"], z["v"], phi=phi, out=z["o"], lse=z["lse"], workspace=ws)
+            mk("gdpa_fwd", False)
             if cfg.backward:
-                marks("gdpa_bwd", True)
-                cca.bwd(q, off, k, v, o, lse, do, phi=phi, dq=dq, dk=dk, dv=dv)
-                marks("gdpa_bwd", False)
+                mk("gdpa_bwd", True)
+                cca.bwd(z["q"], off, z["k"], z["v"], z["o"], z["lse"], z["do"], phi=phi, dq=z["dq"], dk=z["dk"],
+                        dv=z["dv"])
+                mk("gdpa_bwd", False)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     print(f"# inputs ready in {t_gen:.1f} s: T={T}", file=sys.stderr, flush=True)
 
-    for _ in range(args.warmup):
-        step()
+    def no_marks(name, start):
+        return None
+
+    # Headline: exactly `steps` steps between synchronisations, nothing else inside.
+    for i in range(args.warmup):
+        step(i, no_marks)
     torch.cuda.synchronize()
-    marks.enabled = True
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i, no_marks)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    marks.enabled = False
     ms_per_step = wall * 1e3 / args.steps
+    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms per step", file=sys.stderr, flush=True)
+
+    # Statistics pass (separate from the headline): per-step HIP events and per-stage
+    # events on the library's stream over >= 50 steps and >= 1 s.
+    n_stats = max(50, int(math.ceil(1000.0 / max(ms_per_step, 1e-3))))
+    n_stats = min(n_stats, 20000)
+    step_ev = []
+    marks.enabled = True
+    for i in range(n_stats):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step(i, marks)
+        e1.record()
+        step_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    marks.enabled = False
+    step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
 
     B, H, d, n = cfg.batch, cfg.heads, cfg.head_dim, cfg.n_kv
     layers = max(cfg.layers, 1)
@@ -1035,11 +1107,20 @@ def main():
         wg_flops = layers * 2 * (f1 + f2)
     value = gdpa_flops / (ms_per_step * 1e-3) / 1e12
 
-    totals = marks.totals_ms()
-    counts = marks.counts()
-    per_launch = {k: totals[k] / counts[k] for k in totals}
-    breakdown = {k: round(totals[k] / args.steps, 4) for k in totals}
-    dom = max(totals, key=lambda k: totals[k])
+    # Per-stage times: medians over the statistics steps of each stage's time per step.
+    per_step_stage = {k: np.array([a.elapsed_time(b) for a, b in v]).reshape(n_stats, -1).sum(axis=1)
+                      for k, v in marks.pairs.items()}
+    counts = {k: len(v) // n_stats for k, v in marks.pairs.items()}
+    stage_ms = {k: float(np.median(v)) for k, v in per_step_stage.items()}
+    per_launch = {k: stage_ms[k] / counts[k] for k in stage_ms}
+    breakdown = {k: round(v, 4) for k, v in stage_ms.items()}
+    fwd_ms = stage_ms.get("gdpa_fwd", 0.0)
+    bwd_ms = stage_ms.get("gdpa_bwd", 0.0)
+    fwd_tflops = layers * fwd_f / (fwd_ms * 1e-3) / 1e12 if fwd_ms > 0 else None
+    fwd_bwd_tflops = (layers * (fwd_f + bwd_f) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+                      if cfg.backward and bwd_ms > 0 else None)
+
+    dom = max(stage_ms, key=lambda k: stage_ms[k])
     f_dom, b_dom = units[dom]
     t_dom = per_launch[dom] * 1e-3
     t_mfma, t_hbm = f_dom / (PEAK_BF16_TFLOPS * 1e12), b_dom / (PEAK_HBM_GBS * 1e9)
@@ -1064,6 +1145,9 @@ def main():
     else:
         workload = f"GDPA {'fwd+bwd' if cfg.backward else 'fwd'}: {cfg.name}, phi={phi}, T={T}"
 
+    def frac(x):
+        return None if x is None else round(x / PEAK_BF16_TFLOPS, 4)
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -1080,10 +1164,17 @@ def main():
         "config": {"workload": workload, "global_batch": B, "tokens": T, "heads": H, "head_dim": d,
                    "n_kv": n, "layers": cfg.layers or 1, "phi": phi, "seed": args.seed},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "gdpa_only_tflops": round(gdpa_flops / (sum(totals.get(k, 0.0) for k in ("gdpa_fwd", "gdpa_bwd"))
-                                               / args.steps * 1e-3) / 1e12, 2),
+        "fwd_tflops": None if fwd_tflops is None else round(fwd_tflops, 2),
+        "fwd_frac_of_bf16_peak": frac(fwd_tflops),
+        "fwd_bwd_tflops": None if fwd_bwd_tflops is None else round(fwd_bwd_tflops, 2),
+        "fwd_bwd_frac_of_bf16_peak": frac(fwd_bwd_tflops),
+        "gdpa_only_tflops": round(gdpa_flops / ((fwd_ms + bwd_ms) * 1e-3) / 1e12, 2),
         "gdpa_tflop_per_step": round(gdpa_flops / 1e12, 3),
         "e2e_tflops_incl_weightgen": round((gdpa_flops + wg_flops) / (ms_per_step * 1e-3) / 1e12, 2),
+        "step_ms_stats": {"steps": n_stats, "median": round(float(np.median(step_ms)), 4),
+                          "p10": round(float(np.percentile(step_ms, 10)), 4),
+                          "p90": round(float(np.percentile(step_ms, 90)), 4),
+                          "input_copies_rotated": rotate},
         "breakdown_ms_per_step": breakdown,
         "roofline": roof,
     }

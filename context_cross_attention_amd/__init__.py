@@ -82,7 +82,7 @@ EXPORTS = ("gdpa_workspace_bytes", "gdpa_fwd", "gdpa_bwd", "gdpa_weightgen_fwd",
            "gdpa_fwd_jagged_kv", "gdpa_bwd_jagged_kv", "gdpa_check_kv_offsets", "gdpa_add_bf16",
            "gdpa_fwd_biased", "gdpa_bwd_biased", "gdpa_biased_workspace_bytes",
            "gdpa_grouped_workspace_bytes", "gdpa_fwd_grouped", "gdpa_bwd_grouped",
-           "gdpa_swa_block_fwd", "gdpa_swa_block_bwd", "gdpa_bwd_noalloc",
+           "gdpa_swa_block_fwd", "gdpa_swa_block_bwd", "gdpa_bwd_noalloc", "gdpa_fwd_block",
            "gdpa_check_offsets", "gdpa_status_str", "gdpa_last_hip_error")
 
 
@@ -104,6 +104,8 @@ def load(path: str = LIB_PATH):
     lib.gdpa_bwd.restype = ctypes.c_int
     lib.gdpa_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdpa_bwd_noalloc.restype = ctypes.c_int
+    lib.gdpa_fwd_block.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.gdpa_fwd_block.restype = ctypes.c_int
     lib.gdpa_weightgen_fwd.argtypes = [i32, i32, i64, vp, vp, vp, vp]
     lib.gdpa_weightgen_fwd.restype = ctypes.c_int
     lib.gdpa_weightgen_bwd_w.argtypes = [i32, i32, i64, vp, vp, vp, vp]
@@ -298,6 +300,35 @@ def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                       _stream())
     _check(st, "gdpa_bwd")
     return dq, dk, dv
+
+
+def fwd_block(x: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor, phi: str = "softmax",
+              scale: Optional[float] = None, o: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Residual layer block: o = GDPA(x; k, v) and y = x + o in one pass (x [T,H,d] is
+    the queries).  Returns (o, y, lse for softmax else None)."""
+    lib = load()
+    B, n, H, d = k.shape
+    T = x.shape[0]
+    dev = x.device
+    _require(x, "x", (T, H, d), x.dtype, dev)
+    _require(k, "k", (B, n, H, d), x.dtype, dev)
+    _require(v, "v", (B, n, H, d), x.dtype, dev)
+    _require(offsets, "offsets", (B + 1,), torch.int32, dev)
+    o = torch.empty_like(x) if o is None else o
+    y = torch.empty_like(x) if y is None else y
+    _require(o, "o", (T, H, d), x.dtype, dev)
+    _require(y, "y", (T, H, d), x.dtype, dev)
+    if phi == "softmax":
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev) if lse is None else lse
+        _require(lse, "lse", (T, H), torch.float32, dev)
+    else:
+        lse = None
+    prob = make_problem(x, offsets, k, phi, scale, 0)
+    ws = _workspace(prob, False, dev, workspace)
+    _check(lib.gdpa_fwd_block(ctypes.byref(prob), _ptr(offsets), _ptr(x), _ptr(k), _ptr(v), _ptr(o), _ptr(y),
+                              _ptr(lse), _ptr(ws), ws.numel(), _stream()), "gdpa_fwd_block")
+    return o, y, lse
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # GDPA_NOALLOC_SCRATCH_BYTES of include/gdpa.h

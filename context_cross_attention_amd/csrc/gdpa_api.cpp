@@ -133,7 +133,7 @@ gdpa_status fwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
                      const void* q, const void* k, const void* v, const void* residual, void* o,
                      float* lse, void* workspace, size_t workspace_bytes, void* stream,
                      const float* score_bias = nullptr, const float* out_bias = nullptr,
-                     bool launch = true) {
+                     bool launch = true, void* o_plus_q = nullptr) {
   const gdpa_status st = check_problem(p);
   if (st != GDPA_OK) return st;
   if (offsets == nullptr || k == nullptr || v == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
@@ -160,6 +160,7 @@ gdpa_status fwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
   a.kv_offsets = kv_offsets;
   a.score_bias = score_bias;
   a.out_bias = out_bias;
+  a.o_plus_q = o_plus_q;
   a.B = p->batch;
   a.T = p->total_tokens;
   a.n = p->n_kv;
@@ -306,6 +307,17 @@ gdpa_status gdpa_bwd_jagged_kv(const gdpa_problem* p, const int32_t* offsets, co
   if (kv_offsets == nullptr) return GDPA_ERR_INVALID_ARGUMENT;
   return bwd_impl(p, offsets, kv_offsets, q, k, v, o, lse, d_o, dq, dk, dv, workspace, workspace_bytes,
                   stream);
+}
+
+gdpa_status gdpa_fwd_block(const gdpa_problem* p, const int32_t* offsets, const void* x, const void* k,
+                           const void* v, void* o, void* y, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (p != nullptr && p->flags != 0) return GDPA_ERR_UNSUPPORTED;
+  if (p != nullptr && p->total_tokens > 0 &&
+      (y == nullptr || o == nullptr || y == x || y == o || y == k || y == v))
+    return GDPA_ERR_INVALID_ARGUMENT;
+  return fwd_impl(p, offsets, nullptr, x, k, v, nullptr, o, lse, workspace, workspace_bytes, stream, nullptr,
+                  nullptr, true, y);
 }
 
 gdpa_status gdpa_add_bf16(int64_t count, void* out, const void* x0, const void* x1, const void* x2,

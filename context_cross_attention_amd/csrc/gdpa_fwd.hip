@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
         bf16x4 ov;
         ov[0] = f2bf(v0); ov[1] = f2bf(v1); ov[2] = f2bf(v2); ov[3] = f2bf(v3);
         *(bf16x4*)(op + col) = ov;
-        if (SW && a.o_plus_q != nullptr) {  // the block's residual sum X + O
+        if (a.o_plus_q != nullptr) {  // the residual block's sum X + O (X = the queries)
           const u32x2 xq = *(const u32x2*)((const uint16_t*)a.q + base + col);
           bf16x4 yv;
           yv[0] = f2bf(v0 + __uint_as_float(xq[0] << 16));
@@ -289,6 +289,11 @@ __global__ __launch_bounds__(128) void fwd_f32_kernel(const FwdArgs a) {
   const float* obp = a.out_bias != nullptr ? a.out_bias + ((size_t)b * a.H + h) * D : nullptr;
 #pragma unroll
   for (int e = 0; e < D; ++e) op[e] = acc[e] * inv + (RESID ? rp[e] : 0.f) + (obp != nullptr ? obp[e] : 0.f);
+  if (a.o_plus_q != nullptr) {  // the residual block's sum X + O (X = the queries)
+    float* yp = (float*)a.o_plus_q + (size_t)t * rs + (size_t)h * D;
+    const float* qx = (const float*)a.q + (size_t)t * rs + (size_t)h * D;
+    for (int e = 0; e < D; ++e) yp[e] = op[e] + qx[e];
+  }
   if (PHI == 0 && a.lse != nullptr) a.lse[(size_t)t * a.H + h] = m + logf(l);
 }
 

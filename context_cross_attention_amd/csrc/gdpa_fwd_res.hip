@@ -36,7 +36,9 @@ __device__ __forceinline__ int vt_row(int i) { return 16 * ((i >> 2) & 1) + 4 * 
 __device__ __forceinline__ int vt_chunk(int q, int d) { return q ^ (((d >> 4) & 1) << 3); }
 
 // RESID: 0 none, 1 residual is the query tensor, 2 a separate residual tensor,
-// 3 FFN biases (a.score_bias and / or a.out_bias; no residual).
+// 3 FFN biases (a.score_bias and / or a.out_bias; no residual), 4 residual block:
+// O to a.o and O + Q to a.o_plus_q (the layer output X + GDPA(X) with its GDPA term
+// kept, which the softmax backward needs).
 template <int D, int NMAX, int PHI, int RESID>
 __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const int32_t* __restrict__ order) {
   constexpr int NW = 8, NT = NW * 64, KS = D / 16, DT = D / 32, CH = D / 8;
@@ -245,6 +247,13 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
             const bf16x8 qv = qc[2 * dt + hh];
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] += (float)qv[e];
+          } else if (RESID == 4) {
+            const bf16x8 qv = qc[2 * dt + hh];
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = v[e] + (float)qv[e];
+            *(bf16x8*)((uint16_t*)a.o_plus_q + obase + 32 * dt + 8 * hh) =
+                pack8(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
           } else if (RESID == 2) {
             const u32x4 rr = gload16((const uint16_t*)a.residual + obase + 32 * dt + 8 * hh);
 #pragma unroll
@@ -280,13 +289,14 @@ static void fwd_res_launch(const FwdArgs& a, const int32_t* order, int resid, hi
   if (resid == 0) hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 0>), g, blk, 0, s, a, order);
   else if (resid == 1) hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 1>), g, blk, 0, s, a, order);
   else if (resid == 2) hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 2>), g, blk, 0, s, a, order);
-  else hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 3>), g, blk, 0, s, a, order);
+  else if (resid == 3) hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 3>), g, blk, 0, s, a, order);
+  else hipLaunchKernelGGL((fwd_res_kernel<D, NMAX, PHI, 4>), g, blk, 0, s, a, order);
 }
 
 template <int D, int NMAX>
 static hipError_t fwd_res_d(const FwdArgs& a, const int32_t* order, int phi, bool resid, hipStream_t s) {
   const bool biased = a.score_bias != nullptr || a.out_bias != nullptr;  // never with a residual
-  const int mode = biased ? 3 : (!resid ? 0 : (a.residual == a.q ? 1 : 2));
+  const int mode = a.o_plus_q != nullptr ? 4 : biased ? 3 : (!resid ? 0 : (a.residual == a.q ? 1 : 2));
   return dispatch_phi(phi, [&](auto P) {
     fwd_res_launch<D, NMAX, decltype(P)::value>(a, order, mode, s);
     return hipGetLastError();

@@ -11,8 +11,9 @@ Backward of sum(X_L * G):
     dX_l = dX_{l+1} + dQ_l,   dW_K^l = dK_l^T C,   dW_V^l = dV_l^T C.
 
 All buffers are allocated once; a step only sequences library calls on the
-current stream.  Only SiLU (the FFN form) is stacked: the softmax backward would
-also need each layer's un-summed output.
+current stream.  With the row softmax the backward's row term needs each layer's
+un-summed output O_l and its LSE: the forward keeps them (gdpa_fwd_block writes O_l
+and X_l + O_l in one pass); the elementwise maps need neither.
 """
 from __future__ import annotations
 
@@ -20,15 +21,13 @@ from typing import Callable, List, Optional
 
 import torch
 
-from . import bwd, fwd, weightgen_bwd_w, weightgen_fwd
+from . import bwd, fwd, fwd_block, make_problem, weightgen_bwd_w, weightgen_fwd, workspace_bytes
 
 
 class StackedGdpa:
     def __init__(self, offsets: torch.Tensor, ctx: torch.Tensor, w_k: List[torch.Tensor],
                  w_v: List[torch.Tensor], heads: int, n_kv: int, total_tokens: int,
                  phi: str = "silu", scale: Optional[float] = None):
-        if phi == "softmax":
-            raise NotImplementedError("stacked layers use an elementwise map (the FFN form)")
         dev = ctx.device
         self.offsets, self.ctx, self.w_k, self.w_v = offsets, ctx, w_k, w_v
         self.L = len(w_k)
@@ -48,8 +47,15 @@ class StackedGdpa:
         self.dv = torch.empty((B, n, H, d), dtype=bf, device=dev)
         self.dw_k = [torch.empty_like(w) for w in w_k]
         self.dw_v = [torch.empty_like(w) for w in w_v]
-        self.ws_f = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
-        self.ws_b = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+        softmax = phi == "softmax"
+        # softmax: each layer's GDPA output and LSE, kept for the backward's row term.
+        self.o = [torch.empty((T, H, d), dtype=bf, device=dev) for _ in range(self.L)] if softmax else None
+        self.lse = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(self.L)] if softmax else None
+        probe_q = torch.empty((T, H, d), dtype=bf, device="meta")
+        probe_k = torch.empty((B, n, H, d), dtype=bf, device="meta")
+        prob = make_problem(probe_q, None, probe_k, phi, scale)
+        self.ws_f = torch.empty(max(workspace_bytes(prob, False), 256), dtype=torch.uint8, device=dev)
+        self.ws_b = torch.empty(max(workspace_bytes(prob, True), 256), dtype=torch.uint8, device=dev)
 
     def forward(self, x0: torch.Tensor, mark: Optional[Callable[[str, bool], None]] = None):
         """X_0 = x0 ([T, H*d] or [T, H, d]); returns X_L ([T, H, d])."""
@@ -61,8 +67,12 @@ class StackedGdpa:
             weightgen_fwd(self.ctx, self.w_v[l], out=self.v[l].view(self.B, -1))
             mark("weightgen_fwd", False)
             mark("gdpa_fwd", True)
-            fwd(self.x[l], self.offsets, self.k[l], self.v[l], phi=self.phi, scale=self.scale,
-                residual=self.x[l], out=self.x[l + 1], workspace=self.ws_f)
+            if self.o is not None:
+                fwd_block(self.x[l], self.offsets, self.k[l], self.v[l], phi=self.phi, scale=self.scale,
+                          o=self.o[l], y=self.x[l + 1], lse=self.lse[l], workspace=self.ws_f)
+            else:
+                fwd(self.x[l], self.offsets, self.k[l], self.v[l], phi=self.phi, scale=self.scale,
+                    residual=self.x[l], out=self.x[l + 1], workspace=self.ws_f)
             mark("gdpa_fwd", False)
         return self.x[self.L]
 
@@ -74,7 +84,9 @@ class StackedGdpa:
         for i, l in enumerate(reversed(range(self.L))):
             dst = self.gx[i % 2]
             mark("gdpa_bwd", True)
-            bwd(self.x[l], self.offsets, self.k[l], self.v[l], None, None, src, phi=self.phi,
+            o_l = self.o[l] if self.o is not None else None
+            lse_l = self.lse[l] if self.lse is not None else None
+            bwd(self.x[l], self.offsets, self.k[l], self.v[l], o_l, lse_l, src, phi=self.phi,
                 scale=self.scale, dq=dst, residual=True, dk=self.dk, dv=self.dv,
                 workspace=self.ws_b)
             mark("gdpa_bwd", False)

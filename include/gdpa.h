@@ -127,6 +127,20 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
                      const void* v, const void* o, const float* lse, const void* d_o, void* dq,
                      void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Residual layer block (the stacked personalised FFN: the layer's input tokens
+ * are its queries and its output adds GDPA to them, Kunlun paper summary
+ * section 2.2, GDPA bullet, read as a plain residual): with queries x [T,H,d],
+ *     o = GDPA(x; k, v)   and   y = x + o
+ * written in one pass.  gdpa_fwd with GDPA_FWD_RESIDUAL writes only y; this call
+ * keeps o as well, which the softmax backward of such a layer needs for its row
+ * term (o taken back as y - x would carry y's rounding, relative to |x|).  The
+ * backward is gdpa_bwd with GDPA_BWD_RESIDUAL and this o.  p->flags must be 0;
+ * o and y must be distinct from each other and from x, k and v.  Otherwise as
+ * gdpa_fwd (lse written for softmax when non-NULL; workspace as gdpa_fwd's). */
+gdpa_status gdpa_fwd_block(const gdpa_problem* p, const int32_t* offsets, const void* x, const void* k,
+                           const void* v, void* o, void* y, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Jagged context (a variant of the same op: event-level personalisation gives
  * each event type its own number of context tokens, Kunlun paper summary,
  * section 2.3, Event-Level Personalization bullet; Telegram review, the list of

@@ -238,3 +238,14 @@ def test_bwd_noalloc_checks_before_any_device_call(lib):
     assert noalloc(lib, big) == WS_SMALL
     fits = P(batch=4, total_tokens=(1 << 22) - 4096, max_seqlen=1 << 22, heads=4, head_dim=32, phi=0)
     assert cca.workspace_bytes(fits, True) <= cca.NOALLOC_SCRATCH_BYTES
+
+
+def test_fwd_block_checks(lib):
+    def blk(p, o=ctypes.c_void_p(512), y=ctypes.c_void_p(768), x=V):
+        return lib.gdpa_fwd_block(ctypes.byref(p), V, x, V, V, o, y, None, V, 1 << 20, None)
+    assert blk(P(flags=cca.FWD_RESIDUAL)) == UNSUPPORTED   # the block is already residual
+    assert blk(P(), y=None) == INVALID
+    assert blk(P(), y=V) == INVALID                        # y aliases x (and k, v)
+    assert blk(P(), y=ctypes.c_void_p(512)) == INVALID     # y aliases o
+    assert blk(P(), o=V) == INVALID                        # o aliases an input
+    assert blk(P(head_dim=48)) == UNSUPPORTED

@@ -3,6 +3,7 @@ stack agrees with the oracle's own count, the window pair count is the brute-for
 count, a committed counter record is used only while its kernel sources are
 unchanged, and a multi-GPU request exits with a message before touching a GPU."""
 import json
+import time
 import os
 import subprocess
 import sys
@@ -60,3 +61,15 @@ def test_multi_gpu_request_exits_with_message():
     assert r.returncode == 2
     out = json.loads(r.stdout.strip().splitlines()[-1])
     assert out["n_gpus"] == 2 and "one GPU" in out["error"]
+
+
+def test_cpu_clock_counts_the_cores_a_region_keeps_busy():
+    # One busy thread for ~0.3 s: about one core; the CPU model is read from the host.
+    with bench.CpuClock() as clk:
+        t0 = time.perf_counter()
+        x = 0
+        while time.perf_counter() - t0 < 0.3:
+            x += 1
+    f = clk.fields()
+    assert 0.5 <= f["cores_effective"] <= 1.5 and f["cores"] == 1
+    assert f["processes"] == 1 and f["threads_available"] >= 1 and isinstance(f["cpu_model"], str)

@@ -86,17 +86,18 @@ def test_fullsize_single_layer(gdpa_lib, cfg_id):
             assert e <= TOL["bf16"], (cfg_id, phi, name, e)
 
 
-def test_fullsize_stacked(gdpa_lib):
+@pytest.mark.parametrize("phi", ["silu", "softmax"])
+def test_fullsize_stacked(gdpa_lib, phi):
     from context_cross_attention_amd.stacked import StackedGdpa
     cfg = gi.CONFIGS[5]
     inp = gi.make_stacked_inputs(cfg, seed=0)
     T = int(inp.offsets[-1])
     B, H, n, d = cfg.batch, cfg.heads, cfg.n_kv, cfg.head_dim
     samples = pick_samples(inp.lengths)
-    say(f"case: stacked config 5 T={T} samples={samples} "
+    say(f"case: stacked config 5 phi={phi} T={T} samples={samples} "
         f"(lengths {[int(inp.lengths[b]) for b in samples]})")
     model = StackedGdpa(inp.offsets.cuda(), inp.ctx.cuda(), [w.cuda() for w in inp.w_k],
-                        [w.cuda() for w in inp.w_v], H, n, T, phi="silu")
+                        [w.cuda() for w in inp.w_v], H, n, T, phi=phi)
     x_last = model.forward(inp.x0.cuda())
     dx0, dwk, dwv = model.backward(inp.do.cuda())
     torch.cuda.synchronize()
@@ -108,8 +109,8 @@ def test_fullsize_stacked(gdpa_lib):
     wv = [orc.as_f64(w) for w in inp.w_v]
     ctx = orc.as_f64(inp.ctx)[samples]
     idx = torch.from_numpy(rows)
-    xs = orc.stacked_forward(inp.x0[idx], sub_off, ctx, wk, wv, H, n, "silu")
-    gx, _, _ = orc.stacked_backward(xs, sub_off, ctx, wk, wv, inp.do[idx], H, n, "silu")
+    xs = orc.stacked_forward(inp.x0[idx], sub_off, ctx, wk, wv, H, n, phi)
+    gx, _, _ = orc.stacked_backward(xs, sub_off, ctx, wk, wv, inp.do[idx], H, n, phi)
     errs = {"x_last": max_abs_rel(gather(x_last.reshape(T, -1), rows), xs[-1]),
             "dx0": max_abs_rel(gather(dx0.reshape(T, -1), rows), gx)}
 

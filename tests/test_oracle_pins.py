@@ -394,12 +394,14 @@ def stacked_problem(seed=18, lengths=(3, 0, 5), H=2, d=4, n=3, C=5, layers=2):
     return off, x0, ctx, wk, wv, g
 
 
-def test_stacked_matches_torch_autograd():
+@pytest.mark.parametrize("phi", ["silu", "softmax"])
+def test_stacked_matches_torch_autograd(phi):
     off, x0, ctx, wk, wv, g = stacked_problem()
     H, n, d = 2, 3, 4
-    xs = orc.stacked_forward(x0, off, ctx, wk, wv, H, n, "silu")
-    dx0, dwk, dwv = orc.stacked_backward(xs, off, ctx, wk, wv, g, H, n, "silu")
-    # torch fp64 autograd of the same graph, built from linear layers and SiLU.
+    xs = orc.stacked_forward(x0, off, ctx, wk, wv, H, n, phi)
+    dx0, dwk, dwv = orc.stacked_backward(xs, off, ctx, wk, wv, g, H, n, phi)
+    # torch fp64 autograd of the same graph, built from linear layers and SiLU (the FFN
+    # form) or a row softmax at scale 1/sqrt(d) (attention).
     xt = torch.from_numpy(x0.copy()).requires_grad_()
     ct = torch.from_numpy(ctx)
     wkt = [torch.from_numpy(w.copy()).requires_grad_() for w in wk]
@@ -411,7 +413,9 @@ def test_stacked_matches_torch_autograd():
         rows = []
         for b in range(3):
             xb = x[off[b]:off[b + 1]].reshape(-1, H, d).transpose(0, 1)
-            ob = F.silu(xb @ kl[b].transpose(0, 1).transpose(1, 2)) @ vl[b].transpose(0, 1)
+            sc = xb @ kl[b].transpose(0, 1).transpose(1, 2)
+            pm = F.silu(sc) if phi == "silu" else torch.softmax(sc / math.sqrt(d), dim=-1)
+            ob = pm @ vl[b].transpose(0, 1)
             rows.append(ob.transpose(0, 1).reshape(-1, H * d))
         x = x + torch.cat(rows, 0)
         assert rel_err(xs[l + 1], x.detach().numpy()) <= 1e-13
