@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--phi", default=None, choices=[None, "softmax", "silu", "relu", "gelu", "identity"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stats-steps", type=int, default=0,
+                    help="steps of the statistics pass (default: >= 50 and >= 1 s); small values for profiler runs")
     ap.add_argument("--op", default="gdpa", choices=["gdpa", "swa", "pma", "jagged_kv", "layers", "biased",
                                                    "grouped"],
                     help="swa: sliding-window self-attention on the stacked workload's batch; "
@@ -1077,7 +1079,7 @@ def main():
     # Statistics pass (separate from the headline): per-step HIP events and per-stage
     # events on the library's stream over >= 50 steps and >= 1 s.
     n_stats = max(50, int(math.ceil(1000.0 / max(ms_per_step, 1e-3))))
-    n_stats = min(n_stats, 20000)
+    n_stats = min(n_stats, 20000) if args.stats_steps <= 0 else args.stats_steps
     step_ev = []
     marks.enabled = True
     for i in range(n_stats):
