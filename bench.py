@@ -74,47 +74,46 @@ def parse():
 
 
 CSRC = os.path.join(ROOT, "context_cross_attention_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stacked_b1024_h8_d128_n256.json")
-PMA_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pma_b1024_h8_d128_m32.json")
-
-
-# The sources each timed call's kernels are built from (plus the shared device and
-# launch headers): a committed counter reading is used only while they are unchanged.
-KERNEL_SOURCES = {
-    "gdpa_fwd": ("gdpa_fwd_res.hip", "gdpa_sched.hip"),
-    "gdpa_bwd": ("gdpa_bwd_res.hip", "gdpa_sched.hip"),
-    "weightgen_fwd": ("gdpa_gemm.hip",),
-    "weightgen_bwd": ("gdpa_gemm.hip",),
-    "pma_fwd": ("gdpa_pma.hip", "gdpa_sched.hip"),
-    "pma_bwd": ("gdpa_pma.hip", "gdpa_sched.hip"),
+# Committed counter records of HBM traffic, one per bench workload ((config, phi) or op).
+TRAFFIC_FILES = {
+    (5, "silu"): "traffic_stacked_b1024_h8_d128_n256_silu.json",
+    (3, "softmax"): "traffic_fwd_b512_h8_d128_n512_softmax.json",
+    (4, "softmax"): "traffic_fwdbwd_b256_h4_d128_n1024_softmax.json",
+    "pma": "traffic_pma_b1024_h8_d128_m32.json",
 }
+# Shared device and launch headers: part of every call's kernels.
 COMMON_SOURCES = ("gdpa_device.h", "gdpa_launch.h")
 
 
-def kernel_source_hash(kernel=None):
-    """sha256 over the sources of `kernel`'s call (every kernel source when None),
-    to tie counter readings to a kernel version."""
+def traffic_file(key):
+    """Path of the counter record of workload `key`, or None when none was taken."""
+    name = TRAFFIC_FILES.get(key)
+    return os.path.join(ROOT, "profiles", name) if name else None
+
+
+def source_hash(sources):
+    """sha256 over the named kernel sources and the shared headers, to tie a counter
+    reading to the kernel version it was taken on."""
     h = hashlib.sha256()
-    if kernel is None:
-        names = sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".h", ".cpp")))
-    else:
-        names = sorted(set(KERNEL_SOURCES[kernel]) | set(COMMON_SOURCES))
-    for name in names:
+    for name in sorted(set(sources) | set(COMMON_SOURCES)):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def measured_traffic(kernel, path=TRAFFIC_FILE):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or None
-    (no reading, or the kernel's sources changed since it was taken)."""
+def measured_traffic(stage, path):
+    """HBM bytes per launch of `stage` from a committed counter record, or None (no
+    record for the workload, no reading for the stage, or the sources the record names
+    changed since it was taken)."""
+    if path is None:
+        return None
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    if k is None or kernel not in KERNEL_SOURCES or k.get("source_sha256") != kernel_source_hash(kernel):
+    k = rec.get("kernels", {}).get(stage)
+    if not k or not k.get("sources") or k.get("source_sha256") != source_hash(k["sources"]):
         return None
     return k.get("bytes_per_launch")
 
@@ -922,7 +921,7 @@ def run_pma(args):
     t_dom = totals[dom] / counts[dom] * 1e-3
     f_dom, b_dom = units[dom]
     roof = {"bound": "hbm", "achieved": round(b_dom / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=measured_traffic(dom, PMA_TRAFFIC_FILE),
+    roof.update(frac=round(roof["achieved"] / roof["peak"], 4), traffic=measured_traffic(dom, traffic_file("pma")),
                 kernel=dom,
                 launch_ms=round(totals[dom] / counts[dom], 4),
                 algorithmic_per_launch={"flops": f_dom, "bytes": b_dom},
@@ -1133,7 +1132,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(f_dom / t_dom / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dom)
+    roof["traffic"] = measured_traffic(dom, traffic_file((args.config, phi)))
     roof["kernel"] = dom
     roof["launch_ms"] = round(per_launch[dom], 4)
     roof["algorithmic_per_launch"] = {"flops": f_dom, "bytes": b_dom}

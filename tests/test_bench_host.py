@@ -43,16 +43,33 @@ def test_pooling_units_count_every_tensor_once():
 
 
 def test_counter_record_tied_to_sources(tmp_path):
-    rec = {"kernels": {"gdpa_bwd": {"bytes_per_launch": 123, "source_sha256": bench.kernel_source_hash("gdpa_bwd")},
-                       "gdpa_fwd": {"bytes_per_launch": 456, "source_sha256": "0" * 64}}}
+    srcs = ["gdpa_bwd_res.hip", "gdpa_sched.hip"]
+    rec = {"kernels": {"gdpa_bwd": {"bytes_per_launch": 123, "sources": srcs, "source_sha256": bench.source_hash(srcs)},
+                       "gdpa_fwd": {"bytes_per_launch": 456, "sources": ["gdpa_fwd_res.hip"], "source_sha256": "0" * 64},
+                       "pma_fwd": {"bytes_per_launch": 789, "source_sha256": bench.source_hash([])}}}
     p = tmp_path / "traffic.json"
     p.write_text(json.dumps(rec))
     assert bench.measured_traffic("gdpa_bwd", str(p)) == 123
     assert bench.measured_traffic("gdpa_fwd", str(p)) is None      # sources changed since
+    assert bench.measured_traffic("pma_fwd", str(p)) is None       # record names no sources
     assert bench.measured_traffic("weightgen_fwd", str(p)) is None  # no reading
     assert bench.measured_traffic("gdpa_bwd", str(tmp_path / "missing.json")) is None
+    assert bench.measured_traffic("gdpa_bwd", None) is None
     # Each call hashes only its own kernels' sources (and the shared headers).
-    assert bench.kernel_source_hash("gdpa_bwd") != bench.kernel_source_hash("pma_bwd")
+    assert bench.source_hash(srcs) != bench.source_hash(["gdpa_pma.hip", "gdpa_sched.hip"])
+
+
+def test_traffic_records_are_per_workload():
+    # A workload without a record of its own never borrows another's reading.
+    assert bench.traffic_file((5, "softmax")) is None
+    assert bench.traffic_file((4, "silu")) is None
+    for key in bench.TRAFFIC_FILES:
+        path = bench.traffic_file(key)
+        assert os.path.exists(path), path
+        with open(path) as f:
+            rec = json.load(f)
+        for stage, k in rec["kernels"].items():
+            assert k["sources"] and k["bytes_per_launch"] > 0, (key, stage)
 
 
 def test_multi_gpu_request_exits_with_message():
