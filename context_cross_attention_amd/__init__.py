@@ -19,7 +19,9 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdpa.so")
+# GDPA_LIB names another build of the same library (e.g. the host-sanitized copy that
+# `python -m context_cross_attention_amd.build --sanitize` writes for CPU-only tests).
+LIB_PATH = os.environ.get("GDPA_LIB") or os.path.join(_HERE, "libgdpa.so")
 
 PHI = {"softmax": 0, "silu": 1, "relu": 2, "gelu": 3, "identity": 4}
 DTYPE = {torch.float32: 0, torch.bfloat16: 1}

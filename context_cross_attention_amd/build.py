@@ -1,9 +1,13 @@
 """Build libgdpa.so (HIP kernels + C ABI) for gfx950, in-tree.
 
-    python -m context_cross_attention_amd.build
+    python -m context_cross_attention_amd.build             # the library
+    python -m context_cross_attention_amd.build --sanitize  # + _build/libgdpa_asan.so
 
 Compiles every source under csrc/ with hipcc into objects under _build/ and
-links them into context_cross_attention_amd/libgdpa.so.
+links them into context_cross_attention_amd/libgdpa.so.  `--sanitize` also builds
+a copy whose host code of the C ABI (gdpa_api.cpp: argument validation, workspace
+planning, the stream cache) carries AddressSanitizer and UndefinedBehaviorSanitizer
+checks, for CPU-only tests of the boundary (the device code is unchanged).
 """
 from __future__ import annotations
 
@@ -65,5 +69,47 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+SAN_LIB = os.path.join(BUILD, "libgdpa_asan.so")
+CLANGXX = os.environ.get("CLANGXX", "/opt/rocm/llvm/bin/clang++")
+# Host-only sanitizer flags: each one is prefixed so that no device code is built with it.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def san_runtime() -> str:
+    """The clang AddressSanitizer runtime that a process loading SAN_LIB must preload."""
+    r = subprocess.run([CLANGXX, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """_build/libgdpa_asan.so: gdpa_api.cpp with host sanitizers, the kernels as built."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        if src == "gdpa_api.cpp":
+            obj = os.path.join(BUILD, "gdpa_api_asan.o")
+            cmd = [HIPCC, "-x", "hip", *CFLAGS, *SAN_HOST, "-g", "-c", os.path.join(CSRC, src), "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed for {src} (sanitized):\n{r.stderr}")
+        elif not os.path.exists(obj):
+            _compile(src)
+        objs.append(obj)
+    # The host link pulls in clang's shared sanitizer runtimes; the objects already hold
+    # their device code.
+    cmd = [CLANGXX, "-shared", "-fPIC", "-shared-libsan", "-fsanitize=address,undefined", "-o", SAN_LIB, *objs,
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     build()
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized()

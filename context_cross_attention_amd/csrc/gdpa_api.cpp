@@ -568,7 +568,7 @@ gdpa_status gdpa_bwd_noalloc(const gdpa_problem* p, const int32_t* offsets, cons
 }
 
 gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv) {
-  if (host_kv_offsets == nullptr || batch < 1 || n_kv < 1) return GDPA_ERR_INVALID_ARGUMENT;
+  if (host_kv_offsets == nullptr || batch < 0 || n_kv < 1) return GDPA_ERR_INVALID_ARGUMENT;
   if (host_kv_offsets[0] != 0) return GDPA_ERR_INVALID_ARGUMENT;
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t rows = (int64_t)host_kv_offsets[b + 1] - host_kv_offsets[b];
@@ -932,7 +932,7 @@ gdpa_status gdpa_pma_bwd(const gdpa_pma_problem* p, const int32_t* offsets, cons
 
 gdpa_status gdpa_check_offsets(const int32_t* host_offsets, int32_t batch, int32_t total_tokens,
                                int32_t max_seqlen) {
-  if (host_offsets == nullptr || batch < 1 || total_tokens < 0 || max_seqlen < 0)
+  if (host_offsets == nullptr || batch < 0 || total_tokens < 0 || max_seqlen < 0)
     return GDPA_ERR_INVALID_ARGUMENT;
   if (host_offsets[0] != 0 || host_offsets[batch] != total_tokens) return GDPA_ERR_INVALID_ARGUMENT;
   for (int32_t b = 0; b < batch; ++b) {

@@ -261,8 +261,9 @@ gdpa_status gdpa_bwd_noalloc(const gdpa_problem* p, const int32_t* offsets, cons
                              const void* v, const void* o, const float* lse, const void* d_o, void* dq,
                              void* dk, void* dv, void* stream);
 
-/* Host-side check of a HOST copy of kv_offsets: kv_offsets[0] = 0 and every
- * sample owns 1 .. n_kv rows; GDPA_OK or GDPA_ERR_INVALID_ARGUMENT. */
+/* Host-side check of a HOST copy of kv_offsets ([batch + 1] int32): kv_offsets[0] = 0
+ * and every sample owns 1 .. n_kv rows (n_kv >= 1, batch >= 0: an empty batch is
+ * {0}); GDPA_OK or GDPA_ERR_INVALID_ARGUMENT. */
 gdpa_status gdpa_check_kv_offsets(const int32_t* host_kv_offsets, int32_t batch, int32_t n_kv);
 
 /* Weight generation (paper summary section 2.1, interaction block; Telegram
@@ -395,9 +396,10 @@ gdpa_status gdpa_pma_bwd(const gdpa_pma_problem* p, const int32_t* offsets, cons
                          const void* d_o, void* d_seeds, void* dk, void* dv, void* workspace,
                          size_t workspace_bytes, void* stream);
 
-/* Host-side check of a HOST copy of offsets: returns GDPA_OK when offsets[0] = 0,
- * the array is non-decreasing, offsets[B] = total_tokens and every length is at
- * most max_seqlen; GDPA_ERR_INVALID_ARGUMENT otherwise. */
+/* Host-side check of a HOST copy of offsets ([batch + 1] int32): returns GDPA_OK when
+ * offsets[0] = 0, the array is non-decreasing, offsets[batch] = total_tokens and every
+ * length is at most max_seqlen (batch, total_tokens, max_seqlen >= 0; an empty batch
+ * is {0} with total_tokens = 0); GDPA_ERR_INVALID_ARGUMENT otherwise. */
 gdpa_status gdpa_check_offsets(const int32_t* host_offsets, int32_t batch, int32_t total_tokens,
                                int32_t max_seqlen);
 

@@ -319,8 +319,9 @@ def gdpa_backward(q, offsets, k, v, do, phi: str = "softmax", scale: Optional[fl
 # ---------------------------------------------------------------------------
 # Stacked residual layers with generated K/V (Telegram review, layer step 1:
 # K and V come from the context features; paper summary section 2.1: the
-# weight-generation module of the interaction block; GDPA "allows stable
-# stacking of the PFFN", read as a plain residual between layers).
+# weight-generation module of the interaction block; section 2.2, GDPA bullet:
+# the personalised FFN becomes stable to stack, read as a plain residual between
+# layers).
 # ---------------------------------------------------------------------------
 
 def weight_generation(ctx, w, n: int, H: int, d: int) -> np.ndarray:

@@ -170,6 +170,8 @@ def test_status_strings_and_offsets_check(lib):
     assert not cca.check_offsets([1, 3, 10], 10, 8)        # does not start at 0
     assert not cca.check_offsets([0, 3, 10], 11, 8)        # wrong total
     assert not cca.check_offsets([0, 3, 10], 10, 6)        # longer than max_seqlen
+    assert cca.check_offsets([0], 0, 0)                    # empty batch
+    assert not cca.check_offsets([0], 1, 0)                # empty batch with tokens
 
 
 def test_group_struct_matches_header(tmp_path):
