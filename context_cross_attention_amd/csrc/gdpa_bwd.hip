@@ -72,10 +72,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_bf16_kernel(const BwdArgs
     b = find_sample(a.chunk_start, a.B, c);
     jc = c - a.chunk_start[b];
   } else {
-    const int rank = item / (H * nch);
-    const int rem = item - rank * H * nch;
-    h = rem / nch;
-    jc = rem - h * nch;
+    // The nch chunks of one (sample, head) read the same Q and dO rows.  Blocks are
+    // dealt to the 8 XCDs round robin, so block 8 s + x runs on XCD x: the chunks
+    // of pair 8 s' + x take slots s = nch s' .. nch s' + nch - 1 of XCD x, and their
+    // Q / dO reads after the first hit that XCD's L2.  Pairs stay in longest-first
+    // order across slots; the grid is padded to whole groups of 8 pairs.
+    const int x = item & 7, slot = item >> 3;
+    const int grp = slot / nch;
+    jc = slot - grp * nch;
+    const int pair = 8 * grp + x;
+    if (pair >= a.B * H) return;
+    const int rank = pair / H;
+    h = pair - rank * H;
     b = a.order[rank];
   }
   const int seq0 = a.offsets[b], L = a.offsets[b + 1] - seq0;
@@ -457,8 +465,9 @@ int bwd_bf16_waves(int d, int n) {
 
 template <int D, int NW>
 static hipError_t bwd_bf16_dw(const BwdArgs& a, int phi, bool with_dq, hipStream_t s) {
-  const long items = (long)a.B * a.H * a.n_chunks;
-  if (items == 0) return hipSuccess;
+  const long pairs = (long)a.B * a.H;
+  if (pairs == 0 || a.n_chunks == 0) return hipSuccess;
+  const long items = (pairs + 7) / 8 * 8 * a.n_chunks;  // whole groups of 8 pairs (see the kernel)
   const dim3 g((unsigned)items), blk(NW * 64);
   const bool biased = a.score_bias != nullptr || a.d_score_bias != nullptr;
   return dispatch_phi(phi, [&](auto P) {

@@ -6,9 +6,12 @@
 // sample's own tokens).  Organisation:
 //   * 8 waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs);
 //     wave w owns context rows 32 w .. 32 w + 31 and keeps their dK, dV fp32
-//     accumulators (32 x 128 each) for the whole sample, with their K and V rows
-//     in registers as MFMA B operands.  Rows past n are zero.
-//   * K^T is resident in LDS ([d][j]) for the dQ product.
+//     accumulators (32 x 128 each) for the whole sample, with their V rows in
+//     registers as MFMA B operands.  Rows past n are zero.
+//   * K^T is resident in LDS ([d][j]): 16-byte reads give the A operand of the dQ
+//     product, and transpose reads (ds_read_b64_tr_b16) the K rows that S = Q K^T
+//     takes as B operand, which leaves the registers K would hold free for reading
+//     every MFMA's LDS operands one step ahead.
 //   * Q and dO (and, for softmax, the row LSE and rowsum(dO O)) of each 32-row
 //     query step reach LDS by asynchronous global->LDS copies issued by waves
 //     4..7 two steps ahead into a 3-slot ring: no registers hold staged data and
@@ -21,7 +24,10 @@
 //     row), for the next step while waves 0..3 compute dQ: it waits only for its
 //     own copies, and the transposition costs the step no barrier.  The transposed
 //     tiles are built with transpose reads (ds_read_b64_tr_b16) and 16-byte
-//     writes.  Every MFMA operand read is a 16-byte, bank-conflict-free LDS read.
+//     writes.  Every MFMA operand read is bank-conflict free, and each product's
+//     loop reads the operands of its next k-step before issuing the current
+//     MFMAs (with scheduling fences: left alone, the compiler sinks every read next
+//     to its MFMA and each MFMA then waits out a whole LDS round trip).
 //   * Waves 0..3 then compute dQ^T for head columns 32 w .. 32 w + 31 over all
 //     context rows (dQ^T = K^T dS^T), whose C tile (rows permuted) gives each lane
 //     16 consecutive columns of one token: 16-byte stores, residual added in fp32.
@@ -45,12 +51,16 @@ __device__ __forceinline__ int tok_pos(int t) { return (t & ~12) | ((t & 4) << 1
 // dQ^T = K^T dS^T: the A operand's row i = 8 a + 4 b + c of each 32-column block is
 // head column kt_row(i) = 16 b + 4 a + c, so that C-tile lane group g holds the 16
 // consecutive columns 16 g .. 16 g + 15 in register order (two 16-byte stores).
-// K^T rows are 528 bytes apart, so row d starts at bank group d % 16 (16-byte groups of
-// the 64 4-byte banks); the 16-byte chunk q of row d is stored at chunk
-// q ^ (8 (d / 16 % 2)) so that the rows {0..3, 16..19, 4..7, 20..23} + 8 k read by one
-// 16-lane phase of a ds_read_b128 fall in distinct bank groups.
+// K^T rows are 576 bytes apart (64 mod 256: four consecutive rows occupy the four 64-byte
+// quarters of the 256-byte bank period) and the 16-byte chunk q of row d is stored at
+// chunk q ^ kt_x(d), kt_x(d) = (d / 4) % 2 + 2 ((d / 16) % 2).  Then (a) the rows
+// {0..3, 16..19, 4..7, 20..23} + 8 k read at one chunk by a 16-lane phase of a ds_read_b128
+// (the dQ product's A operand) hit 16 distinct 16-byte bank groups, and (b) a transpose
+// read of four consecutive rows d .. d + 3 (d % 4 = 0) by 32 lanes, 64 bytes of one
+// aligned 4-chunk block each (the K operand of S), covers all 256 bytes of the period.
 __device__ __forceinline__ int kt_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
-__device__ __forceinline__ int kt_col(int j, int d) { return 8 * ((j >> 3) ^ (((d >> 4) & 1) << 3)) + (j & 7); }
+__device__ __forceinline__ int kt_x(int d) { return ((d >> 2) & 1) | (((d >> 4) & 1) << 1); }
+__device__ __forceinline__ int kt_col(int j, int d) { return 8 * ((j >> 3) ^ kt_x(d)) + (j & 7); }
 
 __device__ __forceinline__ uint16_t half_of(const u32x4& v, int i) {
   return (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
@@ -65,7 +75,8 @@ template <int PHI, int DQB>
 __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   constexpr int D = 128, NT = 512, NJ = 256, BQ = 32, KS = D / 16, DT = D / 32;
   constexpr int LDT = BQ + 8;   // Qt, dOt rows (20 dwords: likewise)
-  constexpr int LDJ = NJ + 8;   // Kt and dS rows (132 dwords)
+  constexpr int LDJ = NJ + 32;  // Kt rows (144 dwords)
+  constexpr int LDS_ = NJ + 8;  // dS rows (132 dwords: 16 consecutive rows, distinct bank groups)
   constexpr int LDE = D;        // bf16 dK / dV rows in the epilogue
   // Ring slot: Q tile and dO tile (bf16, each 4 blocks of 32 rows x 64 bytes: block G
   // holds head columns 32 G .. 32 G + 31 of every token, the 16-byte chunk q of row t at
@@ -78,7 +89,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   __shared__ __align__(16) uint16_t QdT[2 * D * LDT];  // Q^T then dO^T (one base address)
   uint16_t* const Qt = QdT;
   uint16_t* const dOt = QdT + D * LDT;
-  __shared__ __align__(16) uint16_t dSs[BQ * LDJ];
+  __shared__ __align__(16) uint16_t dSs[BQ * LDS_];
   static_assert(8 * 32 * LDE <= D * LDJ, "epilogue tiles must fit in Kt");
 
   const int H = a.H;
@@ -100,7 +111,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   // K and V rows of this wave as B operands (lane (j + 32 g), items d = 16 ks + 8 g + i),
   // zero past n; K^T written into LDS from the same registers (32 consecutive j per
   // half-wave: each 2-byte write instruction covers two contiguous 64-byte runs).
-  bf16x8 kf[KS], vf[KS];
+  bf16x8 vf[KS];
   {
     const size_t row = (crow0 + min(j, n - 1)) * rs + (size_t)h * D + 8 * g;
     u32x4 kr[KS], vr[KS];
@@ -115,7 +126,6 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
         kr[ks] = u32x4{};
         vr[ks] = u32x4{};
       }
-      kf[ks] = as_bf16x8(kr[ks]);
       vf[ks] = as_bf16x8(vr[ks]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -222,11 +232,35 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
     // k-step ks reads chunk (2 ks + g) % 4 of block ks / 2: two base offsets (even and
     // odd ks) plus immediates.
     const int oe = slot_off(lx, gx), oo = slot_off(lx, gx + 2);
+    // K operand of S (lane (j + 32 g): K[j][16 ks + 8 g + i]) by two transpose reads of
+    // K^T: lane 4 r + c of 16-lane group G addresses row 16 ks + 8 (G / 2) + 4 hh + r,
+    // columns 32 w + 16 (G % 2) + 4 c .. + 3 (chunk q = 4 w + 2 (G % 2) + c / 2 at
+    // q ^ kt_x(row), kt_x(row) = hh + 2 (ks % 2)).
+    const int tu = lx & 15, tG = (lx + 32 * gx) >> 4;
+    const int kq = 4 * wave + 2 * (tG & 1) + ((tu & 3) >> 1);
+    const int tbase = (8 * (tG >> 1) + (tu >> 2)) * LDJ + 4 * (tu & 1) + 8 * (kq & ~3);
+    auto kop = [&](int ks) {
+      bf16x4 lo4 = lds_read_tr4(&Kt[tbase + 16 * ks * LDJ + 8 * ((kq & 3) ^ (2 * (ks & 1)))]);
+      bf16x4 hi4 = lds_read_tr4(&Kt[tbase + (16 * ks + 4) * LDJ + 8 * ((kq & 3) ^ (1 + 2 * (ks & 1)))]);
+      return cat8(lo4, hi4);
+    };
+    // Operands of k-step ks + 1 are read while the MFMAs of ks run (scheduling fences
+    // keep the compiler from sinking the reads next to their MFMAs).
+    bf16x8 qo[2], doo[2], ko[2];
+    auto sdp_load = [&](int ks, int bsel) {
+      const int o = (ks >> 1) * 1024 + ((ks & 1) ? oo : oe);
+      qo[bsel] = lds_read8(&Qs[o]);
+      doo[bsel] = lds_read8(&dOs[o]);
+      ko[bsel] = kop(ks);
+    };
+    sdp_load(0, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int o = (ks >> 1) * 1024 + ((ks & 1) ? oo : oe);
-      S = mfma32(lds_read8(&Qs[o]), kf[ks], S);
-      dP = mfma32(lds_read8(&dOs[o]), vf[ks], dP);
+      if (ks + 1 < KS) sdp_load(ks + 1, (ks + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      S = mfma32(qo[ks & 1], ko[ks & 1], S);
+      dP = mfma32(doo[ks & 1], vf[ks], dP);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // Lane (j + 32 g), register r: token t = 8 (r / 4) + 4 g + r % 4.  S becomes P
     // and dP becomes dS / scale.
@@ -276,17 +310,26 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       const u32x4 sw = __builtin_bit_cast(u32x4, sa[kk]);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        dSs[(16 * kk + 8 * (i >> 2) + 4 * g + (i & 3)) * LDJ + j] = half_of(sw, i);
+        dSs[(16 * kk + 8 * (i >> 2) + 4 * g + (i & 3)) * LDS_ + j] = half_of(sw, i);
     }
-    // dV += P^T dO, dK += dS^T Q over the 32 tokens.
+    // dV += P^T dO, dK += dS^T Q over the 32 tokens (operands one step ahead).
+    bf16x8 bo[2], bq[2];
+    auto dvdk_load = [&](int st, int bsel) {
+      const int kk = st / DT, dt = st % DT;
+      const int o = (32 * dt + lr) * LDT + 16 * kk + 8 * g;
+      bo[bsel] = lds_read8(&dOt[o]);
+      bq[bsel] = lds_read8(&Qt[o]);
+    };
+    dvdk_load(0, 0);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int o = (32 * dt + lr) * LDT + 16 * kk + 8 * g;
-        dV[dt] = mfma32(pa[kk], lds_read8(&dOt[o]), dV[dt]);
-        dK[dt] = mfma32(sa[kk], lds_read8(&Qt[o]), dK[dt]);
-      }
+    for (int st = 0; st < 2 * DT; ++st) {
+      if (st + 1 < 2 * DT) dvdk_load(st + 1, (st + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kk = st / DT, dt = st % DT;
+      dV[dt] = mfma32(pa[kk], bo[st & 1], dV[dt]);
+      dK[dt] = mfma32(sa[kk], bq[st & 1], dK[dt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     __syncthreads();  // dS complete; Qt and dOt are free
 
     if (wave >= 4 && s + 1 < nsteps) {
@@ -302,12 +345,25 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       // immediate offsets cover all k-steps.
       const int lxd = opaque(lr);
       const int kr = 32 * wave + kt_row(lxd);
-      const int sw = ((kr >> 4) & 1) * 64;
-      const int oa_p = kr * LDJ + 8 * g + sw, oa_m = kr * LDJ + 8 * g - sw;
-      const int ob = lxd * LDJ + 8 * g;
+      // Chunk 2 ks + g of row kr sits at (2 ks + g) ^ kt_x(kr) = 2 (ks ^ x1) + (g ^ x0):
+      // +-16 halves (sign from ks % 2) on rows with x1 = 1, so two base addresses plus
+      // immediate offsets cover all k-steps.
+      const int x0 = kt_x(kr) & 1, sw = (kt_x(kr) >> 1) * 16;
+      const int oa_p = kr * LDJ + 8 * (g ^ x0) + sw, oa_m = kr * LDJ + 8 * (g ^ x0) - sw;
+      const int ob = lxd * LDS_ + 8 * g;
+      bf16x8 ka[2], sb[2];
+      auto dq_load = [&](int ks, int bsel) {
+        ka[bsel] = lds_read8(&Kt[(ks & 1 ? oa_m : oa_p) + 16 * ks]);
+        sb[bsel] = lds_read8(&dSs[ob + 16 * ks]);
+      };
+      dq_load(0, 0);
 #pragma unroll
-      for (int ks = 0; ks < NJ / 16; ++ks)
-        dq = mfma32(lds_read8(&Kt[((ks >> 2) & 1 ? oa_m : oa_p) + 16 * ks]), lds_read8(&dSs[ob + 16 * ks]), dq);
+      for (int ks = 0; ks < NJ / 16; ++ks) {
+        if (ks + 1 < NJ / 16) dq_load(ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dq = mfma32(ka[ks & 1], sb[ks & 1], dq);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // Lane (t + 32 g), register r: column 32 w + 16 g + r of token t = lr.
       if (lr < rows) {
         uint16_t* dst = (uint16_t*)a.dq + (size_t)(seq0 + tq + lr) * rs + (size_t)h * D + 32 * wave + 16 * g;

@@ -219,16 +219,12 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
       if (jt + 2 < ntile) scores(32 * (jt + 2), Sa);
       mix(32 * (jt + 1), Sb);
     }
-    if (PHI == kPhiSilu) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[dt] *= -kLn2;
-    }
-
+    // The output is O times a per-row factor (SiLU: the constant -ln 2; softmax: 1 / the
+    // row sum), applied in the epilogue together with the residual (one FMA per item).
+    float oscale = PHI == kPhiSilu ? -kLn2 : 1.0f;
     if (PHI == 0) {
       const float l_tot = l_run + wave_xor32(l_run);
-      const float inv = 1.0f / l_tot;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[dt] *= inv;
+      oscale = 1.0f / l_tot;
       if (tvalid && g == 0 && a.lse != nullptr)
         a.lse[(size_t)(seq0 + t) * H + h] = (m_run + __log2f(l_tot)) * kLn2;
     }
@@ -240,32 +236,35 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           float v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = O[dt][8 * hh + e];
           if (RESID == 1) {
             // Residual is Q itself: the same columns are items of the Q operand.
             const bf16x8 qv = qc[2 * dt + hh];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] += (float)qv[e];
-          } else if (RESID == 4) {
+            for (int e = 0; e < 8; ++e) v[e] = fmaf(O[dt][8 * hh + e], oscale, (float)qv[e]);
+          } else if (RESID == 2) {
+            const u32x4 rr = gload16((const uint16_t*)a.residual + obase + 32 * dt + 8 * hh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              v[e] = fmaf(O[dt][8 * hh + e], oscale, bf2f((uint16_t)(rr[e >> 1] >> (16 * (e & 1)))));
+          } else if (RESID == 3 && a.out_bias != nullptr) {
+            const float* bp = a.out_bias + ((size_t)b * H + h) * D + 32 * dt + 16 * g + 8 * hh;
+            const f32x4 b0 = *(const f32x4*)bp, b1 = *(const f32x4*)(bp + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = fmaf(O[dt][8 * hh + e], oscale, b0[e]);
+              v[4 + e] = fmaf(O[dt][8 * hh + 4 + e], oscale, b1[e]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = O[dt][8 * hh + e] * oscale;
+          }
+          if (RESID == 4) {
             const bf16x8 qv = qc[2 * dt + hh];
             float y[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] = v[e] + (float)qv[e];
             *(bf16x8*)((uint16_t*)a.o_plus_q + obase + 32 * dt + 8 * hh) =
                 pack8(y[0], y[1], y[2], y[3], y[4], y[5], y[6], y[7]);
-          } else if (RESID == 2) {
-            const u32x4 rr = gload16((const uint16_t*)a.residual + obase + 32 * dt + 8 * hh);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] += bf2f((uint16_t)(rr[e >> 1] >> (16 * (e & 1))));
-          } else if (RESID == 3 && a.out_bias != nullptr) {
-            const float* bp = a.out_bias + ((size_t)b * H + h) * D + 32 * dt + 16 * g + 8 * hh;
-            const f32x4 b0 = *(const f32x4*)bp, b1 = *(const f32x4*)(bp + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              v[e] += b0[e];
-              v[4 + e] += b1[e];
-            }
           }
           *(bf16x8*)(op + 32 * dt + 8 * hh) = pack8(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
         }
