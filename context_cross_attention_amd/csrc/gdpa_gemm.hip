@@ -145,10 +145,14 @@ __global__ __launch_bounds__(NT_T, 1) void gemm_nt_kernel(int M, long N, int K,
 #pragma unroll
     for (int kk = 0; kk < NT_K / 16; ++kk) {
       if (kk + 1 < NT_K / 16) load(kk + 1, x[(kk + 1) & 1], y[(kk + 1) & 1]);
+      // Fences keep the next sub-step's reads ahead of these MFMAs (left alone, the
+      // compiler sinks each read next to its first use).
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(x[kk & 1][j], y[kk & 1][i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     stored_last = kx == nk - 1;
@@ -303,18 +307,25 @@ __global__ __launch_bounds__(TN_T, 1) void gemm_tn_kernel(int M, long N, int K,
       }
       return v;
     };
+    bf16x8 x[2][2], y[2][4];
+    auto load = [&](int kk, bf16x8* xs, bf16x8* ys) {
+      const int kb = 16 * kk + 8 * gx;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) xs[j] = cat8(trd(Bs, kb, wn + 32 * j), trd(Bs, kb + 4, wn + 32 * j));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ys[i] = cat8(trd(As, kb, wm + 32 * i), trd(As, kb + 4, wm + 32 * i));
+    };
+    // Operands of sub-step kk + 1 are read while the MFMAs of kk run (fences as above).
+    load(0, x[0], y[0]);
 #pragma unroll
     for (int kk = 0; kk < TN_K / 16; ++kk) {
-      const int kb = 16 * kk + 8 * gx;
-      bf16x8 x[2], y[4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) x[j] = cat8(trd(Bs, kb, wn + 32 * j), trd(Bs, kb + 4, wn + 32 * j));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = cat8(trd(As, kb, wm + 32 * i), trd(As, kb + 4, wm + 32 * i));
+      if (kk + 1 < TN_K / 16) load(kk + 1, x[(kk + 1) & 1], y[(kk + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(x[j], y[i], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(x[kk & 1][j], y[kk & 1][i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     stored_last = kx == nk - 1;
