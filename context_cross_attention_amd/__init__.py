@@ -256,6 +256,15 @@ def fwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     return out, lse
 
 
+def bwd_reads_o(dtype, head_dim: int, n_kv: int) -> bool:
+    """Whether the softmax backward reads the forward's output O for its row term.
+
+    The backward that holds a sample's whole context in one work-group (bf16,
+    head_dim 128, n_kv <= 256) sums the row term from P and dP itself and reads no O
+    (the rule of gdpa_bwd in include/gdpa.h)."""
+    return not (dtype == torch.bfloat16 and head_dim == 128 and n_kv <= 256)
+
+
 def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         o: Optional[torch.Tensor], lse: Optional[torch.Tensor], do: torch.Tensor,
         phi: str = "softmax", scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
@@ -263,7 +272,8 @@ def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """GDPA backward of sum(O * dO).  Returns (dq, dk, dv).
 
-    For softmax, o and lse are the forward's outputs; for the elementwise maps they are unused.
+    For softmax, o and lse are the forward's outputs (o may be None where
+    bwd_reads_o() is False); for the elementwise maps they are unused.
     With accumulate_dq, dq (which may be `do` itself) receives dq + dQ.
     With residual, dq receives do + dQ: the gradient of O = Q + GDPA(Q).
     """
@@ -277,7 +287,8 @@ def bwd(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         _require(t, name, (B, n, H, d), q.dtype, dev)
     _require(offsets, "offsets", (B + 1,), torch.int32, dev)
     if phi == "softmax":
-        _require(o, "o", (T, H, d), q.dtype, dev)
+        if o is not None or bwd_reads_o(q.dtype, d, n):
+            _require(o, "o", (T, H, d), q.dtype, dev)
         _require(lse, "lse", (T, H), torch.float32, dev)
     else:
         o, lse = None, None
@@ -352,7 +363,8 @@ def bwd_noalloc(q: torch.Tensor, offsets: torch.Tensor, k: torch.Tensor, v: torc
         _require(t, name, (B, n, H, d), q.dtype, dev)
     _require(offsets, "offsets", (B + 1,), torch.int32, dev)
     if phi == "softmax":
-        _require(o, "o", (T, H, d), q.dtype, dev)
+        if o is not None or bwd_reads_o(q.dtype, d, n):
+            _require(o, "o", (T, H, d), q.dtype, dev)
         _require(lse, "lse", (T, H), torch.float32, dev)
     else:
         o, lse = None, None

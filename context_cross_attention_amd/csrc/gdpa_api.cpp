@@ -50,7 +50,8 @@ gdpa_status check_problem(const gdpa_problem* p) {
 
 // Workspace layouts (each region 256-byte aligned).
 //   forward : tile_start [B+1] int32 (streaming kernel) | order [B] int32 (resident kernel)
-//   backward: order [B] int32 | dvec [T*H] fp32 (softmax) | tile_start [B+1] int32 (bf16,
+//   backward: order [B] int32 | dvec [T*H] fp32 (softmax, except in the one-work-group
+//             backward, which sums the row term itself) | tile_start [B+1] int32 (bf16,
 //             when the context rows span several work-groups: dQ per query tile)
 struct BwdPlan {
   int waves = 0, chunks = 0;
@@ -58,10 +59,16 @@ struct BwdPlan {
   bool split_dq = false;  // several key chunks per (sample, head): dQ from the query-tile kernel
 };
 
+// The one-work-group-per-(sample, head) backward (bf16, d = 128, n <= 256): it sums the
+// softmax row term from P and dP itself, so it needs neither O nor the row-dot pass.
+bool bwd_one_wg(const gdpa_problem* p) {
+  return p->dtype == GDPA_BF16 && gdpa::bwd_res_supported(p->head_dim, p->n_kv);
+}
+
 BwdPlan bwd_plan(const gdpa_problem* p) {
   BwdPlan pl;
   const size_t TH = (size_t)p->total_tokens * p->heads;
-  if (p->dtype == GDPA_BF16 && gdpa::bwd_res_supported(p->head_dim, p->n_kv)) {
+  if (bwd_one_wg(p)) {
     pl.waves = 4;
     pl.chunks = 1;
   } else if (p->dtype == GDPA_BF16) {
@@ -74,7 +81,7 @@ BwdPlan bwd_plan(const gdpa_problem* p) {
   pl.order_off = off;
   off += align_up(sizeof(int32_t) * (size_t)p->batch);
   pl.dvec_off = off;
-  if (p->phi == GDPA_PHI_SOFTMAX) off += align_up(sizeof(float) * TH);
+  if (p->phi == GDPA_PHI_SOFTMAX && !bwd_one_wg(p)) off += align_up(sizeof(float) * TH);
   pl.tile_off = off;
   if (pl.split_dq) off += align_up(sizeof(int32_t) * ((size_t)p->batch + 1));
   pl.total = off;
@@ -98,7 +105,7 @@ struct RecomputePlan {
 RecomputePlan recompute_plan(const gdpa_problem* p, size_t base, bool out_bias) {
   RecomputePlan r;
   r.total = base;
-  r.on = out_bias && p->dtype == GDPA_BF16 && p->phi == GDPA_PHI_SOFTMAX;
+  r.on = out_bias && p->dtype == GDPA_BF16 && p->phi == GDPA_PHI_SOFTMAX && !bwd_one_wg(p);
   if (!r.on) return r;
   const size_t TH = (size_t)p->total_tokens * p->heads;
   r.fwd_off = base;
@@ -195,7 +202,8 @@ gdpa_status bwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
   if (p->total_tokens > 0 && (q == nullptr || d_o == nullptr || dq == nullptr))
     return GDPA_ERR_INVALID_ARGUMENT;
   const bool softmax = p->phi == GDPA_PHI_SOFTMAX;
-  if (softmax && p->total_tokens > 0 && (o == nullptr || lse == nullptr))
+  const bool one_wg = bwd_one_wg(p);  // then O is not read
+  if (softmax && p->total_tokens > 0 && (lse == nullptr || (o == nullptr && !one_wg)))
     return GDPA_ERR_INVALID_ARGUMENT;
   if (p->flags & GDPA_FWD_RESIDUAL) return GDPA_ERR_INVALID_ARGUMENT;
   const bool accum = (p->flags & GDPA_BWD_ACCUM_DQ) != 0;
@@ -218,7 +226,7 @@ gdpa_status bwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
   a.v = v;
   a.d_o = d_o;
   a.lse = lse;
-  a.dvec = softmax ? (const float*)(ws + pl.dvec_off) : nullptr;
+  a.dvec = softmax && !one_wg ? (const float*)(ws + pl.dvec_off) : nullptr;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -246,7 +254,7 @@ gdpa_status bwd_impl(const gdpa_problem* p, const int32_t* offsets, const int32_
     e = gdpa::launch_softmax_dvec(ws + rp.o_off, d_o, (int)TH, p->head_dim, true, (float*)(ws + pl.dvec_off),
                                   s);
     if (e != hipSuccess) return hip_status(e);
-  } else if (softmax && TH > 0) {
+  } else if (softmax && TH > 0 && !one_wg) {
     e = gdpa::launch_softmax_dvec(o, d_o, (int)TH, p->head_dim, p->dtype == GDPA_BF16,
                                   (float*)(ws + pl.dvec_off), s, offsets, p->batch, p->heads, out_bias);
     if (e != hipSuccess) return hip_status(e);

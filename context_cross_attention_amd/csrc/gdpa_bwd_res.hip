@@ -12,7 +12,7 @@
 //     product, and transpose reads (ds_read_b64_tr_b16) the K rows that S = Q K^T
 //     takes as B operand, which leaves the registers K would hold free for reading
 //     every MFMA's LDS operands one step ahead.
-//   * Q and dO (and, for softmax, the row LSE and rowsum(dO O)) of each 32-row
+//   * Q and dO (and, for softmax, the row LSE) of each 32-row
 //     query step reach LDS by asynchronous global->LDS copies issued by waves
 //     4..7 two steps ahead into a 3-slot ring: no registers hold staged data and
 //     HBM latency is covered by two steps of compute.  Each copying wave brings in
@@ -31,6 +31,11 @@
 //   * Waves 0..3 then compute dQ^T for head columns 32 w .. 32 w + 31 over all
 //     context rows (dQ^T = K^T dS^T), whose C tile (rows permuted) gives each lane
 //     16 consecutive columns of one token: 16-byte stores, residual added in fp32.
+//   * Softmax: the row term D_t = rowsum(dO O) of dS = P (dP - D) equals
+//     sum_j P_tj dP_tj, and every context row of the sample is in this work-group, so
+//     it is summed here from P and dP (a cross-lane reduction per wave, then the eight
+//     waves' parts through LDS, with dV's products issued before the barrier that
+//     joins them) instead of by a pass over O and dO: the backward reads no O.
 //   * The score scale is applied once, to dQ per step and to dK at the end.
 //   * Global addresses are clamped into the sample (copies past its last step
 //     re-read valid rows into the free slot, which keeps every wave's count of
@@ -67,6 +72,34 @@ __device__ __forceinline__ uint16_t half_of(const u32x4& v, int i) {
 }
 __device__ __forceinline__ float lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Sum of v[i] over the 32 lanes of each half-wave (lanes 32 g .. 32 g + 31), for all 16
+// i at once: each level pairs lanes, and each lane keeps the half of its values that it
+// shares with its partner's kept half, so one lane per pair of lanes ends with one sum.
+// Levels: rows of 16 lanes 0 <-> 1 and 2 <-> 3 (v_permlane16_swap: lanes of the even row
+// keep i < 8), then lane ^ 8 (DPP row_ror:8), i <-> 7 - i within 8 lanes (row_half_mirror),
+// lane ^ 2, lane ^ 1 (quad permutations).  Lane l returns the sum of v[(l / 2) % 16].
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float half_sum16(const float (&v)[16], int lane) {
+  float a[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[q]), __float_as_uint(v[q + 8]), false, false);
+    a[q] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  float c[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) c[q] = (b3 ? a[q + 4] : a[q]) + dpp_f<0x128>(b3 ? a[q] : a[q + 4]);
+  float d[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) d[q] = (b2 ? c[q + 2] : c[q]) + dpp_f<0x141>(b2 ? c[q] : c[q + 2]);
+  const float e = (b1 ? d[1] : d[0]) + dpp_f<0x4E>(b1 ? d[0] : d[1]);
+  return e + dpp_f<0xB1>(e);
+}
 }  // namespace
 
 // DQB: 0 dQ = result, 1 dQ = dO + result (dO from LDS), 2 dQ = dQ + result,
@@ -80,7 +113,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   constexpr int LDE = D;        // bf16 dK / dV rows in the epilogue
   // Ring slot: Q tile and dO tile (bf16, each 4 blocks of 32 rows x 64 bytes: block G
   // holds head columns 32 G .. 32 G + 31 of every token, the 16-byte chunk q of row t at
-  // position q ^ ((t / 4) % 4)), then LSE[32] and rowsum(dO O)[32] (fp32, softmax only).
+  // position q ^ ((t / 4) % 4)), then LSE[32] (fp32, softmax only) and 128 unused bytes.
   constexpr int NSLOT = 3, TILE_B = BQ * D * 2, SLOT_B = 2 * TILE_B + 2 * BQ * 4;
   constexpr int DMA_OPS = PHI == 0 ? 5 : 4;  // copies per step issued by each of waves 4..7
   static_assert(BQ * D / 8 == NT, "one 16-byte chunk per thread and tensor");
@@ -90,6 +123,10 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   uint16_t* const Qt = QdT;
   uint16_t* const dOt = QdT + D * LDT;
   __shared__ __align__(16) uint16_t dSs[BQ * LDS_];
+  // Softmax row term of each step's 32 tokens: per-wave partial sums [token][wave], and
+  // each wave's own copy of the totals [wave][token].
+  __shared__ __align__(16) float Dpart[PHI == 0 ? BQ * 8 : 4];
+  __shared__ __align__(16) float Dw[PHI == 0 ? 8 * BQ : 4];
   static_assert(8 * 32 * LDE <= D * LDJ, "epilogue tiles must fit in Kt");
 
   const int H = a.H;
@@ -160,10 +197,10 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       dma16(__builtin_amdgcn_readfirstlane(sb + 1024 * k), (const uint16_t*)a.q + off);
       dma16(__builtin_amdgcn_readfirstlane(sb + TILE_B + 1024 * k), (const uint16_t*)a.d_o + off);
     }
-    if (PHI == 0) {  // lanes 0..31: LSE of rows 0..31; lanes 32..63: rowsum(dO O) (every copying wave)
+    if (PHI == 0) {  // LSE of rows 0..31 (lanes 32..63 repeat it into the unused second half)
       const size_t r = (size_t)(seq0 + min(tq + lr, L - 1)) * H + h;
       dma4(__builtin_amdgcn_readfirstlane(lds_addr(ring) + (uint32_t)((st % NSLOT) * SLOT_B + 2 * TILE_B)),
-           g == 0 ? (const void*)(a.lse + r) : (const void*)(a.dvec + r));
+           (const void*)(a.lse + r));
     }
   };
 
@@ -220,7 +257,6 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
     const uint16_t* Qs = (const uint16_t*)slot;
     const uint16_t* dOs = (const uint16_t*)(slot + TILE_B);
     const float* lse_s = (const float*)(slot + 2 * TILE_B);
-    const float* dvec_s = lse_s + BQ;
     const int lx = opaque(lr), gx = opaque(g);
     // Step s's slot landed (waited for by waves 4..7 before they built Qt / dOt for it)
     // and Qt / dOt hold step s; step s - 1 is finished with dSs and its slot.
@@ -264,19 +300,57 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
     }
     // Lane (j + 32 g), register r: token t = 8 (r / 4) + 4 g + r % 4.  S becomes P
     // and dP becomes dS / scale.
+    bf16x8 pa[2], sa[2];
     if (PHI == 0) {
+      // P from the row LSE, and this wave's part of the row term D_t = sum_j P_tj dP_tj
+      // (= rowsum(dO O)), summed over its 32 context rows: lane (2 i + 32 g + e), e < 2,
+      // ends up with register i's sum (token 8 (i / 4) + 4 g + i % 4).
+      float R[16];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 ls = *(const GDPA_LDS f32x4*)&lse_s[8 * q4 + 4 * g];
-        const f32x4 dvv = *(const GDPA_LDS f32x4*)&dvec_s[8 * q4 + 4 * g];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * q4 + c;
           float p = fast_exp2(fmaf(S[r], sl2, DQB == 3 ? fmaf(-ls[c], kLog2e, sbj2) : -ls[c] * kLog2e));
           if (!jvalid) p = 0.f;
           S[r] = p;
-          dP[r] = p * (dP[r] - dvv[c]);
+          R[r] = p * dP[r];
         }
+      }
+      const int ln = opaque(lane), ri = (ln >> 1) & 15;
+      const float part = half_sum16(R, ln);
+      if ((ln & 1) == 0) Dpart[(8 * (ri >> 2) + 4 * (ln >> 5) + (ri & 3)) * 8 + wave] = part;
+      // dV needs only P: its products run while the other waves finish their parts.
+      pa[0] = pack_c8(S, 0);
+      pa[1] = pack_c8(S, 1);
+      bf16x8 bo[2];
+      auto dv_load = [&](int st, int bsel) {
+        const int kk = st / DT, dt = st % DT;
+        bo[bsel] = lds_read8(&dOt[(32 * dt + lr) * LDT + 16 * kk + 8 * g]);
+      };
+      dv_load(0, 0);
+#pragma unroll
+      for (int st = 0; st < 2 * DT; ++st) {
+        if (st + 1 < 2 * DT) dv_load(st + 1, (st + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dV[st % DT] = mfma32(pa[st / DT], bo[st & 1], dV[st % DT]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __syncthreads();  // every wave's part of the row term is in Dpart
+      // Each wave totals the 8 parts of the 32 tokens (lanes 0..31, one token each) into
+      // its own row of Dw, then reads back the totals of its registers' tokens.
+      if (ln < 32) {
+        const f32x4 p0 = *(const GDPA_LDS f32x4*)&Dpart[ln * 8];
+        const f32x4 p1 = *(const GDPA_LDS f32x4*)&Dpart[ln * 8 + 4];
+        Dw[wave * BQ + ln] = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
+      }
+      asm volatile("" ::: "memory");  // the reads below follow this wave's writes
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 dvv = *(const GDPA_LDS f32x4*)&Dw[wave * BQ + 8 * q4 + 4 * g];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dP[4 * q4 + c] = S[4 * q4 + c] * (dP[4 * q4 + c] - dvv[c]);
       }
     } else if (PHI == kPhiSilu) {
 #pragma unroll
@@ -300,10 +374,9 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       for (int r = 0; r < 16; ++r)
         if (8 * (r >> 2) + 4 * g + (r & 3) < rows) dsb += dP[r];
     }
-    bf16x8 pa[2], sa[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      pa[kk] = pack_c8(S, kk);
+      if (PHI != 0) pa[kk] = pack_c8(S, kk);
       sa[kk] = pack_c8(dP, kk);
       // dS row-major for the dQ product: item i of k-step kk is token
       // 16 kk + 8 (i / 4) + 4 g + i % 4.
@@ -312,12 +385,13 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       for (int i = 0; i < 8; ++i)
         dSs[(16 * kk + 8 * (i >> 2) + 4 * g + (i & 3)) * LDS_ + j] = half_of(sw, i);
     }
-    // dV += P^T dO, dK += dS^T Q over the 32 tokens (operands one step ahead).
+    // dV += P^T dO (softmax: done above), dK += dS^T Q over the 32 tokens (operands one
+    // step ahead).
     bf16x8 bo[2], bq[2];
     auto dvdk_load = [&](int st, int bsel) {
       const int kk = st / DT, dt = st % DT;
       const int o = (32 * dt + lr) * LDT + 16 * kk + 8 * g;
-      bo[bsel] = lds_read8(&dOt[o]);
+      if (PHI != 0) bo[bsel] = lds_read8(&dOt[o]);
       bq[bsel] = lds_read8(&Qt[o]);
     };
     dvdk_load(0, 0);
@@ -326,7 +400,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       if (st + 1 < 2 * DT) dvdk_load(st + 1, (st + 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
       const int kk = st / DT, dt = st % DT;
-      dV[dt] = mfma32(pa[kk], bo[st & 1], dV[dt]);
+      if (PHI != 0) dV[dt] = mfma32(pa[kk], bo[st & 1], dV[dt]);
       dK[dt] = mfma32(sa[kk], bq[st & 1], dK[dt]);
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -11,9 +11,10 @@ Backward of sum(X_L * G):
     dX_l = dX_{l+1} + dQ_l,   dW_K^l = dK_l^T C,   dW_V^l = dV_l^T C.
 
 All buffers are allocated once; a step only sequences library calls on the
-current stream.  With the row softmax the backward's row term needs each layer's
-un-summed output O_l and its LSE: the forward keeps them (gdpa_fwd_block writes O_l
-and X_l + O_l in one pass); the elementwise maps need neither.
+current stream.  With the row softmax the backward needs each layer's LSE; where it
+also reads the un-summed output O_l for its row term (shapes outside the
+one-work-group backward, see bwd_reads_o) the forward keeps O_l too (gdpa_fwd_block
+writes O_l and X_l + O_l in one pass).  The elementwise maps need neither.
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ from typing import Callable, List, Optional
 
 import torch
 
-from . import bwd, fwd, fwd_block, make_problem, weightgen_bwd_w, weightgen_fwd, workspace_bytes
+from . import bwd, bwd_reads_o, fwd, fwd_block, make_problem, weightgen_bwd_w, weightgen_fwd, workspace_bytes
 
 
 class StackedGdpa:
@@ -48,8 +49,9 @@ class StackedGdpa:
         self.dw_k = [torch.empty_like(w) for w in w_k]
         self.dw_v = [torch.empty_like(w) for w in w_v]
         softmax = phi == "softmax"
-        # softmax: each layer's GDPA output and LSE, kept for the backward's row term.
-        self.o = [torch.empty((T, H, d), dtype=bf, device=dev) for _ in range(self.L)] if softmax else None
+        keep_o = softmax and bwd_reads_o(bf, d, n)
+        # softmax: each layer's LSE (and, where the backward reads it, its GDPA output).
+        self.o = [torch.empty((T, H, d), dtype=bf, device=dev) for _ in range(self.L)] if keep_o else None
         self.lse = [torch.empty((T, H), dtype=torch.float32, device=dev) for _ in range(self.L)] if softmax else None
         probe_q = torch.empty((T, H, d), dtype=bf, device="meta")
         probe_k = torch.empty((B, n, H, d), dtype=bf, device="meta")
@@ -72,7 +74,8 @@ class StackedGdpa:
                           o=self.o[l], y=self.x[l + 1], lse=self.lse[l], workspace=self.ws_f)
             else:
                 fwd(self.x[l], self.offsets, self.k[l], self.v[l], phi=self.phi, scale=self.scale,
-                    residual=self.x[l], out=self.x[l + 1], workspace=self.ws_f)
+                    residual=self.x[l], out=self.x[l + 1],
+                    lse=self.lse[l] if self.lse is not None else None, workspace=self.ws_f)
             mark("gdpa_fwd", False)
         return self.x[self.L]
 

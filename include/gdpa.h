@@ -122,7 +122,10 @@ gdpa_status gdpa_fwd(const gdpa_problem* p, const int32_t* offsets, const void* 
  * accumulated with GDPA_BWD_ACCUM_DQ; dO added with GDPA_BWD_RESIDUAL), dk, dv
  * [B,n,H,d] (overwritten; each is
  * the sum over the sample's own tokens, zero for an empty sample).  With an elementwise map,
- * o and lse are not read and may be NULL. */
+ * o and lse are not read and may be NULL.  The softmax row term rowsum(dO * O) equals
+ * sum_j P_j dP_j; for bf16 with head_dim 128 and n_kv <= 256 (one work-group holds a
+ * sample's whole context) it is summed from P and dP inside the backward, o is not
+ * read and may be NULL (lse is still required). */
 gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* q, const void* k,
                      const void* v, const void* o, const float* lse, const void* d_o, void* dq,
                      void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream);
@@ -133,8 +136,8 @@ gdpa_status gdpa_bwd(const gdpa_problem* p, const int32_t* offsets, const void* 
  *     o = GDPA(x; k, v)   and   y = x + o
  * written in one pass.  gdpa_fwd with GDPA_FWD_RESIDUAL writes only y; this call
  * keeps o as well, which the softmax backward of such a layer needs for its row
- * term (o taken back as y - x would carry y's rounding, relative to |x|).  The
- * backward is gdpa_bwd with GDPA_BWD_RESIDUAL and this o.  p->flags must be 0;
+ * term where it reads o (o taken back as y - x would carry y's rounding, relative
+ * to |x|).  The backward is gdpa_bwd with GDPA_BWD_RESIDUAL and this o.  p->flags must be 0;
  * o and y must be distinct from each other and from x, k and v.  Otherwise as
  * gdpa_fwd (lse written for softmax when non-NULL; workspace as gdpa_fwd's). */
 gdpa_status gdpa_fwd_block(const gdpa_problem* p, const int32_t* offsets, const void* x, const void* k,
@@ -250,8 +253,9 @@ gdpa_status gdpa_bwd_grouped(int32_t n, const gdpa_group* groups, void* workspac
  * and errors as gdpa_bwd without the workspace; a problem whose gdpa_bwd
  * workspace (gdpa_workspace_bytes(p, 1)) exceeds the scratch fails with
  * GDPA_ERR_WORKSPACE_TOO_SMALL before anything is launched (for the softmax map
- * it holds 4 * total_tokens * heads bytes of row dots, so up to about 16.7 M
- * token-head rows; the elementwise maps need only a few bytes per sample).
+ * outside the one-work-group shapes named at gdpa_bwd it holds 4 * total_tokens *
+ * heads bytes of row dots, so up to about 16.7 M token-head rows; otherwise a few
+ * bytes per sample).
  * `stream` must belong to the current device.  The call allocates nothing and
  * nothing in the scratch needs to start at zero.  All calls on one GPU share
  * its scratch: two calls that overlap in time on one GPU (on different streams,

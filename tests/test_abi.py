@@ -84,6 +84,14 @@ def test_bwd_rejects_bad_arguments(lib):
     assert bwd(lib, P(head_dim=16)) == UNSUPPORTED
     assert bwd(lib, P(), lse=None) == INVALID      # softmax needs lse
     assert bwd(lib, P(), o=None) == INVALID
+    # bf16, d = 128, n_kv <= 256: the backward sums the softmax row term itself and
+    # reads no O, so o may be NULL (the call gets as far as the workspace check);
+    # lse is still required.
+    one_wg = dict(head_dim=128, n_kv=4)
+    assert bwd(lib, P(**one_wg), o=None, ws_bytes=4) == WS_SMALL
+    assert bwd(lib, P(**one_wg), o=None, lse=None) == INVALID
+    assert bwd(lib, P(head_dim=128, n_kv=300), o=None) == INVALID
+    assert bwd(lib, P(dtype=0, **one_wg), o=None) == INVALID   # fp32 reads O
     assert bwd(lib, P(), dk=None) == INVALID
     assert bwd(lib, P(flags=cca.FWD_RESIDUAL)) == INVALID
     assert bwd(lib, P(), dq=V, do=V) == INVALID    # in-place dQ needs the accumulate flag
