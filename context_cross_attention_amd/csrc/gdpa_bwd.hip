@@ -190,6 +190,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_bf16_kernel(const BwdArgs
     }
     __syncthreads();
     if (tq + BQ < tq_end) load_step(tq + BQ);
+    // SW: no token of this step sees any of the wave's 32 key rows (all are after the
+    // tokens, or all left their windows): nothing to add (no barrier follows in the
+    // step without dQ).
+    if (SW && !DQ && (tq + BQ - 1 < j0 + 32 * wave || tq - a.window >= j0 + 32 * wave + 31)) continue;
 
     // S = Q K^T and dP = dO V^T for the wave's 32 context rows.
     f32x16 S = f32x16{}, dP = f32x16{};

@@ -115,6 +115,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
     store_block(jb);
     __syncthreads();
     if (jb + BN < jend) gload_block(jb + BN);
+    // SW: none of the wave's 32 query rows sees a key row of this block (all lie after
+    // the rows, or all left their windows): it adds nothing (no barrier follows).
+    if (SW && (jb > qlo + 32 * wave + 31 || jb + BN - 1 <= qlo + 32 * wave - a.window)) continue;
     // Score bias (BIAS) of rows 32 mt + 8 q + 4 g + {0..3}: register 4 q + i of tile mt.
     float bj[2][16];
 #pragma unroll
