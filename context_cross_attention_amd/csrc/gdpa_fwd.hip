@@ -158,10 +158,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       const float m_new = fmaxf(m_run, mx);
       // A row whose window misses this whole block (SW) keeps m = -inf: shift by 0.
       const float m_use = (SW && m_new == -INFINITY) ? 0.f : m_new;
-      const float corr = fast_exp2(m_run - m_use);
-      l_run *= corr;
+      // Rescale O only when some row's running max moved (wave-uniform test).
+      if (__any(m_new > m_run)) {
+        const float corr = fast_exp2(m_run - m_use);
+        l_run *= corr;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) O[dt] *= corr;
+        for (int dt = 0; dt < DT; ++dt) O[dt] *= corr;
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
