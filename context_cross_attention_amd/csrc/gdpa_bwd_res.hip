@@ -425,17 +425,22 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       const int x0 = kt_x(kr) & 1, sw = (kt_x(kr) >> 1) * 16;
       const int oa_p = kr * LDJ + 8 * (g ^ x0) + sw, oa_m = kr * LDJ + 8 * (g ^ x0) - sw;
       const int ob = lxd * LDS_ + 8 * g;
-      bf16x8 ka[2], sb[2];
+      // One wave per SIMD runs this product (the other transposes), so its operands are
+      // read three k-steps ahead: the registers of phase one are free here (except in
+      // the softmax with FFN biases, which keeps one step ahead to stay within them).
+      constexpr int PF = PHI == 0 && DQB == 3 ? 1 : 3;
+      bf16x8 ka[PF + 1], sb[PF + 1];
       auto dq_load = [&](int ks, int bsel) {
         ka[bsel] = lds_read8(&Kt[(ks & 1 ? oa_m : oa_p) + 16 * ks]);
         sb[bsel] = lds_read8(&dSs[ob + 16 * ks]);
       };
-      dq_load(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < PF; ++ks) dq_load(ks, ks);
 #pragma unroll
       for (int ks = 0; ks < NJ / 16; ++ks) {
-        if (ks + 1 < NJ / 16) dq_load(ks + 1, (ks + 1) & 1);
+        if (ks + PF < NJ / 16) dq_load(ks + PF, (ks + PF) % (PF + 1));
         __builtin_amdgcn_sched_barrier(0);
-        dq = mfma32(ka[ks & 1], sb[ks & 1], dq);
+        dq = mfma32(ka[ks % (PF + 1)], sb[ks % (PF + 1)], dq);
         __builtin_amdgcn_sched_barrier(0);
       }
       // Lane (t + 32 g), register r: column 32 w + 16 g + r of token t = lr.

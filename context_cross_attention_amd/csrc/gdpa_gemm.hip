@@ -24,7 +24,7 @@ namespace gdpa {
 // copies into a 2-stage ring of k steps of 64 that runs on across tile boundaries, one
 // step (64 MFMAs per SIMD) ahead of the MFMAs; each wave issues eight 1 KiB copies
 // (8 rows of 128 bytes) per step, a row's eight 16-byte k chunks stored at positions
-// c ^ (row & 7) so that 8 consecutive rows of one chunk fall in distinct banks.  The
+// c ^ nt_swz(row) so that 16 consecutive rows of one chunk fall in distinct banks.  The
 // MFMA A operand is B's rows (n) and the B operand A's rows (m), so the C tile gives
 // each lane four consecutive n of one m.  A finished tile is written 32 rows at a
 // time through a 4 KiB LDS area of the wave's own (no barrier) and stored as whole
@@ -40,6 +40,11 @@ constexpr int NT_RPI = 1024 / NT_ROW_B;            // rows per 1 KiB copy instru
 constexpr int NT_IPW = NT_M / 8 / NT_RPI;          // copy instructions per wave per tile (4)
 constexpr int NT_STORES = 16;                      // 16-byte stores per wave per tile
 constexpr int NT_CW_B = 32 * 64 * 2;               // per-wave output staging (32 x 64 bf16)
+// Position swizzle of a staged row's 16-byte chunks.  Rows are 128 bytes, half the
+// 256-byte bank period, so rows r and r + 2 start on the same banks; XOR-ing the chunk
+// with (r / 2) % 8 puts the 16 rows that one 16-lane phase of a ds_read_b128 reads (same
+// chunk) in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int nt_swz(int row) { return (row >> 1) & 7; }
 }  // namespace
 
 __global__ __launch_bounds__(NT_T, 1) void gemm_nt_kernel(int M, long N, int K,
@@ -90,7 +95,7 @@ __global__ __launch_bounds__(NT_T, 1) void gemm_nt_kernel(int M, long N, int K,
 #pragma unroll
     for (int q = 0; q < NT_IPW; ++q) {
       const int row = 32 * wave + NT_RPI * q + lane / (NT_ROW_B / 16);
-      const int k = min(k0 + 8 * ((lane % (NT_ROW_B / 16)) ^ (row & 7)), K - 8);
+      const int k = min(k0 + 8 * ((lane % (NT_ROW_B / 16)) ^ nt_swz(row)), K - 8);
       const uint32_t lo = (uint32_t)((32 * wave + NT_RPI * q) * NT_ROW_B);
       dma16(__builtin_amdgcn_readfirstlane(sb + lo), A + (long)min(p.m0 + row, M - 1) * K + k);
       dma16(__builtin_amdgcn_readfirstlane(sb + NT_TILE_B + lo), Bm + min(p.n0 + row, N - 1) * K + k);
@@ -132,13 +137,13 @@ __global__ __launch_bounds__(NT_T, 1) void gemm_nt_kernel(int M, long N, int K,
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int row = wn + 32 * j + lx;
-        xs[j] = lds_read8(&Bs[row * NT_K + 8 * (c ^ (row & 7))]);
+        xs[j] = lds_read8(&Bs[row * NT_K + 8 * (c ^ nt_swz(row))]);
         if (tail && kx * NT_K + 8 * c >= K) xs[j] = bf16x8{};
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wm + 32 * i + lx;
-        ys[i] = lds_read8(&As[row * NT_K + 8 * (c ^ (row & 7))]);
+        ys[i] = lds_read8(&As[row * NT_K + 8 * (c ^ nt_swz(row))]);
       }
     };
     load(0, x[0], y[0]);
