@@ -106,8 +106,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   f32x16 O[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
+  // Online softmax in base 2.  Without biases the running max is kept in units of the
+  // raw product Q.K (the scale is positive, so the max commutes with it) and the scale
+  // enters each exponent through the FMA that subtracts the max: one VALU operation
+  // per score fewer.  With biases the scores are scaled first (sm = 1).
   float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = a.scale * kLog2e;
+  const float sl2 = a.scale * kLog2e, sm = BIAS ? 1.0f : sl2;
 
   gload_block(jbeg);
   for (int jb = jbeg; jb < jend; jb += BN) {
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float s = BIAS ? fmaf(bj[mt][r], kLog2e, S[mt][r] * sl2) : S[mt][r] * sl2;
+          float s = BIAS ? fmaf(bj[mt][r], kLog2e, S[mt][r] * sl2) : S[mt][r];
           if (tail || SW) {
             const int j = jb + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
             if (j >= n || (SW && (j > irow || j <= irow - a.window))) s = -INFINITY;
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       const float m_use = (SW && m_new == -INFINITY) ? 0.f : m_new;
       // Rescale O only when some row's running max moved (wave-uniform test).
       if (__any(m_new > m_run)) {
-        const float corr = fast_exp2(m_run - m_use);
+        const float corr = fast_exp2((m_run - m_use) * sm);
         l_run *= corr;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) O[dt] *= corr;
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(S[mt][r] - m_use);
+          const float p = fast_exp2(fmaf(S[mt][r], sm, -m_use * sm));
           l_run += p;
           S[mt][r] = p;
         }
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) O[dt] *= inv;
     if (tvalid && g == 0 && a.lse != nullptr)
-      a.lse[(size_t)(row0 + trow) * H + h] = (m_run + __log2f(l_tot)) * kLn2;
+      a.lse[(size_t)(row0 + trow) * H + h] = fmaf(m_run, sm, __log2f(l_tot)) * kLn2;
   }
   if (tvalid) {
     // Lane (t, g), register r holds O[t][d = 32 dt + 8 (r / 4) + 4 g + r % 4].

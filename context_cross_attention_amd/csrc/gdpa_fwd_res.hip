@@ -118,7 +118,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
   }
   __syncthreads();
 
-  const float scl = a.scale, sl2 = scl * kLog2e, nsl2 = -sl2;
+  const float scl = a.scale, sl2 = scl * kLog2e, nsl2 = -sl2, sm = RESID == 3 ? 1.0f : sl2;
   const int nchunks = (L + 31) / 32;
   // Query rows past the sample are read from its last row (clamped, always a
   // valid address) and never stored: each lane's row is independent.  k-step ks of
@@ -161,11 +161,14 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         for (int i = 0; i < 4; ++i) bj[4 * q + i] = bv[i];
       }
       if (PHI == 0) {
+        // Without biases the running max is kept in units of the raw product Q.K and
+        // the scale enters each exponent through the FMA that subtracts the max (one
+        // VALU operation per score fewer); with biases the scores are scaled first.
         const bool tail = j0 + 32 > n;
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float s = RESID == 3 ? fmaf(bj[r], kLog2e, S[r] * sl2) : S[r] * sl2;
+          float s = RESID == 3 ? fmaf(bj[r], kLog2e, S[r] * sl2) : S[r];
           if (tail && j0 + 8 * (r >> 2) + 4 * g + (r & 3) >= n) s = -INFINITY;
           S[r] = s;
           mx = fmaxf(mx, s);
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         // Rescale O only when some row's running max moved (wave-uniform test).
         if (__any(mx > m_run)) {
           const float m_new = fmaxf(m_run, mx);
-          const float corr = fast_exp2(m_run - m_new);
+          const float corr = fast_exp2((m_run - m_new) * sm);
           l_run *= corr;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) O[dt] *= corr;
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(S[r] - m_run);
+          const float p = fast_exp2(fmaf(S[r], sm, -m_run * sm));
           l_run += p;
           S[r] = p;
         }
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
       const float l_tot = l_run + wave_xor32(l_run);
       oscale = 1.0f / l_tot;
       if (tvalid && g == 0 && a.lse != nullptr)
-        a.lse[(size_t)(seq0 + t) * H + h] = (m_run + __log2f(l_tot)) * kLn2;
+        a.lse[(size_t)(seq0 + t) * H + h] = fmaf(m_run, sm, __log2f(l_tot)) * kLn2;
     }
     if (tvalid) {
       // Lane group g holds columns 32 dt + 16 g + r in register r (see vt_row).
