@@ -106,12 +106,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
   f32x16 O[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
-  // Online softmax in base 2.  Without biases the running max is kept in units of the
-  // raw product Q.K (the scale is positive, so the max commutes with it) and the scale
-  // enters each exponent through the FMA that subtracts the max: one VALU operation
-  // per score fewer.  With biases the scores are scaled first (sm = 1).
+  // Online softmax in base 2.  With a positive scale and no biases the running max is
+  // kept in units of the raw product Q.K (the max commutes with the scale) and the
+  // scale enters each exponent through the FMA that subtracts the max: one VALU
+  // operation per score fewer.  Otherwise (biases, or a scale <= 0) the scores are
+  // scaled first and sm = 1.
   float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = a.scale * kLog2e, sm = BIAS ? 1.0f : sl2;
+  const float sl2 = a.scale * kLog2e;
+  const bool raw = !BIAS && a.scale > 0.f;
+  const float sm = raw ? sl2 : 1.0f;
 
   gload_block(jbeg);
   for (int jb = jbeg; jb < jend; jb += BN) {
@@ -146,18 +149,27 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       // Online softmax over the context rows, base 2.
       const bool tail = jb + BN > n;
       float mx = -INFINITY;
+      auto mask_max = [&](auto score) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s = BIAS ? fmaf(bj[mt][r], kLog2e, S[mt][r] * sl2) : S[mt][r];
-          if (tail || SW) {
-            const int j = jb + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (j >= n || (SW && (j > irow || j <= irow - a.window))) s = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            float s = score(mt, r);
+            if (tail || SW) {
+              const int j = jb + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
+              if (j >= n || (SW && (j > irow || j <= irow - a.window))) s = -INFINITY;
+            }
+            S[mt][r] = s;
+            mx = fmaxf(mx, s);
           }
-          S[mt][r] = s;
-          mx = fmaxf(mx, s);
-        }
+      };
+      if (raw) {  // wave-uniform
+        mask_max([&](int mt, int r) { return S[mt][r]; });
+      } else {
+        mask_max([&](int mt, int r) {
+          return BIAS ? fmaf(bj[mt][r], kLog2e, S[mt][r] * sl2) : S[mt][r] * sl2;
+        });
+      }
       mx = fmaxf(mx, wave_xor32(mx));
       const float m_new = fmaxf(m_run, mx);
       // A row whose window misses this whole block (SW) keeps m = -inf: shift by 0.

@@ -118,7 +118,10 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
   }
   __syncthreads();
 
-  const float scl = a.scale, sl2 = scl * kLog2e, nsl2 = -sl2, sm = RESID == 3 ? 1.0f : sl2;
+  const float scl = a.scale, sl2 = scl * kLog2e, nsl2 = -sl2;
+  // Softmax: with a positive scale and no biases the running max is kept in raw Q.K
+  // units (see mix); the chunk loop is compiled for both cases (RAW below).
+  const bool raw_max = PHI == 0 && RESID != 3 && scl > 0.f;
   const int nchunks = (L + 31) / 32;
   // Query rows past the sample are read from its last row (clamped, always a
   // valid address) and never stored: each lane's row is independent.  k-step ks of
@@ -132,7 +135,9 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
   };
 
   // One 32-row chunk with Q already in qc; prefetches the Q of chunk ch + NW into qn.
-  auto do_chunk = [&](int ch, const bf16x8* qc, bf16x8* qn) {
+  auto do_chunk = [&](int ch, const bf16x8* qc, bf16x8* qn, auto RAW) {
+    constexpr bool raw = decltype(RAW)::value;
+    const float sm = raw ? sl2 : 1.0f;
     const int t = 32 * ch + lr;
     const bool tvalid = t < L;
     load_q(ch + NW, qn);
@@ -161,17 +166,25 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         for (int i = 0; i < 4; ++i) bj[4 * q + i] = bv[i];
       }
       if (PHI == 0) {
-        // Without biases the running max is kept in units of the raw product Q.K and
-        // the scale enters each exponent through the FMA that subtracts the max (one
-        // VALU operation per score fewer); with biases the scores are scaled first.
+        // With a positive scale and no biases the running max is kept in units of the
+        // raw product Q.K and the scale enters each exponent through the FMA that
+        // subtracts the max (one VALU operation per score fewer); otherwise (biases, or
+        // a scale <= 0) the scores are scaled first and sm = 1.
         const bool tail = j0 + 32 > n;
         float mx = -INFINITY;
+        auto mask_max = [&](auto score) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s = RESID == 3 ? fmaf(bj[r], kLog2e, S[r] * sl2) : S[r];
-          if (tail && j0 + 8 * (r >> 2) + 4 * g + (r & 3) >= n) s = -INFINITY;
-          S[r] = s;
-          mx = fmaxf(mx, s);
+          for (int r = 0; r < 16; ++r) {
+            float s = score(r);
+            if (tail && j0 + 8 * (r >> 2) + 4 * g + (r & 3) >= n) s = -INFINITY;
+            S[r] = s;
+            mx = fmaxf(mx, s);
+          }
+        };
+        if (raw) {
+          mask_max([&](int r) { return S[r]; });
+        } else {
+          mask_max([&](int r) { return RESID == 3 ? fmaf(bj[r], kLog2e, S[r] * sl2) : S[r] * sl2; });
         }
         mx = fmaxf(mx, wave_xor32(mx));
         // Rescale O only when some row's running max moved (wave-uniform test).
@@ -275,11 +288,19 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
   };
 
   // Two register sets for Q alternate between "current" and "prefetch".
-  bf16x8 qa[KS], qb[KS];
-  load_q(wave, qa);
-  for (int ch = wave; ch < nchunks; ch += 2 * NW) {
-    do_chunk(ch, qa, qb);
-    if (ch + NW < nchunks) do_chunk(ch + NW, qb, qa);
+  auto chunks = [&](auto RAW) {
+    bf16x8 qa[KS], qb[KS];
+    load_q(wave, qa);
+    for (int ch = wave; ch < nchunks; ch += 2 * NW) {
+      do_chunk(ch, qa, qb, RAW);
+      if (ch + NW < nchunks) do_chunk(ch + NW, qb, qa, RAW);
+    }
+  };
+  if constexpr (PHI == 0) {
+    if (raw_max) chunks(std::true_type{});  // wave-uniform
+    else chunks(std::false_type{});
+  } else {
+    chunks(std::false_type{});
   }
 }
 

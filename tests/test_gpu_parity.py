@@ -122,6 +122,18 @@ def test_bf16_explicit_scale(gdpa_lib):
     run_case(gdpa_lib, custom_config((90, 140), H=2, d=128, n=128, phi="silu"), "silu", scale=0.5)
 
 
+@pytest.mark.parametrize("n", [200, 512], ids=["resident", "streaming"])
+@pytest.mark.parametrize("scale", [-0.37, 0.0], ids=["negative", "zero"])
+def test_bf16_softmax_nonpositive_scale(gdpa_lib, n, scale):
+    # Any finite scale is accepted.  The forwards keep the softmax's running max in raw
+    # Q.K units only for a positive scale (where the max commutes with it); a negative
+    # scale turns the maximum into a minimum and a zero scale makes every score 0 (the
+    # uniform average, LSE = ln n).  Both forward kernels (resident context, n <= 256
+    # at d = 128, and the streaming one) and the backward are checked.
+    cfg = custom_config((90, 140, 7), H=2, d=128, n=n, phi="softmax")
+    run_case(gdpa_lib, cfg, "softmax", scale=scale, sharp=True)
+
+
 @pytest.mark.parametrize("dtype,d,n", [("bf16", 64, 96), ("f32", 64, 96), ("bf16", 128, 200)])
 @pytest.mark.parametrize("mode", ["accumulate", "residual"])
 def test_residual_and_accumulated_dq(gdpa_lib, dtype, d, n, mode):
