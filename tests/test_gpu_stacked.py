@@ -11,7 +11,11 @@ from tests.gpu_helpers import TOL, max_abs_rel, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("B,c,cols", [(37, 64, 520), (128, 512, 1024), (1, 8, 8), (300, 40, 264)])
+# Shapes: a single partial tile, the stacked workload's ctx width, degenerate sizes,
+# ragged tiles with K below one k-step, and several m-tiles with a ragged K tail and
+# ragged n (the persistent tile walk crosses tiles with a partial last k-step).
+@pytest.mark.parametrize("B,c,cols", [(37, 64, 520), (128, 512, 1024), (1, 8, 8), (300, 40, 264),
+                                      (1030, 200, 696), (513, 72, 2056)])
 def test_weightgen_gemms(gdpa_lib, B, c, cols):
     cca = gdpa_lib
     rng = np.random.default_rng(B + c + cols)
