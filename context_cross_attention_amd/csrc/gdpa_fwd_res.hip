@@ -142,9 +142,9 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
     const bool tvalid = t < L;
     load_q(ch + NW, qn);
     const size_t obase = (size_t)(seq0 + min(t, L - 1)) * rs + (size_t)h * D + 16 * g;
+    // O is first written by the first tile's products (zero accumulator operand), so
+    // it needs no zeroing.
     f32x16 O[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) O[dt] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
     // S^T for the 32 context rows j0 .. j0 + 31.
@@ -155,7 +155,9 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         S = mfma32(lds_read8(&Kc[(j0 + lr) * LDK + 32 * (ks >> 1) + 16 * g + 8 * (ks & 1)]), qc[ks], S);
     };
     // phi of one 32-row tile, then O^T += V^T P^T.
-    auto mix = [&](int j0, f32x16& S) {
+    // FIRST: the chunk's first tile (O not yet written, no running max to rescale).
+    auto mix = [&](int j0, f32x16& S, auto FIRST) {
+      constexpr bool first = decltype(FIRST)::value;
       // Score bias of rows j0 + 8 q + 4 g + {0..3} (register 4 q + i): the scaled
       // score becomes S * scale + b, applied in each map's own units below.
       float bj[16];
@@ -187,8 +189,9 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
           mask_max([&](int r) { return RESID == 3 ? fmaf(bj[r], kLog2e, S[r] * sl2) : S[r] * sl2; });
         }
         mx = fmaxf(mx, wave_xor32(mx));
-        // Rescale O only when some row's running max moved (wave-uniform test).
-        if (__any(mx > m_run)) {
+        if (first) {
+          m_run = mx;
+        } else if (__any(mx > m_run)) {  // rescale O only when some row's running max moved (wave-uniform)
           const float m_new = fmaxf(m_run, mx);
           const float corr = fast_exp2((m_run - m_new) * sm);
           l_run *= corr;
@@ -220,20 +223,28 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         const int vr = vt_row(lr);  // V^T row within each 32-column block
         const uint16_t* vb = &Vt[vr * LDV + 8 * vt_chunk((j0 >> 3) + 2 * kk + g, vr)];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) O[dt] = mfma32(lds_read8(vb + 32 * dt * LDV), p, O[dt]);
+        for (int dt = 0; dt < DT; ++dt)
+          O[dt] = mfma32(lds_read8(vb + 32 * dt * LDV), p, first && kk == 0 ? f32x16{} : O[dt]);
       }
     };
 
     // Software pipeline: the MFMAs for the next tile's scores are issued before
     // this tile's phi, so the VALU work overlaps matrix-core time.
+    // npad is a multiple of 64, so the tiles come in pairs (at least one).
     const int ntile = npad / 32;
     f32x16 Sa, Sb;
     scores(0, Sa);
-    for (int jt = 0; jt < ntile; jt += 2) {
-      scores(32 * (jt + 1), Sb);          // npad is a multiple of 64: tile jt + 1 exists
-      mix(32 * jt, Sa);
+    scores(32, Sb);
+    mix(0, Sa, std::true_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    if (2 < ntile) scores(64, Sa);
+    mix(32, Sb, std::false_type{});
+    __builtin_amdgcn_sched_barrier(0);
+    for (int jt = 2; jt < ntile; jt += 2) {
+      scores(32 * (jt + 1), Sb);
+      mix(32 * jt, Sa, std::false_type{});
       if (jt + 2 < ntile) scores(32 * (jt + 2), Sa);
-      mix(32 * (jt + 1), Sb);
+      mix(32 * (jt + 1), Sb, std::false_type{});
     }
     // The output is O times a per-row factor (SiLU: the constant -ln 2; softmax: 1 / the
     // row sum), applied in the epilogue together with the residual (one FMA per item).
