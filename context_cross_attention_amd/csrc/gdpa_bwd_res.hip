@@ -352,11 +352,21 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) dP[4 * q4 + c] = S[4 * q4 + c] * (dP[4 * q4 + c] - dvv[c]);
       }
+    } else if (PHI == kPhiSilu && DQB != 3) {
+      // With sg = sigmoid(scale S) and q = S sg: P = scale q (the scale is applied to dV
+      // at the end, like dK's) and dS / dP = sg + scale q (1 - sg).
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float sg = fast_rcp(1.0f + fast_exp2(S[r] * c1));
+        const float q = S[r] * sg;
+        S[r] = q;
+        dP[r] = dP[r] * fmaf(scale, fmaf(-q, sg, q), sg);
+      }
     } else if (PHI == kPhiSilu) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float sv = DQB == 3 ? fmaf(S[r], scale, sbj) : S[r] * scale;
-        const float sg = fast_rcp(1.0f + fast_exp2(DQB == 3 ? -sv * kLog2e : S[r] * c1));
+        const float sv = fmaf(S[r], scale, sbj);
+        const float sg = fast_rcp(1.0f + fast_exp2(-sv * kLog2e));
         const float p = sv * sg;
         S[r] = p;
         dP[r] = dP[r] * fmaf(sv - p, sg, sg);
@@ -380,7 +390,10 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
       sa[kk] = pack_c8(dP, kk);
       // dS row-major for the dQ product: item i of k-step kk is token
       // 16 kk + 8 (i / 4) + 4 g + i % 4.
-      const u32x4 sw = __builtin_bit_cast(u32x4, sa[kk]);
+      // (hidden from the optimiser, which would otherwise convert each half again on
+      // its own instead of writing the halves of the packed registers)
+      u32x4 sw = __builtin_bit_cast(u32x4, sa[kk]);
+      asm("" : "+v"(sw));
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         dSs[(16 * kk + 8 * (i >> 2) + 4 * g + (i & 3)) * LDS_ + j] = half_of(sw, i);
@@ -475,6 +488,7 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
   }
   if (wave >= 4) wait_vmcnt<0>();
   __syncthreads();
+  constexpr bool dv_scaled = PHI == kPhiSilu && DQB != 3;  // P was kept without its scale
   uint16_t* Ew = Kt + wave * 32 * LDE;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
@@ -484,7 +498,8 @@ __global__ __launch_bounds__(512, 1) void bwd_res_kernel(const BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         Ew[(8 * (r >> 2) + 4 * g + (r & 3)) * LDE + 32 * dt + lr] =
-            __builtin_bit_cast(uint16_t, f2bf(which == 0 ? dK[dt][r] * scale : dV[dt][r]));
+            __builtin_bit_cast(uint16_t, f2bf(which == 0 || dv_scaled ? (which == 0 ? dK[dt][r] : dV[dt][r]) * scale
+                                                                     : dV[dt][r]));
     uint16_t* dst = (uint16_t*)(which == 0 ? a.dk : a.dv) + (crow0 * H + h) * D;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
