@@ -220,7 +220,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_bf16_kernel(const BwdArgs
         p = phi_value_grad<PHI>(BIAS ? fmaf(S[r], a.scale, sbj) : S[r] * a.scale, gr);
         ds = dP[r] * gr;
       }
-      if (!jvalid || (SW && (jw > tq + t || jw <= tq + t - a.window))) {
+      // Rows past n (lanes with !jvalid) have zero K and V: their scores are finite,
+      // their dK, dV and score-bias gradients are never stored, and they add nothing
+      // to dQ (zero K rows), so only a sliding window's band needs masking.
+      if (SW && (!jvalid || jw > tq + t || jw <= tq + t - a.window)) {
         p = 0.f;
         ds = 0.f;
       }

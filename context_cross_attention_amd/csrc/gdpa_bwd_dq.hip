@@ -22,7 +22,7 @@ template <int D, int PHI, bool SW, bool BIAS = false>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
   constexpr int BM = kFwdTileRows, BN = 64, KS = D / 16, DT = D / 32;
   constexpr int LD = D + 8;                   // K and V rows (16-byte reads of 16 rows: distinct banks)
-  constexpr int kHalves = (PHI == kPhiSoftmax || PHI == kPhiRelu) ? 1 : 2;  // unrolled 32-row halves
+  constexpr int kHalves = (PHI == kPhiGelu || PHI == kPhiIdentity) ? 2 : 1;  // unrolled 32-row halves
   constexpr int CH = D / 8;
   constexpr int SI = (BN * CH + 255) / 256;   // staging chunks per thread per tensor
   __shared__ __align__(16) uint16_t Ks[BN * LD];
@@ -136,7 +136,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
           phi_value_grad<PHI>(BIAS ? fmaf(S[r], a.scale, bj[r]) : S[r] * a.scale, gr);
           ds = dP[r] * gr;
         }
-        if (j >= n || (SW && (j > irow || j <= irow - a.window))) ds = 0.f;
+        // Rows past n hold zero K and V in LDS (finite scores, and zero products with
+        // K), so only a sliding window's band needs masking.
+        if (SW && (j >= n || j > irow || j <= irow - a.window)) ds = 0.f;
         S[r] = ds;
       }
 #pragma unroll

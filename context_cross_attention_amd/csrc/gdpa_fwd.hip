@@ -147,15 +147,25 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
 
     if (PHI == 0) {
       // Online softmax over the context rows, base 2.
+      // Only the last block of a context (or a sliding window's band) has scores to
+      // mask; the test is wave-uniform, and each case is compiled on its own so that
+      // full blocks carry no per-score select.
       const bool tail = jb + BN > n;
       float mx = -INFINITY;
-      auto mask_max = [&](auto score) {
+      if (!raw) {  // wave-uniform: scores in base-2 units first (see sm)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            S[mt][r] = BIAS ? fmaf(bj[mt][r], kLog2e, S[mt][r] * sl2) : S[mt][r] * sl2;
+      }
+      auto mask_max = [&](auto MASK) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float s = score(mt, r);
-            if (tail || SW) {
+            float s = S[mt][r];
+            if (decltype(MASK)::value) {
               const int j = jb + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
               if (j >= n || (SW && (j > irow || j <= irow - a.window))) s = -INFINITY;
             }
@@ -163,13 +173,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
             mx = fmaxf(mx, s);
           }
       };
-      if (raw) {  // wave-uniform
-        mask_max([&](int mt, int r) { return S[mt][r]; });
-      } else {
-        mask_max([&](int mt, int r) {
-          return BIAS ? fmaf(bj[mt][r], kLog2e, S[mt][r] * sl2) : S[mt][r] * sl2;
-        });
-      }
+      if (SW || tail) mask_max(std::true_type{});  // wave-uniform
+      else mask_max(std::false_type{});
       mx = fmaxf(mx, wave_xor32(mx));
       const float m_new = fmaxf(m_run, mx);
       // A row whose window misses this whole block (SW) keeps m = -inf: shift by 0.
