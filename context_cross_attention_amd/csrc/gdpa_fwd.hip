@@ -173,7 +173,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
             mx = fmaxf(mx, s);
           }
       };
-      if (SW || tail) mask_max(std::true_type{});  // wave-uniform
+      // A sliding window's block needs no mask when it lies inside the window of every
+      // row of the wave (and before the end of the sample).
+      const int i0 = qlo + 32 * wave;
+      const bool inside = SW && jb + BN - 1 <= i0 && jb > i0 + 31 - a.window;
+      if (tail || (SW && !inside)) mask_max(std::true_type{});  // wave-uniform
       else mask_max(std::false_type{});
       mx = fmaxf(mx, wave_xor32(mx));
       const float m_new = fmaxf(m_run, mx);
