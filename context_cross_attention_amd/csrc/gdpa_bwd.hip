@@ -213,16 +213,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_bf16_kernel(const BwdArgs
       const int t = 8 * (r >> 2) + 4 * g + (r & 3);
       float p, ds;
       if (PHI == 0) {
-        p = fast_exp2(BIAS ? fmaf(sbj, kLog2e, S[r] * sl2) - lse_s[t] : S[r] * sl2 - lse_s[t]);
+        // P <= 1 for the sample's rows; the cap keeps rows past n finite when every
+        // score of the token is very negative (their P would overflow).
+        p = fminf(fast_exp2(BIAS ? fmaf(sbj, kLog2e, S[r] * sl2) - lse_s[t] : S[r] * sl2 - lse_s[t]), 1.0f);
         ds = p * (dP[r] - dvec_s[t]);
       } else {
         float gr;
         p = phi_value_grad<PHI>(BIAS ? fmaf(S[r], a.scale, sbj) : S[r] * a.scale, gr);
         ds = dP[r] * gr;
       }
-      // Rows past n (lanes with !jvalid) have zero K and V: their scores are finite,
-      // their dK, dV and score-bias gradients are never stored, and they add nothing
-      // to dQ (zero K rows), so only a sliding window's band needs masking.
+      // Rows past n (lanes with !jvalid) have zero K and V: their scores and P are
+      // finite, their dK, dV and score-bias gradients are never stored, and they add
+      // nothing to dQ (zero K rows), so only a sliding window's band needs masking.
       if (SW && (!jvalid || jw > tq + t || jw <= tq + t - a.window)) {
         p = 0.f;
         ds = 0.f;

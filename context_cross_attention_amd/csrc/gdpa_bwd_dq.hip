@@ -129,15 +129,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(const BwdArgs a) {
         const int j = jb + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
         float ds;
         if (PHI == kPhiSoftmax) {
-          const float p = fast_exp2(fmaf(S[r], sl2, BIAS ? fmaf(bj[r], kLog2e, -lse2) : -lse2));
+          // P <= 1 for the sample's rows; the cap keeps rows past n finite when every
+          // score of the token is very negative (their P would overflow).
+          const float p = fminf(fast_exp2(fmaf(S[r], sl2, BIAS ? fmaf(bj[r], kLog2e, -lse2) : -lse2)), 1.0f);
           ds = p * (dP[r] - dvec);
         } else {
           float gr;
           phi_value_grad<PHI>(BIAS ? fmaf(S[r], a.scale, bj[r]) : S[r] * a.scale, gr);
           ds = dP[r] * gr;
         }
-        // Rows past n hold zero K and V in LDS (finite scores, and zero products with
-        // K), so only a sliding window's band needs masking.
+        // Rows past n hold zero K and V in LDS (finite scores and P, and zero products
+        // with K), so only a sliding window's band needs masking.
         if (SW && (j >= n || j > irow || j <= irow - a.window)) ds = 0.f;
         S[r] = ds;
       }

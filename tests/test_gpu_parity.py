@@ -134,6 +134,50 @@ def test_bf16_softmax_nonpositive_scale(gdpa_lib, n, scale):
     run_case(gdpa_lib, cfg, "softmax", scale=scale, sharp=True)
 
 
+def very_negative_scores(base, d, seed):
+    """Q and K of `base` replaced so that every score is below about -100: every query is
+    40 u (plus a little noise) and every key row -40 u + w_j, u the unit vector along
+    (1, ..., 1) and w_j with entries N(0, 1600 / d).  The shared key component is no
+    larger than the varying one (|w_j| is about 40), so dQ stays well conditioned
+    against the bf16 rounding of dS (the shared part cancels from dQ only exactly)."""
+    import dataclasses
+    rng = np.random.default_rng(seed)
+    u = np.full(d, 1.0 / np.sqrt(d))
+    H = base.q.shape[1]
+    q = 40 * u + 0.05 * rng.standard_normal((base.q.shape[0], H, d))
+    k = -40 * u + (40 / np.sqrt(d)) * rng.standard_normal(tuple(base.k.shape))
+    return dataclasses.replace(base, q=torch.from_numpy(q).to(torch.bfloat16),
+                               k=torch.from_numpy(k).to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("d,n", [(128, 100), (64, 100), (128, 300)],
+                         ids=["one-work-group", "key-chunk-with-dq", "key-chunk-and-query-tile"])
+def test_bf16_softmax_all_scores_very_negative(gdpa_lib, d, n):
+    # Every score of every token below about -100, so the row LSE is too and exp(-LSE)
+    # overflows fp32.  The backward kernels compute P for context rows past n (zero K and
+    # V rows, score 0) as exp(-LSE); they must keep it finite there (no inf * 0 in dQ),
+    # whatever the path: the one-work-group backward (d = 128, n <= 256), the key-chunk
+    # kernel with its own dQ (d = 64), and the key-chunk kernel plus the query-tile dQ
+    # kernel (n = 300).
+    cfg = custom_config((70, 33, 130), H=2, d=d, n=n, phi="softmax")
+    inp = very_negative_scores(gi.make_gdpa_inputs(cfg, seed=5, with_grad=True), d, seed=6)
+    say(f"case: very negative scores d={d} n={n} T={inp.total_tokens}")
+    qd, off, kd, vd, do = device_inputs(inp)
+    o, lse = gdpa_lib.fwd(qd, off, kd, vd, phi="softmax")
+    dq, dk, dv = gdpa_lib.bwd(qd, off, kd, vd, o, lse, do, phi="softmax")
+    torch.cuda.synchronize()
+    o_ref, lse_ref = orc.gdpa_forward(inp.q, inp.offsets, inp.k, inp.v, "softmax")
+    assert float(np.nanmax(lse_ref)) < -90.0  # the premise of the case
+    refs = dict(zip(("dq", "dk", "dv"), orc.gdpa_backward(inp.q, inp.offsets, inp.k, inp.v, inp.do, "softmax")))
+    errs = {"o": max_abs_rel(o, o_ref), "lse": max_abs_rel(lse, lse_ref)}
+    errs.update({name: max_abs_rel(got, refs[name]) for name, got in (("dq", dq), ("dk", dk), ("dv", dv))})
+    say("  errors:", {k_: f"{e:.2e}" for k_, e in errs.items()})
+    for t in (o, lse, dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    for name, e in errs.items():
+        assert e <= TOL["bf16"], f"{name}: max-abs-rel {e:.3e}"
+
+
 @pytest.mark.parametrize("dtype,d,n", [("bf16", 64, 96), ("f32", 64, 96), ("bf16", 128, 200)])
 @pytest.mark.parametrize("mode", ["accumulate", "residual"])
 def test_residual_and_accumulated_dq(gdpa_lib, dtype, d, n, mode):
