@@ -172,21 +172,27 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         // raw product Q.K and the scale enters each exponent through the FMA that
         // subtracts the max (one VALU operation per score fewer); otherwise (biases, or
         // a scale <= 0) the scores are scaled first and sm = 1.
+        // Only a tile that runs past n has scores to mask (wave-uniform test); each case
+        // is compiled on its own so that full tiles carry no per-score select.
         const bool tail = j0 + 32 > n;
         float mx = -INFINITY;
-        auto mask_max = [&](auto score) {
+        auto mask_max = [&](auto score, auto MASK) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             float s = score(r);
-            if (tail && j0 + 8 * (r >> 2) + 4 * g + (r & 3) >= n) s = -INFINITY;
+            if (decltype(MASK)::value && j0 + 8 * (r >> 2) + 4 * g + (r & 3) >= n) s = -INFINITY;
             S[r] = s;
             mx = fmaxf(mx, s);
           }
         };
+        auto raw_score = [&](int r) { return S[r]; };
+        auto scaled_score = [&](int r) { return RESID == 3 ? fmaf(bj[r], kLog2e, S[r] * sl2) : S[r] * sl2; };
         if (raw) {
-          mask_max([&](int r) { return S[r]; });
+          if (tail) mask_max(raw_score, std::true_type{});
+          else mask_max(raw_score, std::false_type{});
         } else {
-          mask_max([&](int r) { return RESID == 3 ? fmaf(bj[r], kLog2e, S[r] * sl2) : S[r] * sl2; });
+          if (tail) mask_max(scaled_score, std::true_type{});
+          else mask_max(scaled_score, std::false_type{});
         }
         mx = fmaxf(mx, wave_xor32(mx));
         if (first) {
