@@ -141,7 +141,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_bf16_kernel(const BwdArgs
   // read + 1), columns base + 4 c; item i <-> context row 8 G + 2 (i % 4) + i / 4.
   const int q16_row = 8 * trG + 2 * trr, q16_col = 4 * (lane & 3);
 
-  const float sl2 = a.scale * kLog2e;
+  const float sl2 = a.scale * kLog2e, nsl2 = -sl2;
   const uint16_t* Qg = (const uint16_t*)a.q + (size_t)h * D;
   const uint16_t* dOg = (const uint16_t*)a.d_o + (size_t)h * D;
 
@@ -215,8 +215,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_bf16_kernel(const BwdArgs
       if (PHI == 0) {
         // P <= 1 for the sample's rows; the cap keeps rows past n finite when every
         // score of the token is very negative (their P would overflow).
-        p = fminf(fast_exp2(BIAS ? fmaf(sbj, kLog2e, S[r] * sl2) - lse_s[t] : S[r] * sl2 - lse_s[t]), 1.0f);
+        p = fminf(fast_exp2(BIAS ? fmaf(sbj, kLog2e, S[r] * sl2) - lse_s[t] : fmaf(S[r], sl2, -lse_s[t])), 1.0f);
         ds = p * (dP[r] - dvec_s[t]);
+      } else if (PHI == kPhiSilu && !BIAS) {
+        // With sg = sigmoid(scale S) and q = S sg: P = scale q (the scale is applied to dV
+        // at the end) and ds / dP = sg + scale q (1 - sg).
+        const float sg = fast_rcp(1.0f + fast_exp2(S[r] * nsl2));
+        p = S[r] * sg;
+        ds = dP[r] * fmaf(a.scale, fmaf(-p, sg, p), sg);
       } else {
         float gr;
         p = phi_value_grad<PHI>(BIAS ? fmaf(S[r], a.scale, sbj) : S[r] * a.scale, gr);
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_bf16_kernel(const BwdArgs
       }
       P[r] = p;
       if (BIAS) dsb += ds;  // rows past the sample have dO = 0, so ds = 0 there
-      dS[r] = ds * a.scale;
+      dS[r] = ds;  // the score scale is applied to dK and dQ at the end
     }
 
     // dS^T rows of this wave into LDS: row jl, tokens 8 q + 4 g .. + 3.
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_bf16_kernel(const BwdArgs
         const int t = t0 + 4 * (lane >> 4) + r;
         if (t < rows) {
           const size_t idx = (size_t)(seq0 + tq + t) * rs + (size_t)h * D + d;
-          float v = acc[r];
+          float v = acc[r] * a.scale;
           if (a.dq_base != nullptr) v += bf2f(((const uint16_t*)a.dq_base)[idx]);
           ((uint16_t*)a.dq)[idx] = __builtin_bit_cast(uint16_t, f2bf(v));
         }
@@ -293,6 +299,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_bf16_kernel(const BwdArgs
     dsb += wave_xor32(dsb);
     if (g == 0 && jvalid) a.d_score_bias[(crow0 + jw) * H + h] = dsb;
   }
+  // dK takes the score scale here, and so does dV when P was kept without it (SiLU).
+  constexpr bool dv_scaled = PHI == kPhiSilu && !BIAS;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dK[dt][r] *= a.scale;
+      if (dv_scaled) dV[dt][r] *= a.scale;
+    }
   // dK, dV: lane (d + 32 g), register r holds context row 32 w + 8 (r / 4) + 4 g + r % 4.
   uint16_t* dkp = (uint16_t*)a.dk + (kv0 + h) * D;
   uint16_t* dvp = (uint16_t*)a.dv + (kv0 + h) * D;
