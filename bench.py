@@ -68,6 +68,11 @@ def parse():
                     help="layer schedule of --op layers (the other one is timed alongside)")
     ap.add_argument("--window", type=int, default=512, help="window of --op swa")
     ap.add_argument("--seeds", type=int, default=32, help="seeds of --op pma (1..32)")
+    ap.add_argument("--record-traffic", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="rewrite the committed traffic record of --config/--phi (or --op pma) from "
+                         "two rocprofv3 counter runs of this script (FETCH_SIZE, then WRITE_SIZE; "
+                         "their -d output folders), keeping the record's kernel lists and its copy "
+                         "calibration; no GPU is used")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
@@ -116,6 +121,89 @@ def measured_traffic(stage, path):
     if not k or not k.get("sources") or k.get("source_sha256") != source_hash(k["sources"]):
         return None
     return k.get("bytes_per_launch")
+
+
+def _counter_means(folder, counter):
+    """Mean value of `counter` per dispatch, by kernel name (template arguments kept,
+    namespace and parameter list dropped), over every rocprofv3 counter CSV under
+    `folder`."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                name = name[len("void "):] if name.startswith("void ") else name
+                name = name.split("(")[0].replace("gdpa::", "")
+                key = (name, row["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    sums = {}
+    for (name, _), v in per.items():
+        t = sums.setdefault(name, [0.0, 0])
+        t[0] += v
+        t[1] += 1
+    return {name: tot / cnt for name, (tot, cnt) in sums.items()}
+
+
+def record_traffic(args):
+    """Rewrite the traffic record (JSON and its Markdown summary) of one bench workload
+    from the FETCH_SIZE and WRITE_SIZE counter runs: per stage, the per-dispatch means
+    of its kernels are summed (one launch of the stage runs each once), scaled by the
+    record's copy calibration, and tied to the current sources by their hash."""
+    import gdpa_inputs as gi
+    key = "pma" if args.op == "pma" else (args.config, args.phi or gi.CONFIGS[args.config].phis[0])
+    path = traffic_file(key)
+    if path is None:
+        sys.exit(f"no traffic record for workload {key}")
+    with open(path) as f:
+        rec = json.load(f)
+    fetch = _counter_means(args.record_traffic[0], "FETCH_SIZE")
+    write = _counter_means(args.record_traffic[1], "WRITE_SIZE")
+    cal = rec["calibration"]
+    rows = []
+    for stage, k in rec["kernels"].items():
+        missing = [n for n in k["kernels"] if n not in fetch or n not in write]
+        if missing:
+            sys.exit(f"{stage}: no counter readings for {missing}")
+        k["fetch_kib"] = round(sum(fetch[n] for n in k["kernels"]), 1)
+        k["write_kib"] = round(sum(write[n] for n in k["kernels"]), 1)
+        k["bytes_per_launch"] = int(round((k["fetch_kib"] * cal["fetch_scale"] + k["write_kib"] * cal["write_scale"])
+                                          * 1024))
+        k["source_sha256"] = source_hash(k["sources"])
+        rows.append((stage, k))
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    md = os.path.splitext(path)[0] + ".md"
+    lines = [f"# HBM traffic per launch: {rec['workload']}", "",
+             "Counters `FETCH_SIZE` and `WRITE_SIZE` (KiB per dispatch), each in its own rocprofv3",
+             "run, run from /tmp with TMPDIR=/tmp, repo at $R; the record is then rewritten from",
+             "the two output folders:", "", "```"]
+    lines += [rec["commands"][c] for c in ("bench_fetch", "bench_write")]
+    lines += [f"python3 $R/bench.py {' '.join(sys.argv[1:])}"]
+    lines += [rec["commands"][c] for c in ("copy_fetch", "copy_write")]
+    lines += ["```", "",
+              f"Calibration (the copy runs above): a plain device copy of {cal['copy_bytes'] >> 20} MiB reads "
+              f"`FETCH_SIZE` = {cal['fetch_kib']} KiB and", f"`WRITE_SIZE` = {cal['write_kib']} KiB, so fetched "
+              f"bytes = {cal['fetch_scale']:.4f} x FETCH_SIZE x 1024 and written", f"bytes = "
+              f"{cal['write_scale']:.4f} x WRITE_SIZE x 1024.", "",
+              "| call | kernels | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch (scaled) | "
+              "algorithmic bytes / launch | ratio |", "|---|---|---|---|---|---|---|"]
+    for stage, k in rows:
+        alg = k.get("algorithmic_bytes_per_launch")
+        lines.append(f"| {stage} | {', '.join('`' + n + '`' for n in k['kernels'])} | {k['fetch_kib']} | "
+                     f"{k['write_kib']} | {k['bytes_per_launch'] / 1e9:.3f} GB | "
+                     + (f"{alg / 1e9:.3f} GB | {k['bytes_per_launch'] / alg:.2f} |" if alg else "- | - |"))
+    lines += ["", f"The machine-readable record is `{os.path.basename(path)}`; each entry carries the sha256 "
+              "of the sources its kernels are built from (with the shared device and launch headers), and "
+              "`bench.py` reports `roofline.traffic` for this workload from it only while they still match.", ""]
+    with open(md, "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps({"record": os.path.relpath(path, ROOT),
+                      "bytes_per_launch": {st: k["bytes_per_launch"] for st, k in rows}}))
 
 
 def calibrate_copy(mib):
@@ -977,6 +1065,9 @@ def main():
         print(json.dumps({"error": msg, "n_gpus": args.gpus}))
         sys.exit(2)
 
+    if args.record_traffic:
+        record_traffic(args)
+        return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
