@@ -149,19 +149,26 @@ def _counter_means(folder, counter):
 
 
 def record_traffic(args):
-    """Rewrite the traffic record (JSON and its Markdown summary) of one bench workload
-    from the FETCH_SIZE and WRITE_SIZE counter runs: per stage, the per-dispatch means
-    of its kernels are summed (one launch of the stage runs each once), scaled by the
-    record's copy calibration, and tied to the current sources by their hash."""
+    """`--record-traffic`: rewrite the committed record of the workload that --config /
+    --phi (or --op pma) name."""
     import gdpa_inputs as gi
     key = "pma" if args.op == "pma" else (args.config, args.phi or gi.CONFIGS[args.config].phis[0])
     path = traffic_file(key)
     if path is None:
         sys.exit(f"no traffic record for workload {key}")
+    rewrite_traffic_record(path, args.record_traffic[0], args.record_traffic[1], " ".join(sys.argv[1:]))
+
+
+def rewrite_traffic_record(path, fetch_dir, write_dir, cmdline):
+    """Rewrite the traffic record at `path` (JSON and its Markdown summary) from the
+    FETCH_SIZE and WRITE_SIZE counter runs in `fetch_dir` and `write_dir`: per stage,
+    the per-dispatch means of its kernels are summed (one launch of the stage runs each
+    once), scaled by the record's copy calibration, and tied to the current sources by
+    their hash.  `cmdline` is the bench.py argument list quoted in the summary."""
     with open(path) as f:
         rec = json.load(f)
-    fetch = _counter_means(args.record_traffic[0], "FETCH_SIZE")
-    write = _counter_means(args.record_traffic[1], "WRITE_SIZE")
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
     cal = rec["calibration"]
     rows = []
     for stage, k in rec["kernels"].items():
@@ -183,7 +190,7 @@ def record_traffic(args):
              "run, run from /tmp with TMPDIR=/tmp, repo at $R; the record is then rewritten from",
              "the two output folders:", "", "```"]
     lines += [rec["commands"][c] for c in ("bench_fetch", "bench_write")]
-    lines += [f"python3 $R/bench.py {' '.join(sys.argv[1:])}"]
+    lines += [f"python3 $R/bench.py {cmdline}"]
     lines += [rec["commands"][c] for c in ("copy_fetch", "copy_write")]
     lines += ["```", "",
               f"Calibration (the copy runs above): a plain device copy of {cal['copy_bytes'] >> 20} MiB reads "

@@ -90,3 +90,45 @@ def test_cpu_clock_counts_the_cores_a_region_keeps_busy():
     f = clk.fields()
     assert 0.5 <= f["cores_effective"] <= 1.5 and f["cores"] == 1
     assert f["processes"] == 1 and f["threads_available"] >= 1 and isinstance(f["cpu_model"], str)
+
+
+def test_traffic_record_rewrite(tmp_path):
+    # Two synthetic rocprofv3 counter CSVs (two dispatches per kernel, the second
+    # reading twice the first) rewrite a copy of the committed stacked-workload record:
+    # every stage's bytes are its kernels' mean readings scaled by the record's copy
+    # calibration, and the record ties itself to the current sources.
+    import csv
+    import shutil
+    src = os.path.join(ROOT, "profiles", "traffic_stacked_b1024_h8_d128_n256_silu.json")
+    path = tmp_path / "rec.json"
+    shutil.copy(src, path)
+    rec = json.load(open(src))
+    names = {"bwd_res_kernel<1, 1>": "void gdpa::bwd_res_kernel<1, 1>(gdpa::BwdArgs)",
+             "fwd_res_kernel<128, 256, 1, 1>": "void gdpa::fwd_res_kernel<128, 256, 1, 1>(gdpa::FwdArgs, int const*)",
+             "gemm_nt_kernel": "gdpa::gemm_nt_kernel(int, long, int, unsigned short const*)",
+             "gemm_tn_kernel": "gdpa::gemm_tn_kernel(int, long, int, unsigned short const*)"}
+    base = {n: 1000.0 * (i + 1) for i, n in enumerate(names)}
+    for counter, sub, mult in (("FETCH_SIZE", "f", 1.0), ("WRITE_SIZE", "w", 3.0)):
+        d = tmp_path / sub / "host" / "123"
+        d.mkdir(parents=True)
+        with open(d / "run_counter_collection.csv", "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            did = 0
+            for rep in (1, 2):
+                for n, full in names.items():
+                    did += 1
+                    w.writerow([did, full, counter, base[n] * mult * rep])
+                    w.writerow([did, full, "OTHER", 7.0])
+    bench.rewrite_traffic_record(str(path), str(tmp_path / "f"), str(tmp_path / "w"), "--record-traffic f w")
+    out = json.load(open(path))
+    cal = rec["calibration"]
+    for stage, k in out["kernels"].items():
+        fetch = sum(1.5 * base[n] for n in k["kernels"])
+        write = sum(4.5 * base[n] for n in k["kernels"])
+        assert k["fetch_kib"] == pytest.approx(fetch)
+        assert k["write_kib"] == pytest.approx(write)
+        assert k["bytes_per_launch"] == round((fetch * cal["fetch_scale"] + write * cal["write_scale"]) * 1024)
+        assert k["source_sha256"] == bench.source_hash(k["sources"])
+    md = open(tmp_path / "rec.md").read()
+    assert "--record-traffic f w" in md and "| gdpa_bwd |" in md
