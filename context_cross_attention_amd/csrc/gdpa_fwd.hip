@@ -20,6 +20,15 @@
 
 namespace gdpa {
 
+// Online softmax with a lazy reference max: a row's reference (the shift of its
+// exponentials) moves only when a new score exceeds it by more than this many units
+// of log2, as in FlashAttention-4's conditional rescaling, so the unnormalised P stays
+// at most 2^8 (exact in fp32 and no coarser in bf16, whose precision is relative) and
+// O is rescaled only on the rare tiles that raise some row's max that far.
+namespace {
+constexpr float kRescaleLog2 = 8.0f;
+}  // namespace
+
 // SW: sliding-window self-attention (Kunlun paper summary, section 2.2, Sliding
 // Window Attention bullet): K and V are the sample's own token rows, and token i
 // (position in its sample) attends to positions i - window < j <= i only; the
@@ -180,16 +189,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
       if (tail || (SW && !inside)) mask_max(std::true_type{});  // wave-uniform
       else mask_max(std::false_type{});
       mx = fmaxf(mx, wave_xor32(mx));
+      // m_run is the row's reference max (the shift of its exponentials), moved only
+      // when a score exceeds it by more than 2^kRescaleLog2 (wave-uniform test; the
+      // first finite block of a row always moves it, and a row with no finite score
+      // yet keeps -inf).  A row whose window has missed every block so far (SW) is
+      // shifted by 0.
       const float m_new = fmaxf(m_run, mx);
-      // A row whose window misses this whole block (SW) keeps m = -inf: shift by 0.
-      const float m_use = (SW && m_new == -INFINITY) ? 0.f : m_new;
-      // Rescale O only when some row's running max moved (wave-uniform test).
-      if (__any(m_new > m_run)) {
-        const float corr = fast_exp2((m_run - m_use) * sm);
+      if (__any((m_new - m_run) * sm > kRescaleLog2)) {
+        const float corr = fast_exp2((m_run - ((SW && m_new == -INFINITY) ? 0.f : m_new)) * sm);
         l_run *= corr;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) O[dt] *= corr;
+        m_run = m_new;
       }
+      const float m_use = (SW && m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -198,7 +211,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdArgs a) {
           l_run += p;
           S[mt][r] = p;
         }
-      m_run = m_new;
     } else {
       // Elementwise maps; rows past n are zero in K and V, and phi(0) = 0.
 #pragma unroll

@@ -15,6 +15,15 @@
 
 namespace gdpa {
 
+// Online softmax with a lazy reference max: a row's reference (the shift of its
+// exponentials) moves only when a new score exceeds it by more than this many units
+// of log2, as in FlashAttention-4's conditional rescaling, so the unnormalised P stays
+// at most 2^8 (exact in fp32 and no coarser in bf16, whose precision is relative) and
+// O is rescaled only on the rare tiles that raise some row's max that far.
+namespace {
+constexpr float kRescaleLog2 = 8.0f;
+}  // namespace
+
 // Position of context row j inside V^T rows: the S^T C tile holds, in lane group g,
 // register r, row 8 (r / 4) + 4 g + r % 4 of a 32-row tile; a B-operand k-step kk
 // takes registers 8 kk .. 8 kk + 7.  Storing j = 32 t + 16 kk + 8 a + 4 g + c at
@@ -197,7 +206,7 @@ __global__ __launch_bounds__(512, 1) void fwd_res_kernel(const FwdArgs a, const 
         mx = fmaxf(mx, wave_xor32(mx));
         if (first) {
           m_run = mx;
-        } else if (__any(mx > m_run)) {  // rescale O only when some row's running max moved (wave-uniform)
+        } else if (__any((mx - m_run) * sm > kRescaleLog2)) {  // lazy reference max (wave-uniform test)
           const float m_new = fmaxf(m_run, mx);
           const float corr = fast_exp2((m_run - m_new) * sm);
           l_run *= corr;
